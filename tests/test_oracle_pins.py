@@ -1,0 +1,419 @@
+"""Pins of the C oracle against things other than itself (CPU only).
+
+Each test targets a mistake the oracle could plausibly make: a dropped bias
+term, a wrong nibble or group index, a transposed operand, a wrong tie
+order, the sidecar and clamp in the wrong order, double rounding, a wrong
+combine weight.  The pages print no worked example, so the pins are the
+independent numpy brute force (tests/bruteforce.py), closed forms,
+invariants and exhaustive checks of the conversions.
+"""
+
+import hashlib
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+from scipy.special import softmax
+
+import bruteforce as bf
+from moe_workloads import SHAPES, Shape, make_layer, make_logits, make_x, quantize_affine4
+from moe_workloads.gen import bf16_bits_from_f32, f32_from_bf16_bits
+from oracle import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def tiny(H=128, F=64, E=4, k=2, act="f32", sidecar=False, clamp=0.0, cfg=90):
+    return Shape(f"tiny{H}x{F}x{E}x{k}", cfg, H, F, E, k, act, sidecar=sidecar, clamp=clamp)
+
+
+def rel_l2(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
+
+
+# ------------------------------------------------------------- generators
+def test_generator_is_deterministic():
+    sh = SHAPES["toy"]
+    a = make_layer(sh, layer=0, seed=3)
+    b = make_layer(sh, layer=0, seed=3)
+    c = make_layer(sh, layer=0, seed=4)
+    for name in ("gate_q", "up_s", "down_b"):
+        assert np.array_equal(getattr(a, name), getattr(b, name))
+        assert not np.array_equal(getattr(a, name), getattr(c, name))
+    h = hashlib.sha256(a.gate_q.tobytes() + a.down_s.tobytes()).hexdigest()
+    assert h == hashlib.sha256(b.gate_q.tobytes() + b.down_s.tobytes()).hexdigest()
+    assert np.array_equal(make_x(sh, 3, seed=1), make_x(sh, 3, seed=1))
+    assert np.array_equal(make_logits(sh, 3, seed=1), make_logits(sh, 3, seed=1))
+
+
+def test_expert_bytes_do_not_depend_on_selection():
+    sh = SHAPES["toy"]
+    full = make_layer(sh, seed=5)
+    part = make_layer(sh, experts=[2, 6], seed=5)
+    for name in ("gate_q", "gate_s", "up_q", "down_q", "down_b"):
+        assert np.array_equal(getattr(full, name)[[2, 6]], getattr(part, name)[[2, 6]])
+    assert np.isnan(part.gate_s[0].view(np.float16).astype(np.float32)).all()
+
+
+def test_quantizer_round_trip_error_is_within_half_step():
+    rng = np.random.default_rng(0)
+    w = (rng.standard_normal((16, 256)) * 0.02).astype(np.float32)
+    q, s, b = quantize_affine4(w)
+    deq = bf.dequant_dense(q, s, b)
+    step = np.repeat(s.view(np.float16).astype(np.float64), 64, axis=1)
+    # fp16 rounding of scale and bias adds a little over half a step
+    assert np.all(np.abs(deq - w) <= 0.5 * step + 1e-4)
+
+
+# ------------------------------------------------------------- conversions
+def test_f16_decode_exhaustive_against_numpy():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = bits.view(np.float16).astype(np.float64)
+    ours = np.array([oracle.f16_to_f64(int(v)) for v in bits[::7]])
+    r = ref[::7]
+    finite = np.isfinite(r)
+    assert np.array_equal(ours[finite], r[finite])
+    assert np.array_equal(np.isnan(ours), np.isnan(r))
+
+
+def test_bf16_rounding_is_single_step_ties_to_even():
+    with open(os.path.join(GOLDEN, "bf16_rounding.json")) as f:
+        cases = json.load(f)["cases"]
+    for c in cases:
+        v = float.fromhex(c["value"])
+        assert oracle.f64_to_bf16(v) == int(c["bf16"], 16), c
+
+
+def test_bf16_rounding_matches_fp32_path_off_ties():
+    # For values exactly representable in fp32 no double rounding can occur,
+    # so fp64 -> bf16 must equal the integer-trick fp32 -> bf16 rounding.
+    rng = np.random.default_rng(1)
+    v = (rng.standard_normal(20000) * np.exp(rng.uniform(-20, 20, 20000))).astype(np.float32)
+    ours = oracle.round_bf16(v.astype(np.float64))
+    assert np.array_equal(ours, bf16_bits_from_f32(v))
+
+
+# ----------------------------------------------------------------- dequant
+def test_nibble_order_low_nibble_first():
+    with open(os.path.join(GOLDEN, "nibble_order.json")) as f:
+        fx = json.load(f)
+    q = np.zeros((1, 8), np.uint32)
+    q[0, : len(fx["words"])] = [int(w, 16) for w in fx["words"]]
+    one, zero = np.uint16(0x3C00), np.uint16(0)
+    s = np.full((1, 1), one, np.uint16)
+    b = np.full((1, 1), zero, np.uint16)
+    w = oracle.dequant(q, s, b)[0]
+    assert list(w[: len(fx["elements"])].astype(int)) == fx["elements"]
+
+
+def test_dequant_against_hex_digits_and_groups():
+    rng = np.random.default_rng(2)
+    rows, cols = 3, 256
+    q = rng.integers(0, 2 ** 32, (rows, cols // 8), dtype=np.uint64).astype(np.uint32)
+    s = np.float16(rng.uniform(0.001, 0.1, (rows, cols // 64))).view(np.uint16)
+    b = np.float16(rng.uniform(-1, 1, (rows, cols // 64))).view(np.uint16)
+    w = oracle.dequant(q, s, b)
+    for r in range(rows):
+        for c in range(0, cols, 5):
+            digit = int(("%08x" % q[r, c // 8])[7 - (c % 8)], 16)
+            exp = float(s[r, c // 64].view(np.float16)) * digit + float(b[r, c // 64].view(np.float16))
+            assert w[r, c] == exp
+    assert np.array_equal(w, bf.dequant_dense(q, s, b))
+
+
+# ------------------------------------------------------------------- route
+def test_route_k1_weight_is_one_and_argmax():
+    lg = make_logits(SHAPES["decode"], 6, seed=3)
+    idx, w = oracle.route_topk(lg, 1)
+    assert np.array_equal(idx[:, 0], np.argmax(lg, axis=1))
+    assert np.all(w == 1.0)
+
+
+def test_route_k_equals_e_is_full_softmax():
+    lg = make_logits(SHAPES["toy"], 5, seed=4)
+    idx, w = oracle.route_topk(lg, 8)
+    full = softmax(lg.astype(np.float64), axis=1)
+    got = np.zeros_like(full)
+    for t in range(5):
+        got[t, idx[t]] = w[t]
+    assert np.allclose(got, full, rtol=1e-14, atol=1e-16)
+
+
+def test_route_ties_go_to_lower_id():
+    lg = np.zeros((2, 8), np.float32)
+    lg[1, [5, 2, 7]] = 1.0
+    idx, w = oracle.route_topk(lg, 4)
+    assert idx[0].tolist() == [0, 1, 2, 3]
+    assert idx[1].tolist() == [2, 5, 7, 0]
+    assert np.allclose(w[0], 0.25, rtol=0, atol=1e-16)
+
+
+@pytest.mark.parametrize("E,k,B", [(8, 2, 3), (128, 8, 16), (256, 6, 4), (64, 16, 5)])
+def test_route_against_bruteforce_and_invariants(E, k, B):
+    sh = Shape("r", 91, 64, 64, E, k, "f32")
+    lg = make_logits(sh, B, seed=E + k)
+    idx, w = oracle.route_topk(lg, k)
+    bidx, bw = bf.route(lg, k)
+    assert np.array_equal(idx, bidx)
+    assert np.allclose(w, bw, rtol=1e-13, atol=1e-16)
+    assert np.allclose(w.sum(axis=1), 1.0, rtol=0, atol=1e-15)
+    assert np.all(np.diff(w, axis=1) <= 0)
+    for t in range(B):
+        assert len(set(idx[t].tolist())) == k
+
+
+# -------------------------------------------------------------------- plan
+@pytest.mark.parametrize("regime,B", [("normal", 1), ("normal", 7), ("sharing", 8), ("disjoint", 4),
+                                      ("same", 5), ("zipf", 32)])
+def test_plan_against_bruteforce_and_invariants(regime, B):
+    sh = SHAPES["decode"]
+    idx, _ = oracle.route_topk(make_logits(sh, B, regime=regime, seed=11), sh.top_k)
+    p = oracle.plan(idx, sh.n_experts)
+    q = bf.plan(idx, sh.n_experts)
+    for key in ("counts", "offsets", "sorted_slots", "unique_experts"):
+        assert np.array_equal(p[key], q[key]), key
+    assert p["n_unique"] == q["n_unique"]
+    n = B * sh.top_k
+    assert sorted(p["sorted_slots"].tolist()) == list(range(n))
+    assert p["counts"].sum() == n and p["offsets"][-1] == n
+    flat = idx.ravel()
+    for e in range(sh.n_experts):
+        lst = p["sorted_slots"][p["offsets"][e]:p["offsets"][e + 1]]
+        assert np.all(flat[lst] == e) and np.all(np.diff(lst) > 0)
+    assert p["n_unique"] <= min(sh.n_experts, n)
+    if regime == "same":
+        assert p["n_unique"] == sh.top_k
+    if regime == "disjoint":
+        assert p["n_unique"] == min(n, sh.n_experts)
+
+
+def test_plan_empty_batch():
+    p = oracle.plan(np.zeros((0, 8), np.int32), 16)
+    assert p["n_unique"] == 0 and p["counts"].sum() == 0
+    assert np.all(p["unique_experts"] == -1) and np.all(p["offsets"] == 0)
+
+
+# ------------------------------------------------------------ expert block
+CASES = [
+    dict(H=64, F=64, E=1, k=1, act="f32", B=1),
+    dict(H=128, F=64, E=2, k=1, act="bf16", B=2),
+    dict(H=256, F=128, E=4, k=2, act="f32", B=3),
+    dict(H=128, F=128, E=8, k=4, act="bf16", B=5),
+    dict(H=256, F=64, E=16, k=4, act="bf16", B=2),
+    dict(H=64, F=128, E=8, k=2, act="f32", B=1, sidecar=True, clamp=0.5),
+    dict(H=128, F=64, E=4, k=3, act="bf16", B=4, sidecar=True, clamp=10.0),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "H{H}F{F}E{E}k{k}{act}B{B}".format(**c))
+def test_decode_against_dense_bruteforce(case):
+    sh = tiny(case["H"], case["F"], case["E"], case["k"], case["act"],
+              case.get("sidecar", False), case.get("clamp", 0.0))
+    L = make_layer(sh, seed=7)
+    x = make_x(sh, case["B"], seed=7, scale=4.0 if case.get("clamp") == 0.5 else 1.0)
+    lg = make_logits(sh, case["B"], seed=7)
+    idx, w = oracle.route_topk(lg, sh.top_k)
+    out = oracle.decode_step(L, x, idx, w)
+    bidx, bw, bout = bf.moe_dense(L, x, lg)
+    assert np.array_equal(idx, bidx)
+    assert rel_l2(out, bout) <= 1e-12
+
+
+def test_toy_config_against_bruteforce():
+    sh = SHAPES["toy"]
+    L = make_layer(sh, seed=0)
+    x = make_x(sh, 1, seed=0)
+    lg = make_logits(sh, 1, seed=0)
+    idx, w = oracle.route_topk(lg, sh.top_k)
+    out = oracle.decode_step(L, x, idx, w)
+    _, _, bout = bf.moe_dense(L, x, lg)
+    assert rel_l2(out, bout) <= 1e-12
+
+
+def _onehot_layer(H=128, F=64, seed=0):
+    """Gate weights random nibbles with s=1, b=0; up q=0, b=1 (u = sum x)."""
+    sh = tiny(H, F, 1, 1, "f32", cfg=92)
+    L = make_layer(sh, seed=seed)
+    rng = np.random.default_rng(seed)
+    L.gate_q[:] = rng.integers(0, 2 ** 32, L.gate_q.shape, dtype=np.uint64).astype(np.uint32)
+    L.gate_s[:] = 0x3C00
+    L.gate_b[:] = 0
+    L.up_q[:] = 0
+    L.up_s[:] = 0x3C00
+    L.up_b[:] = 0x3C00
+    return sh, L
+
+
+def test_onehot_x_reads_the_right_nibble():
+    sh, L = _onehot_layer()
+    silu = lambda v: v / (1.0 + math.exp(-v))  # noqa: E731
+    for c in (0, 1, 7, 8, 63, 64, 65, 127):
+        x = np.zeros((1, sh.hidden), np.float32)
+        x[0, c] = 1.0
+        _, h = oracle.decode_step(L, x, np.zeros((1, 1), np.int32), np.ones((1, 1)), want_h=True)
+        for n in range(sh.dff):
+            digit = int(("%08x" % L.gate_q[0, n, c // 8])[7 - (c % 8)], 16)
+            assert h[0, n] == silu(float(digit)) * 1.0, (c, n)
+
+
+def test_zero_nibbles_give_bias_times_group_sums():
+    sh = tiny(256, 64, 1, 1, "f32", cfg=93)
+    L = make_layer(sh, seed=1)
+    rng = np.random.default_rng(1)
+    for q, s, b in ((L.gate_q, L.gate_s, L.gate_b), (L.up_q, L.up_s, L.up_b)):
+        q[:] = 0
+        s[:] = np.float16(rng.uniform(0.01, 0.1, s.shape)).view(np.uint16)
+        b[:] = np.float16(rng.uniform(-0.5, 0.5, b.shape)).view(np.uint16)
+    x = make_x(sh, 1, seed=1)
+    _, h = oracle.decode_step(L, x, np.zeros((1, 1), np.int32), np.ones((1, 1)), want_h=True)
+    X = x.astype(np.float64).reshape(4, 64).sum(axis=1)
+    g = L.gate_b[0].view(np.float16).astype(np.float64) @ X
+    u = L.up_b[0].view(np.float16).astype(np.float64) @ X
+    ref = g / (1 + np.exp(-g)) * u
+    assert np.allclose(h[0], ref, rtol=1e-13, atol=0)
+
+
+def test_single_expert_is_plain_quantized_swiglu_mlp():
+    sh = tiny(256, 128, 1, 1, "bf16", cfg=94)
+    L = make_layer(sh, seed=2)
+    x = make_x(sh, 3, seed=2)
+    out = oracle.decode_step(L, x, np.zeros((3, 1), np.int32), np.ones((3, 1)))
+    X = f32_from_bf16_bits(x).astype(np.float64)
+    Wg = bf.dequant_dense(L.gate_q[0], L.gate_s[0], L.gate_b[0])
+    Wu = bf.dequant_dense(L.up_q[0], L.up_s[0], L.up_b[0])
+    Wd = bf.dequant_dense(L.down_q[0], L.down_s[0], L.down_b[0])
+    g = np.dot(X, Wg.T)
+    u = np.dot(X, Wu.T)
+    ref = np.dot(g / (1 + np.exp(-g)) * u, Wd.T)
+    assert rel_l2(out, ref) <= 1e-13
+
+
+def test_sidecar_applies_before_clamp():
+    # sigma = 2 must equal doubling gate/up scales and biases, bitwise, with
+    # the clamp active; clamping first would give 2*clip(g) != clip(2g).
+    sh = tiny(128, 64, 2, 1, "f32", sidecar=True, clamp=0.75, cfg=95)
+    L = make_layer(sh, seed=3)
+    L.sidecar = np.array([2.0, 2.0], np.float32)
+    x = make_x(sh, 2, seed=3, scale=3.0)
+    idx = np.array([[0], [1]], np.int32)
+    w = np.ones((2, 1))
+    a, ha = oracle.decode_step(L, x, idx, w, want_h=True)
+    L2 = make_layer(sh, seed=3)
+    L2.sidecar = None
+    for arr in (L2.gate_s, L2.gate_b, L2.up_s, L2.up_b):
+        arr[:] = (arr.view(np.float16) * np.float16(2)).view(np.uint16)
+    b, hb = oracle.decode_step(L2, x, idx, w, want_h=True)
+    assert np.array_equal(a, b)
+    # the clamp really fires in this case
+    g_lim = 0.75 / (1 + math.exp(-0.75)) * 0.75
+    assert np.isclose(np.abs(ha).max(), g_lim, rtol=1e-15)
+
+
+def test_forced_clamp_matches_bruteforce():
+    sh = tiny(256, 64, 4, 2, "bf16", sidecar=True, clamp=10.0, cfg=96)
+    L = make_layer(sh, seed=4, std=0.2)
+    x = make_x(sh, 3, seed=4, scale=8.0)
+    lg = make_logits(sh, 3, seed=4)
+    idx, w = oracle.route_topk(lg, sh.top_k)
+    out, h = oracle.decode_step(L, x, idx, w, want_h=True)
+    _, _, bout = bf.moe_dense(L, x, lg)
+    assert rel_l2(out, bout) <= 1e-12
+    lim = 10.0 / (1 + math.exp(-10.0)) * 10.0
+    assert np.abs(h).max() <= lim * (1 + 1e-15)
+    assert np.isclose(np.abs(h).max(), lim, rtol=1e-15)  # clamp reached
+
+
+def test_doubling_down_scale_and_bias_doubles_output_exactly():
+    sh = tiny(128, 128, 4, 2, "bf16", cfg=97)
+    L = make_layer(sh, seed=5)
+    x = make_x(sh, 2, seed=5)
+    idx, w = oracle.route_topk(make_logits(sh, 2, seed=5), 2)
+    a = oracle.decode_step(L, x, idx, w)
+    for arr in (L.down_s, L.down_b):
+        arr[:] = (arr.view(np.float16) * np.float16(2)).view(np.uint16)
+    b = oracle.decode_step(L, x, idx, w)
+    assert np.array_equal(b, 2 * a)
+
+
+def test_combine_weights_are_linear():
+    sh = tiny(128, 64, 4, 2, "f32", cfg=98)
+    L = make_layer(sh, seed=6)
+    x = make_x(sh, 1, seed=6)
+    idx = np.array([[1, 3]], np.int32)
+    _, y = oracle.decode_step(L, x, idx, np.array([[0.25, 0.75]]), want_y=True)
+    out = oracle.decode_step(L, x, idx, np.array([[0.25, 0.75]]))
+    assert np.allclose(out[0], 0.25 * y[0] + 0.75 * y[1], rtol=1e-15, atol=1e-300)
+
+
+# -------------------------------------------------------------- invariants
+def test_batch_invariance_permutation_and_duplicates():
+    sh = tiny(256, 128, 8, 2, "bf16", cfg=99)
+    L = make_layer(sh, seed=8)
+    x = make_x(sh, 5, seed=8)
+    lg = make_logits(sh, 5, seed=8)
+    idx, w = oracle.route_topk(lg, 2)
+    full = oracle.decode_step(L, x, idx, w)
+    for t in range(5):
+        one = oracle.decode_step(L, x[t:t + 1], idx[t:t + 1], w[t:t + 1])
+        assert np.array_equal(one[0], full[t])
+    perm = np.array([3, 0, 4, 1, 2])
+    pidx, pw = oracle.route_topk(lg[perm], 2)
+    pout = oracle.decode_step(L, x[perm], pidx, pw)
+    assert np.array_equal(pout, full[perm])
+    dup = np.repeat(x[2:3], 4, axis=0)
+    didx, dw = oracle.route_topk(np.repeat(lg[2:3], 4, axis=0), 2)
+    assert oracle.plan(didx, 8)["n_unique"] == 2
+    dout = oracle.decode_step(L, dup, didx, dw)
+    assert np.all(dout == dout[0:1])
+
+
+def test_expert_relabelling_invariance():
+    sh = tiny(128, 64, 8, 3, "bf16", cfg=100)
+    L = make_layer(sh, seed=9)
+    x = make_x(sh, 3, seed=9)
+    lg = make_logits(sh, 3, seed=9)
+    idx, w = oracle.route_topk(lg, 3)
+    ref = oracle.decode_step(L, x, idx, w)
+    perm = np.random.default_rng(9).permutation(8)  # new id i holds old expert perm[i]
+    for name in ("gate_q", "gate_s", "gate_b", "up_q", "up_s", "up_b", "down_q", "down_s", "down_b"):
+        setattr(L, name, np.ascontiguousarray(getattr(L, name)[perm]))
+    pidx, pw = oracle.route_topk(np.ascontiguousarray(lg[:, perm]), 3)
+    assert np.array_equal(perm[pidx], idx)
+    assert np.array_equal(oracle.decode_step(L, x, pidx, pw), ref)
+
+
+def test_poisoned_expert_shows_up_as_nan():
+    sh = tiny(128, 64, 4, 1, "f32", cfg=101)
+    L = make_layer(sh, experts=[0, 1, 2], seed=10)
+    x = make_x(sh, 1, seed=10)
+    assert np.isfinite(oracle.decode_step(L, x, np.array([[1]], np.int32), np.ones((1, 1)))).all()
+    assert np.isnan(oracle.decode_step(L, x, np.array([[3]], np.int32), np.ones((1, 1)))).all()
+
+
+def test_output_rounding_error_is_what_bf16_allows():
+    sh = SHAPES["toy"]
+    L = make_layer(sh, seed=12)
+    sh16 = Shape("toy16", 0, 256, 128, 8, 2, "bf16")
+    L.shape = sh16
+    x = make_x(sh16, 4, seed=12)
+    idx, w = oracle.route_topk(make_logits(sh16, 4, seed=12), 2)
+    out = oracle.decode_step(L, x, idx, w)
+    r = rel_l2(oracle.bf16_to_f64(oracle.round_bf16(out)), out)
+    # RNE to 8 significant bits: per element |err| <= 2^-9 relative
+    assert 5e-4 < r < 2.26e-3
+    err = np.abs(oracle.bf16_to_f64(oracle.round_bf16(out)) - out)
+    assert np.all(err <= np.abs(out) * 2.0 ** -8)
+
+
+def test_residual_step_mirrors_two_roundings():
+    rng = np.random.default_rng(13)
+    x = bf16_bits_from_f32(rng.standard_normal(4096).astype(np.float32))
+    out = rng.standard_normal(4096) * 0.1
+    nxt = oracle.residual_bf16(x, out)
+    o16 = f32_from_bf16_bits(oracle.round_bf16(out))
+    ref = bf16_bits_from_f32((f32_from_bf16_bits(x) + o16).astype(np.float32))
+    assert np.array_equal(nxt, ref)
