@@ -1,0 +1,200 @@
+/*
+ * moe_decode.h -- C ABI of the decode-time quantized-expert MoE block for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * One decode step of one MoE layer is three calls on one HIP stream:
+ *
+ *   moe_route_topk   router: top-k experts per token and their weights
+ *   moe_expert_plan  cohort plan: slots grouped by expert, distinct experts
+ *   moe_decode_step  expert block: fused gate+up, SiLU*up, down projection,
+ *                    weighted combine over k per token
+ *
+ * The pages this follows describe the problem, not an API: a router yields
+ * per-token (expert, score) slots and is one named part of the decode cost
+ * next to the expert gather and the combine (page "perf(moe): attribute the
+ * MoE decode gap at the M = 1 expert gather", Proposed Solution, step 2);
+ * routed experts are gathered once per (token, k) slot at M = 1 (same page,
+ * Problem / Background); page "perf(moe): batched decode scales 1.55x
+ * against 3.25x on dense" proposes a token dimension with a sum over k per
+ * token and deduplicating expert ids across the cohort so that each expert
+ * plane is read once per step (Proposed Solution), keeps n_tokens a runtime
+ * extent that must not re-specialise kernels, asks that unsupported
+ * configurations decline rather than fail, and that shapes be validated
+ * before dispatch (Implementation Notes).
+ *
+ * Conventions for every entry point:
+ *   - Every array pointer is a DEVICE pointer unless stated otherwise; the
+ *     caller owns all memory.  The library allocates nothing and keeps no
+ *     per-call state.
+ *   - Calls are asynchronous on `hip_stream` (a hipStream_t; NULL = the
+ *     default stream).  No call synchronises the host with the device.
+ *   - Arguments are validated on the host before anything is enqueued.  A
+ *     bad argument returns MOE_ERR_INVALID_ARG, a shape or mode with no
+ *     kernel returns MOE_ERR_UNSUPPORTED (the caller falls back), a short
+ *     workspace returns MOE_ERR_WORKSPACE; nothing aborts.  A failed launch
+ *     returns MOE_ERR_DEVICE.
+ *   - Expert ids inside device arrays cannot be checked on the host.  The
+ *     kernels never read or write out of bounds on a bad id: the planner
+ *     leaves such slots out of every list and the combine writes NaN for
+ *     a token that holds one.
+ */
+#ifndef MOE_DECODE_H
+#define MOE_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARG = 1,
+    MOE_ERR_UNSUPPORTED = 2,
+    MOE_ERR_WORKSPACE = 3,
+    MOE_ERR_DEVICE = 4
+} moe_status;
+
+typedef enum { MOE_DTYPE_F32 = 0, MOE_DTYPE_BF16 = 1 } moe_dtype;
+
+/* Limits enforced by validation. */
+#define MOE_MAX_EXPERTS 1024
+#define MOE_MAX_TOP_K 16
+
+/*
+ * One MoE layer: stacked expert weights, affine 4-bit, groups of 64 along
+ * the input dimension ("4-bit group 64" checkpoints; page "perf(moe):
+ * batched decode scales 1.55x against 3.25x on dense", Current Behavior).
+ *
+ *   w = scale * q + bias,  q in 0..15
+ *
+ * Weight matrices are stored as [expert][out][in/8] uint32 words; element
+ * 8*w+i of a row sits in nibble i of word w, lowest nibble first.  Scales
+ * and biases are fp16 bit patterns, [expert][out][in/64].
+ *   gate, up : out = dff,    in = hidden
+ *   down     : out = hidden, in = dff
+ * Every `*_q` pointer must be 16-byte aligned, every scale/bias pointer
+ * 4-byte aligned.  The struct itself lives in host memory; the pointers it
+ * holds are device pointers.
+ *
+ * `expert_scale` (optional, NULL = none) is one fp32 factor per expert that
+ * multiplies the gate and up pre-activations (the expert-scale sidecars of
+ * page "perf(moe): attribute ...", Problem / Background).  `clamp_limit`
+ * (0 = none) clips gate and up pre-activations to [-L, L] after the sidecar
+ * and before SiLU*up (the clamp stage named on the same page).
+ */
+typedef struct {
+    int32_t hidden;      /* H, multiple of 64 */
+    int32_t dff;         /* expert intermediate size F, multiple of 64 */
+    int32_t n_experts;   /* E, 1..MOE_MAX_EXPERTS */
+    int32_t top_k;       /* k, 1..min(E, MOE_MAX_TOP_K) */
+    int32_t bits;        /* 4 */
+    int32_t group_size;  /* 64 */
+    int32_t act_dtype;   /* moe_dtype of x, residual and out */
+    float clamp_limit;   /* >= 0; 0 disables the clamp */
+    const uint32_t *gate_q, *up_q, *down_q;
+    const uint16_t *gate_s, *gate_b, *up_s, *up_b, *down_s, *down_b;
+    const float *expert_scale; /* [E] or NULL */
+} moe_layer_t;
+
+/*
+ * Cohort plan of one step (all device arrays, int32, caller-allocated):
+ *   counts[E]            slots routed to each expert
+ *   offsets[E+1]         exclusive prefix sum of counts
+ *   sorted_slots[B*k]    slot ids s = t*k + j grouped by expert, ascending
+ *                        expert, ascending slot within an expert
+ *   unique_experts[E]    distinct experts in ascending order, -1 after
+ *   n_unique[1]          number of distinct experts
+ */
+typedef struct {
+    int32_t *counts, *offsets, *sorted_slots, *unique_experts, *n_unique;
+} moe_plan_t;
+
+/*
+ * Router.  logits fp32 [n_tokens][n_experts] (finite) -> topk_idx int32
+ * [n_tokens][top_k] in descending logit order, ties to the lower expert
+ * id, and topk_w fp32 [n_tokens][top_k], the softmax of the kept logits
+ * (equal to softmax over all experts, top-k, renormalise).
+ * n_tokens == 0 returns MOE_OK without a launch.
+ */
+moe_status moe_route_topk(const float *logits, int32_t n_tokens, int32_t n_experts,
+                          int32_t top_k, int32_t *topk_idx, float *topk_w,
+                          void *hip_stream);
+
+/*
+ * Cohort planner: a stable counting sort of the n_tokens*top_k slots by
+ * expert id and the list of distinct experts, so that each expert's
+ * weights are streamed once per step for all the tokens routed to it.
+ * Reads topk_idx int32 [n_tokens][top_k]; writes every array of `plan`
+ * (a host struct of device pointers).  n_tokens == 0 writes an empty plan.
+ */
+moe_status moe_expert_plan(const int32_t *topk_idx, int32_t n_tokens, int32_t n_experts,
+                           int32_t top_k, const moe_plan_t *plan, void *hip_stream);
+
+/* Bytes of device workspace moe_decode_step needs for up to max_tokens
+ * tokens of this layer's shape (0 if the layer is invalid). */
+size_t moe_workspace_size(const moe_layer_t *layer, int32_t max_tokens);
+
+/*
+ * Expert block of one step.
+ *   x         [n_tokens][hidden], act_dtype
+ *   topk_idx  int32 [n_tokens][top_k], topk_w fp32 [n_tokens][top_k]
+ *   plan      the plan of topk_idx (host struct of device pointers)
+ *   residual  optional [n_tokens][hidden] act_dtype, NULL = none
+ *   out       [n_tokens][hidden] act_dtype; must not alias x or residual
+ *   workspace device memory of at least moe_workspace_size(layer, n_tokens)
+ *             bytes, 256-byte aligned; its contents need no initialisation
+ *
+ *   g = Wg[e] x_t, u = Wu[e] x_t   (fp32 accumulation)
+ *   g, u *= expert_scale[e]        (if given)
+ *   g, u = clip(g, u, -L, L)       (if clamp_limit > 0)
+ *   h = silu(g) * u                (fp32, never rounded)
+ *   y = Wd[e] h                    (fp32)
+ *   o_t = sum_{j<k} topk_w[t][j] * y_{t,j}, in j order, rounded once to
+ *         act_dtype (round to nearest even)
+ *   out_t = o_t, or with a residual: act(residual_t + o_t) in fp32
+ *
+ * The fp32 partials with one final rounding follow page "perf(moe):
+ * batched decode scales 1.55x against 3.25x on dense", Implementation
+ * Notes.  A token's result depends only on that token (bitwise the same
+ * whatever else is in the batch), and repeated calls are bitwise equal.
+ */
+moe_status moe_decode_step(const moe_layer_t *layer, const void *x, int32_t n_tokens,
+                           const int32_t *topk_idx, const float *topk_w,
+                           const moe_plan_t *plan, const void *residual, void *out,
+                           void *workspace, size_t workspace_bytes, void *hip_stream);
+
+/*
+ * The two halves of moe_decode_step, for callers that instrument or overlap
+ * the stages (the pages' fused decode kernel is likewise a gate/up kernel
+ * followed by a down kernel: page "perf(moe): batched decode scales 1.55x
+ * against 3.25x on dense", Current Behavior).  Same arguments, checks and
+ * results as moe_decode_step; enqueue moe_expert_gate_up first, then
+ * moe_expert_down_combine with the same workspace, on one stream.
+ *   moe_expert_gate_up       writes h = silu(g) * u per slot into the workspace
+ *   moe_expert_down_combine  reads h, writes out
+ */
+moe_status moe_expert_gate_up(const moe_layer_t *layer, const void *x, int32_t n_tokens,
+                              const moe_plan_t *plan, void *workspace, size_t workspace_bytes,
+                              void *hip_stream);
+moe_status moe_expert_down_combine(const moe_layer_t *layer, int32_t n_tokens,
+                                   const int32_t *topk_idx, const float *topk_w,
+                                   const moe_plan_t *plan, const void *residual, void *out,
+                                   void *workspace, size_t workspace_bytes, void *hip_stream);
+
+/* Host-only check of a layer descriptor (no device access):
+ * MOE_OK, MOE_ERR_INVALID_ARG or MOE_ERR_UNSUPPORTED. */
+moe_status moe_layer_check(const moe_layer_t *layer);
+
+/* Static description of a status code. */
+const char *moe_status_str(moe_status status);
+
+/* ABI version: bumped when a signature or struct changes. */
+int32_t moe_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_DECODE_H */

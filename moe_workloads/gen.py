@@ -89,7 +89,7 @@ def quantize_affine4(w: np.ndarray):
     """
     rows, cols = w.shape
     assert cols % GROUP == 0
-    g = w.reshape(rows, cols // GROUP, GROUP).astype(np.float32)
+    g = w.reshape(rows, cols // GROUP, GROUP).astype(np.float32, copy=False)
     mn = g.min(axis=2)
     mx = g.max(axis=2)
     s16 = ((mx - mn) / np.float32(15.0)).astype(np.float16)
@@ -97,10 +97,13 @@ def quantize_affine4(w: np.ndarray):
     s = s16.astype(np.float32)[:, :, None]
     b = b16.astype(np.float32)[:, :, None]
     safe = np.where(s == 0, np.float32(1.0), s)
-    q = np.where(s == 0, 0.0, np.rint((g - b) / safe))
-    q = np.clip(q, 0, 15).astype(np.uint32).reshape(rows, cols // 8, 8)
-    shifts = (np.arange(8, dtype=np.uint32) * 4)[None, None, :]
-    words = np.bitwise_or.reduce(q << shifts, axis=2).astype(np.uint32)
+    q = np.rint((g - b) / safe)
+    q *= (s != 0)
+    np.clip(q, 0, 15, out=q)
+    q = q.astype(np.uint8).reshape(rows, cols)
+    # two nibbles per byte, lowest first; four little-endian bytes per word
+    packed = (q[:, 0::2] | (q[:, 1::2] << 4)).astype(np.uint8)
+    words = np.ascontiguousarray(packed).view("<u4").astype(np.uint32)
     return words, s16.view(np.uint16), b16.view(np.uint16)
 
 
@@ -224,6 +227,29 @@ def make_logits(shape: Shape, n_tokens: int, layer: int = 0, regime: str = "norm
 
 
 # ------------------------------------------------- device-side bulk weights
+def quantize_affine4_torch(w):
+    """:func:`quantize_affine4` on a torch tensor ``w[n, rows, cols]`` (any
+    device), bit-identical to the numpy version on the same fp32 values.
+    Returns int32 words [n, rows, cols/8] and int16 fp16-bit scale/bias."""
+    import torch
+
+    n, rows, cols = w.shape
+    grp = w.reshape(n, rows, cols // GROUP, GROUP)
+    mn = grp.amin(dim=3)
+    mx = grp.amax(dim=3)
+    s16 = ((mx - mn) / 15.0).half()
+    b16 = mn.half()
+    s = s16.float().unsqueeze(3)
+    b = b16.float().unsqueeze(3)
+    safe = torch.where(s == 0, torch.ones_like(s), s)
+    q = torch.round((grp - b) / safe) * (s != 0)
+    q = q.clamp_(0, 15).to(torch.int64).view(n, rows, cols // 8, 8)
+    shifts = torch.arange(8, device=w.device, dtype=torch.int64) * 4
+    words = (q << shifts).sum(dim=3)  # < 2^32, in int64
+    words = torch.where(words >= 2 ** 31, words - 2 ** 32, words).to(torch.int32)
+    return words, s16.view(torch.int16), b16.view(torch.int16)
+
+
 def make_layer_device(shape: Shape, layer: int, device, seed: int = 0, std: float = 0.02,
                       chunk_experts: int = 8):
     """Same recipe as :func:`make_layer` (N(0,std), affine 4-bit g64) drawn with
@@ -239,23 +265,7 @@ def make_layer_device(shape: Shape, layer: int, device, seed: int = 0, std: floa
     g = torch.Generator(device=device)
     g.manual_seed(int(np.random.SeedSequence([seed, shape.cfg, layer, 9]).generate_state(1)[0]))
     out = {}
-    shifts = (torch.arange(8, device=device, dtype=torch.int32) * 4)
-
-    def quant(w):  # w [n, rows, cols] fp32 -> words int32, s, b int16 bits
-        n, rows, cols = w.shape
-        grp = w.view(n, rows, cols // GROUP, GROUP)
-        mn = grp.amin(dim=3)
-        mx = grp.amax(dim=3)
-        s16 = ((mx - mn) / 15.0).half()
-        b16 = mn.half()
-        s = s16.float().unsqueeze(3)
-        b = b16.float().unsqueeze(3)
-        safe = torch.where(s == 0, torch.ones_like(s), s)
-        q = torch.where(s == 0, torch.zeros_like(grp), torch.round((grp - b) / safe))
-        q = q.clamp_(0, 15).to(torch.int32).view(n, rows, cols // 8, 8)
-        words = (q << shifts).sum(dim=3, dtype=torch.int64).to(torch.int64)
-        words = torch.where(words >= 2 ** 31, words - 2 ** 32, words).to(torch.int32)
-        return words, s16.view(torch.int16), b16.view(torch.int16)
+    quant = quantize_affine4_torch
 
     for name, rows, cols in (("gate", F, H), ("up", F, H), ("down", H, F)):
         qs, ss, bs = [], [], []

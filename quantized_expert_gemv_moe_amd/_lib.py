@@ -1,0 +1,270 @@
+"""ctypes binding of ``libmoe_decode.so`` (include/moe_decode.h).
+
+Argument marshalling only: every step of the decode block runs in the HIP
+kernels behind the C ABI.  torch is used for device memory and the current
+HIP stream.  There is no fallback: if the library is not built, or a call
+returns an error status, this module raises.
+"""
+
+from __future__ import annotations
+
+import ctypes as C
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+from . import build as _build
+
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_DEVICE = range(5)
+MOE_DTYPE_F32, MOE_DTYPE_BF16 = 0, 1
+MOE_MAX_EXPERTS = 1024
+MOE_MAX_TOP_K = 16
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_str(status)} (status {status})")
+
+
+class LayerStruct(C.Structure):
+    _fields_ = [
+        ("hidden", C.c_int32), ("dff", C.c_int32), ("n_experts", C.c_int32), ("top_k", C.c_int32),
+        ("bits", C.c_int32), ("group_size", C.c_int32), ("act_dtype", C.c_int32),
+        ("clamp_limit", C.c_float),
+        ("gate_q", C.c_void_p), ("up_q", C.c_void_p), ("down_q", C.c_void_p),
+        ("gate_s", C.c_void_p), ("gate_b", C.c_void_p), ("up_s", C.c_void_p), ("up_b", C.c_void_p),
+        ("down_s", C.c_void_p), ("down_b", C.c_void_p),
+        ("expert_scale", C.c_void_p),
+    ]
+
+
+class PlanStruct(C.Structure):
+    _fields_ = [("counts", C.c_void_p), ("offsets", C.c_void_p), ("sorted_slots", C.c_void_p),
+                ("unique_experts", C.c_void_p), ("n_unique", C.c_void_p)]
+
+
+_lib = None
+
+EXPORTS = ("moe_route_topk", "moe_expert_plan", "moe_workspace_size", "moe_decode_step",
+           "moe_expert_gate_up", "moe_expert_down_combine", "moe_layer_check", "moe_status_str",
+           "moe_abi_version")
+
+
+def library_path() -> str:
+    return _build.LIB_PATH
+
+
+def lib() -> C.CDLL:
+    """The loaded HIP library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        path = library_path()
+        if not os.path.exists(path):
+            raise RuntimeError(
+                f"HIP library {path} is not built; run __graft_entry__.build() "
+                "or python -m quantized_expert_gemv_moe_amd.build")
+        L = C.CDLL(path)
+        vp, i32 = C.c_void_p, C.c_int32
+        L.moe_route_topk.argtypes = [vp, i32, i32, i32, vp, vp, vp]
+        L.moe_route_topk.restype = C.c_int
+        L.moe_expert_plan.argtypes = [vp, i32, i32, i32, C.POINTER(PlanStruct), vp]
+        L.moe_expert_plan.restype = C.c_int
+        L.moe_workspace_size.argtypes = [C.POINTER(LayerStruct), i32]
+        L.moe_workspace_size.restype = C.c_size_t
+        L.moe_decode_step.argtypes = [C.POINTER(LayerStruct), vp, i32, vp, vp, C.POINTER(PlanStruct),
+                                      vp, vp, vp, C.c_size_t, vp]
+        L.moe_decode_step.restype = C.c_int
+        L.moe_expert_gate_up.argtypes = [C.POINTER(LayerStruct), vp, i32, C.POINTER(PlanStruct), vp,
+                                         C.c_size_t, vp]
+        L.moe_expert_gate_up.restype = C.c_int
+        L.moe_expert_down_combine.argtypes = [C.POINTER(LayerStruct), i32, vp, vp, C.POINTER(PlanStruct), vp,
+                                              vp, vp, C.c_size_t, vp]
+        L.moe_expert_down_combine.restype = C.c_int
+        L.moe_layer_check.argtypes = [C.POINTER(LayerStruct)]
+        L.moe_layer_check.restype = C.c_int
+        L.moe_status_str.argtypes = [C.c_int]
+        L.moe_status_str.restype = C.c_char_p
+        L.moe_abi_version.argtypes = []
+        L.moe_abi_version.restype = C.c_int32
+        _lib = L
+    return _lib
+
+
+def status_str(status: int) -> str:
+    return lib().moe_status_str(int(status)).decode()
+
+
+def _check(status: int, where: str):
+    if status != MOE_OK:
+        raise MoeError(status, where)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> C.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return C.c_void_p(stream.cuda_stream)
+
+
+# ------------------------------------------------------------------- layer
+@dataclass
+class DeviceLayer:
+    """Device tensors of one layer plus the ABI descriptor pointing at them."""
+
+    hidden: int
+    dff: int
+    n_experts: int
+    top_k: int
+    act_dtype: int
+    clamp_limit: float
+    tensors: dict
+    struct: LayerStruct
+
+    @staticmethod
+    def from_tensors(hidden, dff, n_experts, top_k, act: str, clamp_limit: float, tensors: dict):
+        """``tensors``: gate_q/up_q/down_q (int32 or uint32 words), *_s/*_b (fp16 bits as
+        int16/uint16), optional 'sidecar' (fp32 [E]); all on the same device."""
+        t = {k: v for k, v in tensors.items() if v is not None}
+        for k, v in t.items():
+            if not v.is_contiguous():
+                raise ValueError(f"{k} must be contiguous")
+        st = LayerStruct(hidden=hidden, dff=dff, n_experts=n_experts, top_k=top_k, bits=4,
+                         group_size=64, act_dtype=MOE_DTYPE_BF16 if act == "bf16" else MOE_DTYPE_F32,
+                         clamp_limit=float(clamp_limit))
+        for name in ("gate_q", "up_q", "down_q", "gate_s", "gate_b", "up_s", "up_b", "down_s", "down_b"):
+            setattr(st, name, t[name].data_ptr())
+        sc = t.get("sidecar")
+        st.expert_scale = None if sc is None else sc.data_ptr()
+        return DeviceLayer(hidden, dff, n_experts, top_k, st.act_dtype, float(clamp_limit), t, st)
+
+    @staticmethod
+    def from_host(layer, device="cuda"):
+        """Copy a ``moe_workloads.Layer`` (numpy) to the device."""
+        import numpy as np
+
+        def dev(a, dt):
+            return torch.from_numpy(np.ascontiguousarray(a).view(dt)).to(device)
+
+        sh = layer.shape
+        t = {}
+        for n in ("gate_q", "up_q", "down_q"):
+            t[n] = dev(getattr(layer, n), np.int32)
+        for n in ("gate_s", "gate_b", "up_s", "up_b", "down_s", "down_b"):
+            t[n] = dev(getattr(layer, n), np.int16)
+        t["sidecar"] = None if layer.sidecar is None else dev(layer.sidecar.astype(np.float32), np.float32)
+        return DeviceLayer.from_tensors(sh.hidden, sh.dff, sh.n_experts, sh.top_k, sh.act,
+                                        layer.clamp or 0.0, t)
+
+    def check(self) -> int:
+        return lib().moe_layer_check(C.byref(self.struct))
+
+
+# -------------------------------------------------------------------- plan
+@dataclass
+class Plan:
+    counts: torch.Tensor
+    offsets: torch.Tensor
+    sorted_slots: torch.Tensor
+    unique_experts: torch.Tensor
+    n_unique: torch.Tensor
+    struct: PlanStruct
+
+    @staticmethod
+    def allocate(n_experts: int, max_slots: int, device="cuda") -> "Plan":
+        i32 = dict(dtype=torch.int32, device=device)
+        p = [torch.empty(n_experts, **i32), torch.empty(n_experts + 1, **i32),
+             torch.empty(max(max_slots, 1), **i32), torch.empty(n_experts, **i32), torch.empty(1, **i32)]
+        st = PlanStruct(*[x.data_ptr() for x in p])
+        return Plan(*p, st)
+
+
+# ------------------------------------------------------------- entry points
+def route_topk(logits: torch.Tensor, top_k: int, idx: Optional[torch.Tensor] = None,
+               w: Optional[torch.Tensor] = None, stream=None):
+    """moe_route_topk: fp32 logits [B,E] -> (int32 idx [B,k], fp32 w [B,k])."""
+    if logits.dtype != torch.float32 or logits.dim() != 2 or not logits.is_contiguous():
+        raise ValueError("logits must be a contiguous fp32 [B, E] tensor")
+    B, E = logits.shape
+    if idx is None:
+        idx = torch.empty((B, top_k), dtype=torch.int32, device=logits.device)
+    if w is None:
+        w = torch.empty((B, top_k), dtype=torch.float32, device=logits.device)
+    _check(lib().moe_route_topk(_ptr(logits), B, E, top_k, _ptr(idx), _ptr(w), _stream(stream)),
+           "moe_route_topk")
+    return idx, w
+
+
+def expert_plan(idx: torch.Tensor, n_experts: int, plan: Optional[Plan] = None, stream=None) -> Plan:
+    """moe_expert_plan over int32 idx [B,k]."""
+    if idx.dtype != torch.int32 or idx.dim() != 2 or not idx.is_contiguous():
+        raise ValueError("idx must be a contiguous int32 [B, k] tensor")
+    B, k = idx.shape
+    if plan is None:
+        plan = Plan.allocate(n_experts, B * k, device=idx.device)
+    if plan.sorted_slots.numel() < B * k or plan.counts.numel() < n_experts:
+        raise ValueError("plan buffers are too small")
+    _check(lib().moe_expert_plan(_ptr(idx), B, n_experts, k, C.byref(plan.struct), _stream(stream)),
+           "moe_expert_plan")
+    return plan
+
+
+def workspace_size(layer: DeviceLayer, max_tokens: int) -> int:
+    return int(lib().moe_workspace_size(C.byref(layer.struct), int(max_tokens)))
+
+
+def alloc_workspace(layer: DeviceLayer, max_tokens: int, device="cuda") -> torch.Tensor:
+    n = workspace_size(layer, max_tokens)
+    if n == 0 and max_tokens > 0:
+        raise MoeError(layer.check() or MOE_ERR_INVALID_ARG, "moe_workspace_size")
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def decode_step(layer: DeviceLayer, x: torch.Tensor, idx: torch.Tensor, w: torch.Tensor, plan: Plan,
+                out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                residual: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """moe_decode_step: x [B,H] (bf16 or fp32 per the layer) -> out [B,H]."""
+    want = torch.bfloat16 if layer.act_dtype == MOE_DTYPE_BF16 else torch.float32
+    if x.dtype != want or x.dim() != 2 or not x.is_contiguous():
+        raise ValueError(f"x must be a contiguous {want} [B, H] tensor")
+    B = x.shape[0]
+    if out is None:
+        out = torch.empty_like(x)
+    if workspace is None:
+        workspace = alloc_workspace(layer, B, device=x.device)
+    _check(lib().moe_decode_step(C.byref(layer.struct), _ptr(x), B, _ptr(idx), _ptr(w), C.byref(plan.struct),
+                                 _ptr(residual), _ptr(out), _ptr(workspace), workspace.numel(),
+                                 _stream(stream)), "moe_decode_step")
+    return out
+
+
+def expert_gate_up(layer: DeviceLayer, x: torch.Tensor, plan: Plan, workspace: torch.Tensor, stream=None):
+    """moe_expert_gate_up: first half of decode_step (h into the workspace)."""
+    _check(lib().moe_expert_gate_up(C.byref(layer.struct), _ptr(x), x.shape[0], C.byref(plan.struct),
+                                    _ptr(workspace), workspace.numel(), _stream(stream)), "moe_expert_gate_up")
+
+
+def expert_down_combine(layer: DeviceLayer, n_tokens: int, idx: torch.Tensor, w: torch.Tensor, plan: Plan,
+                        out: torch.Tensor, workspace: torch.Tensor, residual: Optional[torch.Tensor] = None,
+                        stream=None):
+    """moe_expert_down_combine: second half of decode_step."""
+    _check(lib().moe_expert_down_combine(C.byref(layer.struct), n_tokens, _ptr(idx), _ptr(w), C.byref(plan.struct),
+                                         _ptr(residual), _ptr(out), _ptr(workspace), workspace.numel(),
+                                         _stream(stream)), "moe_expert_down_combine")
+    return out
+
+
+def decode_layer(layer: DeviceLayer, x: torch.Tensor, logits: torch.Tensor, plan: Optional[Plan] = None,
+                 workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                 residual: Optional[torch.Tensor] = None, bufs: Optional[dict] = None, stream=None):
+    """The three calls of one layer step: route, plan, expert block."""
+    bufs = bufs or {}
+    idx, w = route_topk(logits, layer.top_k, bufs.get("idx"), bufs.get("w"), stream=stream)
+    plan = expert_plan(idx, layer.n_experts, plan, stream=stream)
+    out = decode_step(layer, x, idx, w, plan, out=out, workspace=workspace, residual=residual, stream=stream)
+    return out, idx, w, plan

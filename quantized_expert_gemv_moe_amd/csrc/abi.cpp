@@ -1,0 +1,121 @@
+// Host-only part of the C ABI: argument validation, workspace sizing and
+// status strings.  Nothing here touches the device, so every check runs
+// (and is tested) without a GPU.  Validating shapes before dispatch instead
+// of failing inside a launch follows page "perf(moe): batched decode scales
+// 1.55x against 3.25x on dense", Implementation Notes (error handling).
+#include <stdint.h>
+
+#include "moe_internal.h"
+
+namespace moe {
+
+static bool pow2_le64(int v) { return v >= 1 && v <= 64 && (v & (v - 1)) == 0; }
+
+// Down projection (and any GEMV over K): fewest lanes per row, i.e. the most
+// chunks per lane (nv <= 4) with lanes per row a power of two.
+bool pick_geometry(int K, Geometry *g) {
+    if (K <= 0 || K % 64) return false;
+    const int kch = K / 32;
+    for (int nv = 4; nv >= 1; --nv) {
+        if (kch % nv == 0 && pow2_le64(kch / nv)) {
+            g->lpr = kch / nv;
+            g->nv = nv;
+            return true;
+        }
+    }
+    return false;
+}
+
+// Gate/up projection: a whole wave per row when the row is 64..256 chunks
+// (one reduction per row serves both matrices and all tokens in registers),
+// otherwise the generic choice.
+bool pick_geometry_gate_up(int K, Geometry *g) {
+    if (K <= 0 || K % 64) return false;
+    const int kch = K / 32;
+    if (kch % 64 == 0 && kch / 64 <= 4) {
+        g->lpr = 64;
+        g->nv = kch / 64;
+        return true;
+    }
+    return pick_geometry(K, g);
+}
+
+static bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+moe_status check_layer(const moe_layer_t *L) {
+    if (!L) return MOE_ERR_INVALID_ARG;
+    if (L->hidden <= 0 || L->dff <= 0 || L->n_experts < 1 || L->top_k < 1)
+        return MOE_ERR_INVALID_ARG;
+    if (L->n_experts > MOE_MAX_EXPERTS) return MOE_ERR_UNSUPPORTED;
+    if (L->top_k > L->n_experts) return MOE_ERR_INVALID_ARG;
+    if (L->top_k > MOE_MAX_TOP_K) return MOE_ERR_UNSUPPORTED;
+    if (L->bits != 4 || L->group_size != 64) return MOE_ERR_UNSUPPORTED;
+    if (L->hidden % 64 || L->dff % 64) return MOE_ERR_UNSUPPORTED;
+    if (L->act_dtype != MOE_DTYPE_F32 && L->act_dtype != MOE_DTYPE_BF16) return MOE_ERR_INVALID_ARG;
+    if (!(L->clamp_limit >= 0.0f) || L->clamp_limit > 3.0e38f) return MOE_ERR_INVALID_ARG;
+    const void *q[3] = {L->gate_q, L->up_q, L->down_q};
+    for (const void *p : q)
+        if (!p || !aligned(p, 16)) return MOE_ERR_INVALID_ARG;
+    const void *sb[6] = {L->gate_s, L->gate_b, L->up_s, L->up_b, L->down_s, L->down_b};
+    for (const void *p : sb)
+        if (!p || !aligned(p, 4)) return MOE_ERR_INVALID_ARG;
+    if (L->expert_scale && !aligned(L->expert_scale, 4)) return MOE_ERR_INVALID_ARG;
+    Geometry g;
+    if (!pick_geometry_gate_up(L->hidden, &g) || !pick_geometry(L->dff, &g)) return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+
+moe_status check_route_args(const void *logits, int32_t n_tokens, int32_t n_experts,
+                            int32_t top_k, const void *idx, const void *w) {
+    if (n_tokens < 0 || n_experts < 1 || top_k < 1 || top_k > n_experts) return MOE_ERR_INVALID_ARG;
+    if (n_experts > MOE_MAX_EXPERTS || top_k > MOE_MAX_TOP_K) return MOE_ERR_UNSUPPORTED;
+    if (n_tokens > 0 && (!logits || !idx || !w)) return MOE_ERR_INVALID_ARG;
+    if ((int64_t)n_tokens * top_k > INT32_MAX / 2) return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+
+moe_status check_plan_args(const void *idx, int32_t n_tokens, int32_t n_experts, int32_t top_k,
+                           const moe_plan_t *plan) {
+    if (n_tokens < 0 || n_experts < 1 || top_k < 1 || top_k > n_experts) return MOE_ERR_INVALID_ARG;
+    if (n_experts > MOE_MAX_EXPERTS || top_k > MOE_MAX_TOP_K) return MOE_ERR_UNSUPPORTED;
+    if (!plan || !plan->counts || !plan->offsets || !plan->unique_experts || !plan->n_unique)
+        return MOE_ERR_INVALID_ARG;
+    if (n_tokens > 0 && (!idx || !plan->sorted_slots)) return MOE_ERR_INVALID_ARG;
+    if ((int64_t)n_tokens * top_k > INT32_MAX / 2) return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+
+Workspace workspace_layout(const moe_layer_t *L, int64_t max_tokens) {
+    Workspace w{0, 0, 0};
+    const size_t slots = (size_t)max_tokens * (size_t)L->top_k;
+    w.h_off = 0;
+    w.y_off = align256(slots * (size_t)L->dff * sizeof(float));
+    w.total = w.y_off + align256(slots * (size_t)L->hidden * sizeof(float));
+    return w;
+}
+
+}  // namespace moe
+
+extern "C" {
+
+size_t moe_workspace_size(const moe_layer_t *layer, int32_t max_tokens) {
+    if (moe::check_layer(layer) != MOE_OK || max_tokens < 0) return 0;
+    return moe::workspace_layout(layer, max_tokens).total;
+}
+
+moe_status moe_layer_check(const moe_layer_t *layer) { return moe::check_layer(layer); }
+
+const char *moe_status_str(moe_status s) {
+    switch (s) {
+        case MOE_OK: return "ok";
+        case MOE_ERR_INVALID_ARG: return "invalid argument";
+        case MOE_ERR_UNSUPPORTED: return "unsupported configuration (caller falls back)";
+        case MOE_ERR_WORKSPACE: return "workspace too small";
+        case MOE_ERR_DEVICE: return "device launch failed";
+    }
+    return "unknown status";
+}
+
+int32_t moe_abi_version(void) { return 1; }
+
+}  // extern "C"

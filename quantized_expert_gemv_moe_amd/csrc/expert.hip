@@ -1,0 +1,637 @@
+// Expert kernels of one decode step (gfx950) and moe_decode_step.
+//
+// The expert block the pages turn on is the SwitchGLU expert evaluated once
+// per (token, k) slot at M = 1 (page "perf(moe): attribute the MoE decode
+// gap at the M = 1 expert gather", Problem / Background), with the
+// deepseek_v4 clamp stage and the inkling expert-scale sidecars named on
+// the same page, and a token dimension whose outputs are summed over k per
+// token with fp32 partials and one final rounding (page "perf(moe): batched
+// decode scales 1.55x against 3.25x on dense", Proposed Solution and
+// Implementation Notes).  Every kernel here walks the *distinct* experts of
+// the plan, so an expert's weights are streamed from HBM once per step for
+// all the tokens routed to it, and each workgroup keeps its weights in
+// registers while it loops over those tokens.
+//
+//   gate_up : (distinct expert, block of dff rows) per one-wave workgroup.
+//             A row is read as 16-byte chunks by LPR lanes (64 for hidden
+//             2048..8192).  4-bit weights are unpacked in registers; bf16
+//             activations go through v_dot2_f32_bf16 with the nibbles
+//             turned into bf16 pairs of value 128 + q, the offset folded
+//             back with the chunk's activation sum; fp32 activations use
+//             exact fp32 FMAs.  The group bias is folded as bias * sum(x).
+//             Gate and up share the activations; SiLU(g) * u is written as
+//             fp32 h per slot.
+//   down    : (distinct expert, block of hidden rows) per 4-wave workgroup.
+//             h of the expert's slots and its per-group sums are staged in
+//             LDS; exact fp32 FMAs (h is never rounded to bf16).
+//   combine : out[t] = sum_j w[t][j] * y[t*k+j] in j order, one rounding.
+#include <hip/hip_runtime.h>
+#include <math.h>
+
+#include "device_util.h"
+#include "moe_internal.h"
+
+namespace moe {
+
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+
+struct PlanView {
+    const int *offsets;
+    const int *sorted_slots;
+    const int *unique_experts;
+    const int *n_unique;
+};
+
+struct GateUpArgs {
+    const uint4 *gate_q, *up_q;
+    const uint16_t *gate_s, *gate_b, *up_s, *up_b;
+    const float *expert_scale;
+    float clamp_limit;
+    const void *x;
+    PlanView plan;
+    float *h;
+    int hidden, dff, n_experts, top_k, n_slots;
+};
+
+struct DownArgs {
+    const uint4 *down_q;
+    const uint16_t *down_s, *down_b;
+    const float *h;
+    PlanView plan;
+    float *y;
+    int hidden, dff, n_experts, n_slots, slots_per_stage;
+};
+
+// Resolve the distinct expert of this workgroup; false when past the end or
+// when the plan is malformed (never indexes out of bounds).
+__device__ __forceinline__ bool plan_expert(const PlanView &p, int u, int n_experts, int n_slots,
+                                            int *e, int *first, int *count) {
+    if (u >= p.n_unique[0]) return false;
+    const int ex = p.unique_experts[u];
+    if ((unsigned)ex >= (unsigned)n_experts) return false;
+    const int a = p.offsets[ex], b = p.offsets[ex + 1];
+    if (a < 0 || b > n_slots || a > b) return false;
+    *e = ex;
+    *first = a;
+    *count = b - a;
+    return true;
+}
+
+// Streaming 16-byte load of weights that are read once per step.
+__device__ __forceinline__ uint4 load_stream(const uint4 *p) {
+    typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+    const v4u v = __builtin_nontemporal_load((const v4u *)p);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                           __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+// Eight nibbles of `w` against eight bf16 activations given as the pairs
+// xp[p] = (x[p], x[p + 4]).  Each nibble pair becomes a bf16 pair of value
+// (128 + q[p], 128 + q[p + 4]) by masking into the mantissa of 128.0; the
+// products are exact in fp32.
+__device__ __forceinline__ float dot8_q4_bf16(uint32_t w, const uint32_t *xp, float acc) {
+    const uint32_t M = 0x000F000Fu, B = 0x43004300u;
+    acc = dot2_bf16((w & M) | B, xp[0], acc);
+    acc = dot2_bf16(((w >> 4) & M) | B, xp[1], acc);
+    acc = dot2_bf16(((w >> 8) & M) | B, xp[2], acc);
+    acc = dot2_bf16(((w >> 12) & M) | B, xp[3], acc);
+    return acc;
+}
+
+// sum_i (128 + q_i) x_i over the 32 weights of one 16-byte chunk.
+__device__ __forceinline__ float dot32_q4_bf16(uint4 q, const uint32_t *xp) {
+    const float a0 = dot8_q4_bf16(q.x, xp + 0, 0.f);
+    const float a1 = dot8_q4_bf16(q.y, xp + 4, 0.f);
+    const float a2 = dot8_q4_bf16(q.z, xp + 8, 0.f);
+    const float a3 = dot8_q4_bf16(q.w, xp + 12, 0.f);
+    return (a0 + a1) + (a2 + a3);
+}
+
+// 32 bf16 activations starting at element c0 of row xr: the 16 pairs used by
+// dot8_q4_bf16 and their fp32 sum.
+__device__ __forceinline__ float load_x32_bf16_pairs(const uint16_t *x, size_t xr, int c0,
+                                                     uint32_t *xp) {
+    const uint4 *p = (const uint4 *)(x + xr + c0);
+    float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint4 w = p[i];  // elements 8i .. 8i+7 as (x0,x1),(x2,x3),(x4,x5),(x6,x7)
+        xp[4 * i + 0] = (w.x & 0xFFFFu) | (w.z << 16);
+        xp[4 * i + 1] = (w.x >> 16) | (w.z & 0xFFFF0000u);
+        xp[4 * i + 2] = (w.y & 0xFFFFu) | (w.w << 16);
+        xp[4 * i + 3] = (w.y >> 16) | (w.w & 0xFFFF0000u);
+        s0 += (bf16_bits_to_f32(w.x & 0xFFFFu) + bf16_bits_to_f32(w.x >> 16)) +
+              (bf16_bits_to_f32(w.y & 0xFFFFu) + bf16_bits_to_f32(w.y >> 16));
+        s1 += (bf16_bits_to_f32(w.z & 0xFFFFu) + bf16_bits_to_f32(w.z >> 16)) +
+              (bf16_bits_to_f32(w.w & 0xFFFFu) + bf16_bits_to_f32(w.w >> 16));
+    }
+    return s0 + s1;
+}
+
+// 32 fp32 activations starting at element c0 of row xr and their sum.
+__device__ __forceinline__ float load_x32_f32(const float *x, size_t xr, int c0, float *dst) {
+    const float4 *p = (const float4 *)(x + xr + c0);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float4 w = p[i];
+        dst[4 * i + 0] = w.x;
+        dst[4 * i + 1] = w.y;
+        dst[4 * i + 2] = w.z;
+        dst[4 * i + 3] = w.w;
+    }
+    float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        s0 += dst[4 * i + 0];
+        s1 += dst[4 * i + 1];
+        s2 += dst[4 * i + 2];
+        s3 += dst[4 * i + 3];
+    }
+    return (s0 + s1) + (s2 + s3);
+}
+
+// ------------------------------------------------------- cross-lane sums
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppQuad1032 = 0xB1;  // quad_perm [1,0,3,2]
+constexpr int kDppQuad2301 = 0x4E;  // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;
+constexpr int kDppMirror = 0x140;
+
+// Sum over aligned segments of LPR lanes; every lane of a segment gets the
+// same value (each step adds the same two numbers on both partner lanes).
+template <int LPR>
+__device__ __forceinline__ float seg_sum(float v) {
+    if constexpr (LPR >= 2) v += dpp<kDppQuad1032>(v);
+    if constexpr (LPR >= 4) v += dpp<kDppQuad2301>(v);
+    if constexpr (LPR >= 8) v += dpp<kDppHalfMirror>(v);
+    if constexpr (LPR >= 16) v += dpp<kDppMirror>(v);
+    if constexpr (LPR >= 32) v += __shfl_xor(v, 16, kWave);
+    if constexpr (LPR >= 64) v += __shfl_xor(v, 32, kWave);
+    return v;
+}
+
+// Sum of lo and hi 32-lane halves of a and b at once: lanes 0..31 return
+// a[l] + a[l+32], lanes 32..63 return b[l-32] + b[l] (v_permlane32_swap).
+__device__ __forceinline__ float swap32_sum(float a, float b) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Same on 16-lane rows: rows (0,1) of a go to row 0, of b to row 1, rows
+// (2,3) of a to row 2, of b to row 3 (v_permlane16_swap).
+__device__ __forceinline__ float swap16_sum(float a, float b) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Wave-wide sums of eight per-lane values at once.  Lane l returns the total
+// of v[2 * (l >> 4) + ((l >> 3) & 1)]: lanes 16r..16r+7 hold v[2r] and lanes
+// 16r+8..16r+15 hold v[2r+1].  ~23 VALU ops instead of 8 separate trees.
+__device__ __forceinline__ float wave_sum8(const float *v) {
+    const int lane = threadIdx.x & (kWave - 1);
+    float w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = swap32_sum(v[i], v[i + 4]);
+    // w[i]: lanes 0..31 partial of v[i], lanes 32..63 partial of v[i+4]
+    const float z0 = swap16_sum(w[0], w[2]);  // rows: v0 v2 v4 v6
+    const float z1 = swap16_sum(w[1], w[3]);  // rows: v1 v3 v5 v7
+    const bool upper = lane & 8;
+    const float t = upper ? z1 : z0;
+    const float s = upper ? z0 : z1;
+    float m = t + dpp<kDppMirror>(s);
+    m += dpp<kDppHalfMirror>(m);
+    m += dpp<kDppQuad2301>(m);
+    m += dpp<kDppQuad1032>(m);
+    return m;
+}
+
+// ---------------------------------------------------------------- gate+up
+
+__device__ __forceinline__ float silu_mul(float g, float u, float sc, float lim) {
+    g *= sc;
+    u *= sc;
+    if (lim > 0.f) {
+        g = fminf(fmaxf(g, -lim), lim);
+        u = fminf(fmaxf(u, -lim), lim);
+    }
+    return g / (1.f + expf(-g)) * u;
+}
+
+// One wave per workgroup.  LPR lanes per row, NV chunks per lane, RI rows
+// per segment; TCH tokens' activations in registers at a time.
+template <int LPR, int NV, int RI, bool XBF16>
+__global__ __launch_bounds__(kWave) void gate_up_kernel(GateUpArgs a) {
+    constexpr int RPI = kWave / LPR;  // rows per wave-wide pass
+    constexpr int ROWS_WG = RPI * RI;
+    constexpr int TCH = (XBF16 && NV == 1) ? 2 : 1;
+    constexpr bool WAVE8 = (LPR == kWave && RI == 4);
+    int e, first, count;
+    if (!plan_expert(a.plan, blockIdx.y, a.n_experts, a.n_slots, &e, &first, &count)) return;
+
+    const int lane = threadIdx.x;
+    const int sl = lane % LPR;
+    const int row0 = blockIdx.x * ROWS_WG + lane / LPR;
+    const int H = a.hidden, F = a.dff;
+    const int qrow = H / 32, grow = H / kGroup;
+
+    uint4 wg[RI][NV], wu[RI][NV];
+    float sg[RI][NV], bg[RI][NV], su[RI][NV], bu[RI][NV];
+#pragma unroll
+    for (int r = 0; r < RI; ++r) {
+        const int row = row0 + r * RPI;
+        const int rr = row < F ? row : F - 1;
+        const size_t rq = ((size_t)e * F + rr) * qrow;
+        const size_t rs = ((size_t)e * F + rr) * grow;
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+            const int ch = v * LPR + sl;
+            wg[r][v] = load_stream(a.gate_q + rq + ch);
+            wu[r][v] = load_stream(a.up_q + rq + ch);
+            sg[r][v] = f16_bits_to_f32(a.gate_s[rs + ch / 2]);
+            bg[r][v] = f16_bits_to_f32(a.gate_b[rs + ch / 2]);
+            su[r][v] = f16_bits_to_f32(a.up_s[rs + ch / 2]);
+            bu[r][v] = f16_bits_to_f32(a.up_b[rs + ch / 2]);
+            if constexpr (XBF16) {  // fold the +128 of the bf16 nibble trick into the bias
+                bg[r][v] = fmaf(-128.f, sg[r][v], bg[r][v]);
+                bu[r][v] = fmaf(-128.f, su[r][v], bu[r][v]);
+            }
+        }
+    }
+    const float sc = a.expert_scale ? a.expert_scale[e] : 1.f;
+    const float lim = a.clamp_limit;
+
+    for (int t0 = 0; t0 < count; t0 += TCH) {
+        int slot[TCH];
+        float xs[TCH][NV];
+        uint32_t xp[XBF16 ? TCH : 1][XBF16 ? NV : 1][16];
+        float xf[XBF16 ? 1 : TCH][XBF16 ? 1 : NV][32];
+#pragma unroll
+        for (int i = 0; i < TCH; ++i) {
+            slot[i] = -1;
+            if (i > 0 && t0 + i >= count) break;  // uniform: the chunk's tail is empty
+            slot[i] = a.plan.sorted_slots[first + t0 + i];
+            if ((unsigned)slot[i] >= (unsigned)a.n_slots) slot[i] = 0;  // malformed plan: stay in bounds
+            const size_t xr = (size_t)(slot[i] / a.top_k) * H;
+#pragma unroll
+            for (int v = 0; v < NV; ++v) {
+                const int c0 = (v * LPR + sl) * 32;
+                if constexpr (XBF16)
+                    xs[i][v] = load_x32_bf16_pairs((const uint16_t *)a.x, xr, c0, xp[i][v]);
+                else
+                    xs[i][v] = load_x32_f32((const float *)a.x, xr, c0, xf[i][v]);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < TCH; ++i) {
+            if (i > 0 && t0 + i >= count) break;
+            float part[2 * RI];
+#pragma unroll
+            for (int r = 0; r < RI; ++r) {
+                float g = 0.f, u = 0.f;
+#pragma unroll
+                for (int v = 0; v < NV; ++v) {
+                    float dg, du;
+                    if constexpr (XBF16) {
+                        dg = dot32_q4_bf16(wg[r][v], xp[i][v]);
+                        du = dot32_q4_bf16(wu[r][v], xp[i][v]);
+                    } else {
+                        dg = dot32_q4(wg[r][v], xf[i][v]);
+                        du = dot32_q4(wu[r][v], xf[i][v]);
+                    }
+                    g += fmaf(sg[r][v], dg, bg[r][v] * xs[i][v]);
+                    u += fmaf(su[r][v], du, bu[r][v] * xs[i][v]);
+                }
+                part[2 * r] = g;
+                part[2 * r + 1] = u;
+            }
+            if constexpr (WAVE8) {
+                const float tot = wave_sum8(part);
+                const float other = dpp<kDppMirror>(tot);  // lane 16r reads lane 16r+15 (the u)
+                const int r = lane >> 4;
+                const int row = row0 + r * RPI;
+                if ((lane & 15) == 0 && row < F)
+                    a.h[(size_t)slot[i] * F + row] = silu_mul(tot, other, sc, lim);
+            } else {
+#pragma unroll
+                for (int r = 0; r < RI; ++r) {
+                    const float g = seg_sum<LPR>(part[2 * r]);
+                    const float u = seg_sum<LPR>(part[2 * r + 1]);
+                    const int row = row0 + r * RPI;
+                    if (sl == 0 && row < F)
+                        a.h[(size_t)slot[i] * F + row] = silu_mul(g, u, sc, lim);
+                }
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------------- down
+
+// Four waves per workgroup.  h of up to `slots_per_stage` slots and its
+// sums per 64-group live in dynamic LDS: [S][F] floats, then [S][F/64].
+template <int LPR, int NV, int RI>
+__global__ __launch_bounds__(kBlock) void down_kernel(DownArgs a) {
+    constexpr int RPI = kWave / LPR;
+    constexpr int ROWS_WG = RPI * RI * (kBlock / kWave);
+    extern __shared__ float lds[];
+    int e, first, count;
+    if (!plan_expert(a.plan, blockIdx.y, a.n_experts, a.n_slots, &e, &first, &count)) return;
+
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int sl = lane % LPR;
+    const int row0 = blockIdx.x * ROWS_WG + wave * RPI * RI + lane / LPR;
+    const int H = a.hidden, F = a.dff;
+    const int qrow = F / 32, grow = F / kGroup;
+    const int S = a.slots_per_stage;
+    float *hl = lds;               // [S][F]
+    float *gs = lds + (size_t)S * F;  // [S][F/64]
+
+    uint4 wd[RI][NV];
+    float sd[RI][NV], bd[RI][NV];
+#pragma unroll
+    for (int r = 0; r < RI; ++r) {
+        const int row = row0 + r * RPI;
+        const int rr = row < H ? row : H - 1;
+        const size_t rq = ((size_t)e * H + rr) * qrow;
+        const size_t rs = ((size_t)e * H + rr) * grow;
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+            const int ch = v * LPR + sl;
+            wd[r][v] = load_stream(a.down_q + rq + ch);
+            sd[r][v] = f16_bits_to_f32(a.down_s[rs + ch / 2]);
+            // the bias of a group is applied once, by the lane holding its even chunk
+            bd[r][v] = (ch & 1) ? 0.f : f16_bits_to_f32(a.down_b[rs + ch / 2]);
+        }
+    }
+
+    for (int s0 = 0; s0 < count; s0 += S) {
+        const int ns = count - s0 < S ? count - s0 : S;
+        __syncthreads();  // previous stage fully consumed
+        const int f4 = F / 4;
+        for (int i = threadIdx.x; i < ns * f4; i += kBlock) {
+            const int j = i / f4, c = i - j * f4;
+            int slot = a.plan.sorted_slots[first + s0 + j];
+            if ((unsigned)slot >= (unsigned)a.n_slots) slot = 0;  // malformed plan: stay in bounds
+            ((float4 *)(hl + (size_t)j * F))[c] = ((const float4 *)(a.h + (size_t)slot * F))[c];
+        }
+        __syncthreads();
+        // per-group sums of h: two threads per group, 32 elements each
+        for (int i = threadIdx.x; i < ns * grow * 2; i += kBlock) {
+            const int j = i / (grow * 2), g = (i / 2) % grow, half = i & 1;
+            const float *src = hl + (size_t)j * F + g * kGroup + half * 32;
+            float s = 0.f;
+#pragma unroll
+            for (int c = 0; c < 32; ++c) s += src[c];
+            s += dpp<kDppQuad1032>(s);  // partner thread holds the other half
+            if (!half) gs[j * grow + g] = s;
+        }
+        __syncthreads();
+        for (int j = 0; j < ns; ++j) {
+            int slot = a.plan.sorted_slots[first + s0 + j];
+            if ((unsigned)slot >= (unsigned)a.n_slots) slot = 0;
+            float hv[NV][32], hsum[NV];
+#pragma unroll
+            for (int v = 0; v < NV; ++v) {
+                const int ch = v * LPR + sl;
+                const float4 *p = (const float4 *)(hl + (size_t)j * F + ch * 32);
+#pragma unroll
+                for (int c = 0; c < 8; ++c) {
+                    const float4 q = p[c];
+                    hv[v][4 * c + 0] = q.x;
+                    hv[v][4 * c + 1] = q.y;
+                    hv[v][4 * c + 2] = q.z;
+                    hv[v][4 * c + 3] = q.w;
+                }
+                hsum[v] = gs[j * grow + ch / 2];
+            }
+#pragma unroll
+            for (int r = 0; r < RI; ++r) {
+                float y = 0.f;
+#pragma unroll
+                for (int v = 0; v < NV; ++v) y += fmaf(sd[r][v], dot32_q4(wd[r][v], hv[v]), bd[r][v] * hsum[v]);
+                y = seg_sum<LPR>(y);
+                const int row = row0 + r * RPI;
+                if (sl == 0 && row < H) a.y[(size_t)slot * H + row] = y;
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------- combine
+
+template <bool BF16>
+__global__ __launch_bounds__(kBlock) void combine_kernel(const float *__restrict__ y,
+                                                         const int *__restrict__ topk_idx,
+                                                         const float *__restrict__ topk_w,
+                                                         const void *residual, void *out,
+                                                         int hidden, int top_k, int n_experts) {
+    const int t = blockIdx.y;
+    const int m = blockIdx.x * kBlock + threadIdx.x;
+    if (m >= hidden) return;
+    float acc = 0.f;
+    bool bad = false;
+    for (int j = 0; j < top_k; ++j) {
+        const int s = t * top_k + j;
+        bad |= (unsigned)topk_idx[s] >= (unsigned)n_experts;
+        acc = fmaf(topk_w[s], y[(size_t)s * hidden + m], acc);
+    }
+    if (bad) acc = __builtin_nanf("");
+    const size_t o = (size_t)t * hidden + m;
+    if constexpr (BF16) {
+        uint16_t r = f32_to_bf16_rne(acc);
+        if (residual) {
+            const float sum = bf16_bits_to_f32(((const uint16_t *)residual)[o]) + bf16_bits_to_f32(r);
+            r = f32_to_bf16_rne(sum);
+        }
+        ((uint16_t *)out)[o] = r;
+    } else {
+        if (residual) acc = ((const float *)residual)[o] + acc;
+        ((float *)out)[o] = acc;
+    }
+}
+
+// ------------------------------------------------------------ dispatching
+
+template <int LPR, int NV>
+static moe_status launch_gate_up(const GateUpArgs &a, bool bf16, int groups_y, hipStream_t s) {
+    // rows per lane segment: four for the whole-wave rows (the 8-value
+    // transposed reduction), fewer when a lane holds many chunks
+    constexpr int RI = (LPR == kWave) ? (NV <= 2 ? 4 : 2) : (NV <= 2 ? 2 : 1);
+    constexpr int rows = (kWave / LPR) * RI;
+    const dim3 grid((a.dff + rows - 1) / rows, groups_y);
+    if (bf16)
+        hipLaunchKernelGGL((gate_up_kernel<LPR, NV, RI, true>), grid, dim3(kWave), 0, s, a);
+    else
+        hipLaunchKernelGGL((gate_up_kernel<LPR, NV, RI, false>), grid, dim3(kWave), 0, s, a);
+    return MOE_OK;
+}
+
+constexpr size_t kDownLdsBytes = 32768;
+
+template <int LPR, int NV>
+static moe_status launch_down(DownArgs a, int groups_y, int max_count, hipStream_t s) {
+    constexpr int RI = 1;
+    constexpr int rows = (kWave / LPR) * RI * (kBlock / kWave);
+    const size_t per_slot = ((size_t)a.dff + a.dff / kGroup) * sizeof(float);
+    int S = (int)(kDownLdsBytes / per_slot);
+    if (S < 1) return MOE_ERR_UNSUPPORTED;
+    if (S > max_count) S = max_count;
+    a.slots_per_stage = S;
+    const dim3 grid((a.hidden + rows - 1) / rows, groups_y);
+    hipLaunchKernelGGL((down_kernel<LPR, NV, RI>), grid, dim3(kBlock), S * per_slot, s, a);
+    return MOE_OK;
+}
+
+// Every (lanes per row, chunks per lane) pair that the geometry pickers return.
+#define MOE_GEOMETRY_SWITCH(G, RET, FN, ...)                           \
+    switch ((G).lpr * 8 + (G).nv) {                                    \
+        case 64 * 8 + 1: RET = FN<64, 1>(__VA_ARGS__); break;          \
+        case 64 * 8 + 2: RET = FN<64, 2>(__VA_ARGS__); break;          \
+        case 64 * 8 + 3: RET = FN<64, 3>(__VA_ARGS__); break;          \
+        case 64 * 8 + 4: RET = FN<64, 4>(__VA_ARGS__); break;          \
+        case 32 * 8 + 3: RET = FN<32, 3>(__VA_ARGS__); break;          \
+        case 32 * 8 + 4: RET = FN<32, 4>(__VA_ARGS__); break;          \
+        case 16 * 8 + 3: RET = FN<16, 3>(__VA_ARGS__); break;          \
+        case 16 * 8 + 4: RET = FN<16, 4>(__VA_ARGS__); break;          \
+        case 8 * 8 + 3: RET = FN<8, 3>(__VA_ARGS__); break;            \
+        case 8 * 8 + 4: RET = FN<8, 4>(__VA_ARGS__); break;            \
+        case 4 * 8 + 3: RET = FN<4, 3>(__VA_ARGS__); break;            \
+        case 4 * 8 + 4: RET = FN<4, 4>(__VA_ARGS__); break;            \
+        case 2 * 8 + 3: RET = FN<2, 3>(__VA_ARGS__); break;            \
+        case 2 * 8 + 4: RET = FN<2, 4>(__VA_ARGS__); break;            \
+        case 1 * 8 + 2: RET = FN<1, 2>(__VA_ARGS__); break;            \
+        case 1 * 8 + 3: RET = FN<1, 3>(__VA_ARGS__); break;            \
+        case 1 * 8 + 4: RET = FN<1, 4>(__VA_ARGS__); break;            \
+        default: RET = MOE_ERR_UNSUPPORTED; break;                     \
+    }
+
+// Host-side checks shared by the three expert entry points.
+static moe_status check_step(const moe_layer_t *layer, int32_t n_tokens, const moe_plan_t *plan,
+                             void *workspace, size_t workspace_bytes) {
+    moe_status st = check_layer(layer);
+    if (st != MOE_OK) return st;
+    if (n_tokens < 0) return MOE_ERR_INVALID_ARG;
+    if ((int64_t)n_tokens * layer->top_k > INT32_MAX / 2) return MOE_ERR_UNSUPPORTED;
+    if (n_tokens == 0) return MOE_OK;
+    if (!plan || !plan->offsets || !plan->sorted_slots || !plan->unique_experts || !plan->n_unique)
+        return MOE_ERR_INVALID_ARG;
+    if (!workspace || (uintptr_t)workspace % 256) return MOE_ERR_INVALID_ARG;
+    if (workspace_bytes < workspace_layout(layer, n_tokens).total) return MOE_ERR_WORKSPACE;
+    return MOE_OK;
+}
+
+static PlanView plan_view(const moe_plan_t *plan) {
+    return PlanView{plan->offsets, plan->sorted_slots, plan->unique_experts, plan->n_unique};
+}
+
+static int groups_y_of(const moe_layer_t *layer, int n_tokens) {
+    const int n_slots = n_tokens * layer->top_k;
+    return n_slots < layer->n_experts ? n_slots : layer->n_experts;
+}
+
+static moe_status enqueue_gate_up(const moe_layer_t *layer, const void *x, int n_tokens,
+                                  const moe_plan_t *plan, void *workspace, hipStream_t stream) {
+    Geometry gu;
+    pick_geometry_gate_up(layer->hidden, &gu);
+    const Workspace ws = workspace_layout(layer, n_tokens);
+    float *h = (float *)((char *)workspace + ws.h_off);
+    GateUpArgs ga{(const uint4 *)layer->gate_q, (const uint4 *)layer->up_q, layer->gate_s,
+                  layer->gate_b, layer->up_s, layer->up_b, layer->expert_scale,
+                  layer->clamp_limit, x, plan_view(plan), h, layer->hidden, layer->dff,
+                  layer->n_experts, layer->top_k, n_tokens * layer->top_k};
+    const bool bf16 = layer->act_dtype == MOE_DTYPE_BF16;
+    moe_status st;
+    MOE_GEOMETRY_SWITCH(gu, st, launch_gate_up, ga, bf16, groups_y_of(layer, n_tokens), stream)
+    return st;
+}
+
+static moe_status enqueue_down_combine(const moe_layer_t *layer, int n_tokens, const int32_t *topk_idx,
+                                       const float *topk_w, const moe_plan_t *plan,
+                                       const void *residual, void *out, void *workspace,
+                                       hipStream_t stream) {
+    Geometry gd;
+    pick_geometry(layer->dff, &gd);
+    const Workspace ws = workspace_layout(layer, n_tokens);
+    const float *h = (const float *)((char *)workspace + ws.h_off);
+    float *y = (float *)((char *)workspace + ws.y_off);
+    DownArgs da{(const uint4 *)layer->down_q, layer->down_s, layer->down_b, h, plan_view(plan), y,
+                layer->hidden, layer->dff, layer->n_experts, n_tokens * layer->top_k, 1};
+    moe_status st;
+    MOE_GEOMETRY_SWITCH(gd, st, launch_down, da, groups_y_of(layer, n_tokens), n_tokens, stream)
+    if (st != MOE_OK) return st;
+    const dim3 cgrid((layer->hidden + kBlock - 1) / kBlock, n_tokens);
+    if (layer->act_dtype == MOE_DTYPE_BF16)
+        hipLaunchKernelGGL(combine_kernel<true>, cgrid, dim3(kBlock), 0, stream, y, topk_idx, topk_w,
+                           residual, out, layer->hidden, layer->top_k, layer->n_experts);
+    else
+        hipLaunchKernelGGL(combine_kernel<false>, cgrid, dim3(kBlock), 0, stream, y, topk_idx, topk_w,
+                           residual, out, layer->hidden, layer->top_k, layer->n_experts);
+    return MOE_OK;
+}
+
+static moe_status check_x(const void *x) {
+    if (!x || (uintptr_t)x % 16) return MOE_ERR_INVALID_ARG;
+    return MOE_OK;
+}
+
+static moe_status check_out(const void *x, const int32_t *topk_idx, const float *topk_w,
+                            const void *residual, const void *out) {
+    if (!topk_idx || !topk_w || !out) return MOE_ERR_INVALID_ARG;
+    if (out == x || (residual && out == residual)) return MOE_ERR_INVALID_ARG;
+    if ((uintptr_t)out % 4 || (residual && (uintptr_t)residual % 4)) return MOE_ERR_INVALID_ARG;
+    return MOE_OK;
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" moe_status moe_expert_gate_up(const moe_layer_t *layer, const void *x, int32_t n_tokens,
+                                         const moe_plan_t *plan, void *workspace,
+                                         size_t workspace_bytes, void *hip_stream) {
+    moe_status st = check_step(layer, n_tokens, plan, workspace, workspace_bytes);
+    if (st != MOE_OK || n_tokens == 0) return st;
+    if ((st = check_x(x)) != MOE_OK) return st;
+    st = enqueue_gate_up(layer, x, n_tokens, plan, workspace, (hipStream_t)hip_stream);
+    if (st != MOE_OK) return st;
+    return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_DEVICE;
+}
+
+extern "C" moe_status moe_expert_down_combine(const moe_layer_t *layer, int32_t n_tokens,
+                                              const int32_t *topk_idx, const float *topk_w,
+                                              const moe_plan_t *plan, const void *residual,
+                                              void *out, void *workspace, size_t workspace_bytes,
+                                              void *hip_stream) {
+    moe_status st = check_step(layer, n_tokens, plan, workspace, workspace_bytes);
+    if (st != MOE_OK || n_tokens == 0) return st;
+    if ((st = check_out(nullptr, topk_idx, topk_w, residual, out)) != MOE_OK) return st;
+    st = enqueue_down_combine(layer, n_tokens, topk_idx, topk_w, plan, residual, out, workspace,
+                              (hipStream_t)hip_stream);
+    if (st != MOE_OK) return st;
+    return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_DEVICE;
+}
+
+extern "C" moe_status moe_decode_step(const moe_layer_t *layer, const void *x, int32_t n_tokens,
+                                      const int32_t *topk_idx, const float *topk_w,
+                                      const moe_plan_t *plan, const void *residual, void *out,
+                                      void *workspace, size_t workspace_bytes, void *hip_stream) {
+    moe_status st = check_step(layer, n_tokens, plan, workspace, workspace_bytes);
+    if (st != MOE_OK || n_tokens == 0) return st;
+    if ((st = check_x(x)) != MOE_OK) return st;
+    if ((st = check_out(x, topk_idx, topk_w, residual, out)) != MOE_OK) return st;
+    hipStream_t stream = (hipStream_t)hip_stream;
+    st = enqueue_gate_up(layer, x, n_tokens, plan, workspace, stream);
+    if (st != MOE_OK) return st;
+    st = enqueue_down_combine(layer, n_tokens, topk_idx, topk_w, plan, residual, out, workspace, stream);
+    if (st != MOE_OK) return st;
+    return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_DEVICE;
+}

@@ -1,0 +1,37 @@
+// Host-side helpers shared by the entry points (validation, geometry).
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "moe_decode.h"
+
+namespace moe {
+
+// Lane geometry of a GEMV over K inputs: a row is read as K/32 16-byte
+// chunks by `lpr` lanes (a power of two, 1..64), each lane taking `nv`
+// chunks (1..4), chunk c of a row going to lane c % lpr.
+struct Geometry {
+    int lpr;
+    int nv;
+};
+bool pick_geometry(int K, Geometry *g);
+bool pick_geometry_gate_up(int K, Geometry *g);
+
+// Validation without device access.
+moe_status check_layer(const moe_layer_t *layer);
+moe_status check_route_args(const void *logits, int32_t n_tokens, int32_t n_experts,
+                            int32_t top_k, const void *idx, const void *w);
+moe_status check_plan_args(const void *idx, int32_t n_tokens, int32_t n_experts,
+                           int32_t top_k, const moe_plan_t *plan);
+
+// Workspace layout of moe_decode_step: h [slots][dff] fp32, then the
+// per-slot expert outputs [slots][hidden] fp32, each 256-byte aligned.
+struct Workspace {
+    size_t h_off, y_off, total;
+};
+Workspace workspace_layout(const moe_layer_t *layer, int64_t max_tokens);
+
+constexpr size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+}  // namespace moe

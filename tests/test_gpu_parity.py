@@ -1,0 +1,257 @@
+"""GPU parity of the HIP path against the oracle, through the C ABI.
+
+Indices and the dedup plan bit-exact; router weights within 1e-6; outputs
+within relative L2 2e-3 of the fp64 oracle (plus the tighter diagnostic
+against the once-rounded oracle, see gpu_helpers).  Every workload shape at
+its full size, the routing regimes, and the edge cases.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import quantized_expert_gemv_moe_amd as moe
+from gpu_helpers import GpuRun, check_against_oracle, dev_x, host_bits, layer_for, log, rel_l2
+from moe_workloads import SHAPES, Shape, make_layer, make_logits, make_x
+from oracle import oracle
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    assert torch.cuda.is_available(), "GPU tests need a ROCm device"
+    moe.lib()
+    yield
+
+
+# ------------------------------------------------------------------ router
+ROUTER_CASES = [
+    ("toy", 1, "normal"), ("decode", 1, "normal"), ("cohort", 4, "sharing"), ("cohort", 8, "sharing"),
+    ("wide", 1, "normal"), ("wide", 4, "normal"), ("stack", 32, "zipf"), ("decode", 1000, "normal"),
+]
+
+
+@pytest.mark.parametrize("name,B,regime", ROUTER_CASES)
+def test_router_matches_oracle(name, B, regime):
+    sh = SHAPES[name]
+    lg = make_logits(sh, B, regime=regime, seed=21)
+    idx, w = moe.route_topk(torch.from_numpy(lg).cuda(), sh.top_k)
+    ridx, rw = oracle.route_topk(lg, sh.top_k)
+    assert np.array_equal(idx.cpu().numpy(), ridx)
+    assert np.abs(w.cpu().numpy() - rw).max() <= 1e-6
+    assert np.allclose(w.sum(dim=1).cpu().numpy(), 1.0, atol=1e-6)
+
+
+@pytest.mark.parametrize("E,k", [(8, 1), (8, 8), (64, 16), (1024, 16), (1024, 1), (100, 7), (1, 1)])
+def test_router_shapes_and_ties(E, k):
+    sh = Shape("r", 30, 64, 64, E, k, "f32")
+    lg = make_logits(sh, 37, seed=E + k)
+    lg[0] = 0.0                      # all tied: ids ascending
+    lg[1, ::3] = 1.0                 # partial ties
+    lg[2] = -lg[2]
+    idx, w = moe.route_topk(torch.from_numpy(lg).cuda(), k)
+    ridx, rw = oracle.route_topk(lg, k)
+    assert np.array_equal(idx.cpu().numpy(), ridx)
+    assert np.abs(w.cpu().numpy() - rw).max() <= 1e-6
+    assert idx.cpu().numpy()[0].tolist() == list(range(k))
+    if k == 1:
+        assert np.all(w.cpu().numpy() == 1.0)
+
+
+def test_router_empty_batch_is_a_no_op():
+    idx = torch.full((0, 8), -5, dtype=torch.int32, device="cuda")
+    w = torch.zeros((0, 8), dtype=torch.float32, device="cuda")
+    moe.route_topk(torch.zeros((0, 128), device="cuda"), 8, idx, w)
+    torch.cuda.synchronize()
+
+
+# --------------------------------------------------------------------- plan
+def plan_np(plan, n):
+    return dict(counts=plan.counts.cpu().numpy(), offsets=plan.offsets.cpu().numpy(),
+                sorted_slots=plan.sorted_slots[:n].cpu().numpy(),
+                unique_experts=plan.unique_experts.cpu().numpy(), n_unique=int(plan.n_unique.item()))
+
+
+@pytest.mark.parametrize("E,k,B,kind", [
+    (128, 8, 1, "router"), (128, 8, 4, "sharing"), (128, 8, 8, "disjoint"), (128, 8, 32, "zipf"),
+    (256, 6, 4, "router"), (8, 2, 1, "router"), (128, 8, 1024, "random"), (1024, 16, 512, "random"),
+    (3, 2, 100, "random"), (1, 1, 5, "random"), (128, 8, 16, "same"),
+])
+def test_plan_matches_oracle(E, k, B, kind):
+    sh = Shape("p", 31, 64, 64, E, k, "f32")
+    rng = np.random.default_rng(B * 7 + E)
+    if kind == "random":  # any ids, repeats within a token allowed
+        idx = rng.integers(0, E, (B, k)).astype(np.int32)
+    else:
+        regime = {"router": "normal"}.get(kind, kind)
+        idx, _ = oracle.route_topk(make_logits(sh, B, regime=regime, seed=5), k)
+    plan = moe.expert_plan(torch.from_numpy(idx).cuda(), E)
+    got = plan_np(plan, B * k)
+    ref = oracle.plan(idx, E)
+    for key in ("counts", "offsets", "sorted_slots", "unique_experts"):
+        assert np.array_equal(got[key], ref[key]), key
+    assert got["n_unique"] == ref["n_unique"]
+
+
+def test_plan_empty_batch():
+    plan = moe.Plan.allocate(16, 8)
+    plan.counts.fill_(7)
+    moe.expert_plan(torch.zeros((0, 4), dtype=torch.int32, device="cuda"), 16, plan)
+    got = plan_np(plan, 0)
+    assert got["n_unique"] == 0 and got["counts"].sum() == 0
+    assert np.all(got["offsets"] == 0) and np.all(got["unique_experts"] == -1)
+
+
+# ------------------------------------------------------- expert block parity
+DECODE_CASES = [
+    # (shape, B, regime, x scale)
+    ("toy", 1, "normal", 1.0),
+    ("toy", 3, "normal", 1.0),
+    ("decode", 1, "normal", 1.0),
+    ("cohort", 4, "sharing", 1.0),
+    ("cohort", 8, "sharing", 1.0),
+    ("cohort", 8, "normal", 1.0),
+    ("cohort", 8, "disjoint", 1.0),
+    ("cohort", 6, "same", 1.0),
+    ("wide", 1, "normal", 1.0),
+    ("wide", 4, "normal", 1.0),
+    ("wide", 2, "normal", 8.0),     # forced clamp: ~37 % of gate values beyond 10
+    ("stack", 32, "zipf", 1.0),
+]
+
+
+@pytest.mark.parametrize("name,B,regime,xs", DECODE_CASES)
+def test_decode_step_matches_oracle(name, B, regime, xs):
+    sh = SHAPES[name]
+    log(f"[case] decode {name} B={B} {regime} x*{xs}")
+    lg = make_logits(sh, B, regime=regime, seed=3)
+    L = layer_for(sh, lg, seed=3) if sh.n_experts > 8 else make_layer(sh, seed=3)
+    x = make_x(sh, B, seed=3, scale=xs)
+    run = GpuRun(L, x, lg)
+    check_against_oracle(L, x, lg, run, f"{name}/B{B}/{regime}/x{xs}")
+    if xs > 1.0:
+        h64 = oracle.decode_step(L, x, *oracle.route_topk(lg, sh.top_k), want_h=True)[1]
+        lim = 10.0 / (1 + np.exp(-10.0)) * 10.0
+        assert np.isclose(np.abs(h64).max(), lim) and np.isclose(np.abs(run.h).max(), lim, rtol=1e-6)
+
+
+@pytest.mark.parametrize("H,F,E,k,act", [
+    (256, 128, 8, 8, "f32"),       # k = E
+    (512, 192, 16, 1, "bf16"),     # k = 1; 4 lanes x 4 chunks per gate/up row, 2 x 3 per down row
+    (1024, 1536, 32, 4, "bf16"),   # 8 x 4 chunks per gate/up row, 16 x 3 per down row
+    (8192, 64, 4, 2, "bf16"),      # 4 chunks per lane in a whole-wave row; one lane per down row
+    (128, 4096, 4, 3, "f32"),      # one lane per gate/up row; one slot per LDS stage in down
+    (64, 64, 2, 2, "bf16"),        # smallest rows
+])
+def test_decode_step_other_shapes(H, F, E, k, act):
+    sh = Shape(f"s{H}x{F}", 32, H, F, E, k, act)
+    B = 5
+    lg = make_logits(sh, B, seed=H + F)
+    L = make_layer(sh, seed=H + F)
+    x = make_x(sh, B, seed=H + F)
+    run = GpuRun(L, x, lg)
+    check_against_oracle(L, x, lg, run, f"{H}x{F}x{E}x{k}/{act}")
+
+
+# --------------------------------------------------------------- invariants
+def test_determinism_batch_invariance_permutation_and_duplicates():
+    sh = SHAPES["cohort"]
+    B = 8
+    lg = make_logits(sh, B, regime="sharing", seed=9)
+    x = make_x(sh, B, seed=9)
+    dup_lg = np.repeat(lg[2:3], 4, axis=0)
+    L = layer_for(sh, np.concatenate([lg, dup_lg]), seed=9)
+    dl = moe.DeviceLayer.from_host(L)
+    a = GpuRun(L, x, lg, dl=dl)
+    b = GpuRun(L, x, lg, dl=dl)
+    assert np.array_equal(a.out, b.out), "run-to-run results differ"
+    for t in range(B):
+        one = GpuRun(L, x[t:t + 1], lg[t:t + 1], dl=dl)
+        assert np.array_equal(one.out[0], a.out[t]), f"token {t} alone differs from the batch"
+    perm = np.array([5, 2, 7, 0, 1, 6, 3, 4])
+    p = GpuRun(L, x[perm], lg[perm], dl=dl)
+    assert np.array_equal(p.out, a.out[perm])
+    d = GpuRun(L, np.repeat(x[2:3], 4, axis=0), dup_lg, dl=dl)
+    assert d.plan_np["n_unique"] == sh.top_k
+    assert np.all(d.out == d.out[0:1]) and np.array_equal(d.out[0], a.out[2])
+
+
+def test_batch_size_changes_between_calls_with_the_same_buffers():
+    sh = SHAPES["cohort"]
+    lgs = {B: make_logits(sh, B, seed=40 + B) for B in (4, 1, 8, 3)}
+    L = layer_for(sh, np.concatenate(list(lgs.values())), seed=40)
+    dl = moe.DeviceLayer.from_host(L)
+    plan = moe.Plan.allocate(sh.n_experts, 8 * sh.top_k)
+    ws = moe.alloc_workspace(dl, 8)
+    for B, lg in lgs.items():
+        x = make_x(sh, B, seed=40 + B)
+        out, idx, w, _ = moe.decode_layer(dl, dev_x(x), torch.from_numpy(lg).cuda(), plan=plan, workspace=ws)
+        ridx, rw = oracle.route_topk(lg, sh.top_k)
+        ref = oracle.decode_step(L, x, ridx, rw)
+        got = oracle.bf16_to_f64(host_bits(out))
+        assert np.array_equal(idx.cpu().numpy(), ridx)
+        assert rel_l2(got, ref) <= 2e-3, B
+
+
+def test_residual_stack_of_layers():
+    sh = SHAPES["stack"]
+    B, n_layers = 32, 4
+    lgs = [make_logits(sh, B, layer=l, regime="zipf", seed=11) for l in range(n_layers)]
+    layers = [layer_for(sh, lgs[l], layer=l, seed=11) for l in range(n_layers)]
+    x0 = make_x(sh, B, seed=11)
+    # oracle: the mirrored stack, and the per-layer inputs it saw
+    seen = []
+    ref = oracle.run_stack(layers, x0, lgs, sh.top_k, hook=lambda l, x, i, w, o: seen.append(x.copy()))
+    xt = dev_x(x0)
+    for l in range(n_layers):
+        dl = moe.DeviceLayer.from_host(layers[l])
+        nxt = torch.empty_like(xt)
+        moe.decode_layer(dl, xt, torch.from_numpy(lgs[l]).cuda(), residual=xt, out=nxt)
+        # teacher-forced: the same layer from the oracle's own input
+        tf = torch.empty_like(xt)
+        moe.decode_layer(dl, dev_x(seen[l]), torch.from_numpy(lgs[l]).cuda(), residual=dev_x(seen[l]), out=tf)
+        idx, w = oracle.route_topk(lgs[l], sh.top_k)
+        o64 = oracle.decode_step(layers[l], seen[l], idx, w)
+        want = oracle.bf16_to_f64(oracle.residual_bf16(seen[l], o64))
+        e = rel_l2(oracle.bf16_to_f64(host_bits(tf)) - oracle.bf16_to_f64(seen[l]),
+                   want - oracle.bf16_to_f64(seen[l]))
+        log(f"[stack] layer {l}: residual-branch rel L2 {e:.3g}")
+        assert e <= 2e-3
+        xt = nxt
+    got = oracle.bf16_to_f64(host_bits(xt))
+    e = rel_l2(got, oracle.bf16_to_f64(ref))
+    log(f"[stack] final x rel L2 {e:.3g}")
+    assert e <= 2e-3
+
+
+def test_invalid_expert_id_gives_nan_for_that_token_only():
+    sh = SHAPES["cohort"]
+    B = 3
+    lg = make_logits(sh, B, seed=12)
+    L = layer_for(sh, lg, seed=12)
+    dl = moe.DeviceLayer.from_host(L)
+    idx, w = oracle.route_topk(lg, sh.top_k)
+    bad = idx.copy()
+    bad[1, 3] = 5000          # out of range: left out of the plan, NaN for token 1
+    bad[2, 0] = -1
+    it = torch.from_numpy(bad).cuda()
+    wt = torch.from_numpy(w.astype(np.float32)).cuda()
+    plan = moe.expert_plan(it, sh.n_experts)
+    x = make_x(sh, B, seed=12)
+    out = moe.decode_step(dl, dev_x(x), it, wt, plan)
+    got = oracle.bf16_to_f64(host_bits(out))
+    assert np.isnan(got[1]).all() and np.isnan(got[2]).all()
+    ref = oracle.decode_step(L, x[:1], idx[:1], w[:1])
+    assert rel_l2(got[0], ref[0]) <= 2e-3
+
+
+def test_empty_batch_decode_step_is_a_no_op():
+    sh = SHAPES["toy"]
+    L = make_layer(sh, seed=1)
+    dl = moe.DeviceLayer.from_host(L)
+    out = torch.full((0, sh.hidden), 3.0, device="cuda")
+    plan = moe.Plan.allocate(sh.n_experts, 1)
+    moe.decode_step(dl, torch.zeros((0, sh.hidden), device="cuda"), torch.zeros((0, 2), dtype=torch.int32, device="cuda"),
+                    torch.zeros((0, 2), device="cuda"), plan, out=out, workspace=torch.empty(256, dtype=torch.uint8, device="cuda"))
+    torch.cuda.synchronize()
