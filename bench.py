@@ -1,8 +1,9 @@
 #!/usr/bin/env python3
 """Decode-step benchmark of the quantized-expert MoE block on one MI355X.
 
-A step is one pass of the whole hot path over one batch: moe_route_topk ->
-moe_expert_plan -> moe_expert_gate_up -> moe_expert_down_combine.  The
+A step is one pass of the whole hot path over one batch: moe_route_plan
+(router and cohort planner in one launch) -> moe_expert_gate_up ->
+moe_expert_down_combine.  The
 default workload is the single-token decode layer (hidden 2048, dff 768, 128
 experts, top-8, B = 1, affine int4 g64 weights, bf16 activations).  Steps
 rotate over R layer instances resident in HBM (48 by default, 16.3 GB of
@@ -115,8 +116,7 @@ class Rotation:
     def step(self, i):
         m = self.moe
         L = self.layers[i]
-        m.route_topk(self.logits[i], self.shape.top_k, self.idx[i], self.w[i])
-        m.expert_plan(self.idx[i], self.shape.n_experts, self.plans[i])
+        m.route_plan(self.logits[i], self.shape.top_k, self.plans[i], self.idx[i], self.w[i])
         m.expert_gate_up(L, self.x[i], self.plans[i], self.ws)
         m.expert_down_combine(L, self.B, self.idx[i], self.w[i], self.plans[i], self.out[i], self.ws)
 
@@ -185,8 +185,8 @@ def run_kernel_pass(rot, reps=4):
     m = rot.moe
     R = rot.R
     stages = {
-        "route": lambda: [m.route_topk(rot.logits[i], rot.shape.top_k, rot.idx[i], rot.w[i]) for i in range(R)],
-        "plan": lambda: [m.expert_plan(rot.idx[i], rot.shape.n_experts, rot.plans[i]) for i in range(R)],
+        "route_plan": lambda: [m.route_plan(rot.logits[i], rot.shape.top_k, rot.plans[i], rot.idx[i], rot.w[i])
+                               for i in range(R)],
         "gate_up": lambda: [m.expert_gate_up(rot.layers[i], rot.x[i], rot.plans[i], rot.ws) for i in range(R)],
         "down_combine": lambda: [m.expert_down_combine(rot.layers[i], rot.B, rot.idx[i], rot.w[i], rot.plans[i],
                                                        rot.out[i], rot.ws) for i in range(R)],

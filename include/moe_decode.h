@@ -106,9 +106,16 @@ typedef struct {
  *                        expert, ascending slot within an expert
  *   unique_experts[E]    distinct experts in ascending order, -1 after
  *   n_unique[1]          number of distinct experts
+ *   work[E][4]           one 16-byte record per distinct expert u, in the
+ *                        order of unique_experts: {expert, offsets[expert],
+ *                        counts[expert], first slot of that expert}; after
+ *                        the last distinct expert {-1, B*k, 0, 0}.  The
+ *                        expert kernels read only this record before they
+ *                        stream an expert's weights.  16-byte aligned.
  */
 typedef struct {
     int32_t *counts, *offsets, *sorted_slots, *unique_experts, *n_unique;
+    int32_t *work;
 } moe_plan_t;
 
 /*
@@ -131,6 +138,16 @@ moe_status moe_route_topk(const float *logits, int32_t n_tokens, int32_t n_exper
  */
 moe_status moe_expert_plan(const int32_t *topk_idx, int32_t n_tokens, int32_t n_experts,
                            int32_t top_k, const moe_plan_t *plan, void *hip_stream);
+
+/*
+ * Router and planner of one step in a single launch (one workgroup) when
+ * n_tokens <= 64 and n_tokens*top_k <= 2048; larger batches run the two
+ * kernels of moe_route_topk and moe_expert_plan.  Same arguments and results
+ * as those two calls.
+ */
+moe_status moe_route_plan(const float *logits, int32_t n_tokens, int32_t n_experts, int32_t top_k,
+                          int32_t *topk_idx, float *topk_w, const moe_plan_t *plan,
+                          void *hip_stream);
 
 /* Bytes of device workspace moe_decode_step needs for up to max_tokens
  * tokens of this layer's shape (0 if the layer is invalid). */

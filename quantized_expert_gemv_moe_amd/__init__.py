@@ -27,6 +27,7 @@ from ._lib import (  # noqa: F401
     expert_plan,
     lib,
     library_path,
+    route_plan,
     route_topk,
     status_str,
     workspace_size,

@@ -43,12 +43,12 @@ class LayerStruct(C.Structure):
 
 class PlanStruct(C.Structure):
     _fields_ = [("counts", C.c_void_p), ("offsets", C.c_void_p), ("sorted_slots", C.c_void_p),
-                ("unique_experts", C.c_void_p), ("n_unique", C.c_void_p)]
+                ("unique_experts", C.c_void_p), ("n_unique", C.c_void_p), ("work", C.c_void_p)]
 
 
 _lib = None
 
-EXPORTS = ("moe_route_topk", "moe_expert_plan", "moe_workspace_size", "moe_decode_step",
+EXPORTS = ("moe_route_topk", "moe_expert_plan", "moe_route_plan", "moe_workspace_size", "moe_decode_step",
            "moe_expert_gate_up", "moe_expert_down_combine", "moe_layer_check", "moe_status_str",
            "moe_abi_version")
 
@@ -72,6 +72,8 @@ def lib() -> C.CDLL:
         L.moe_route_topk.restype = C.c_int
         L.moe_expert_plan.argtypes = [vp, i32, i32, i32, C.POINTER(PlanStruct), vp]
         L.moe_expert_plan.restype = C.c_int
+        L.moe_route_plan.argtypes = [vp, i32, i32, i32, vp, vp, C.POINTER(PlanStruct), vp]
+        L.moe_route_plan.restype = C.c_int
         L.moe_workspace_size.argtypes = [C.POINTER(LayerStruct), i32]
         L.moe_workspace_size.restype = C.c_size_t
         L.moe_decode_step.argtypes = [C.POINTER(LayerStruct), vp, i32, vp, vp, C.POINTER(PlanStruct),
@@ -173,13 +175,15 @@ class Plan:
     sorted_slots: torch.Tensor
     unique_experts: torch.Tensor
     n_unique: torch.Tensor
+    work: torch.Tensor
     struct: PlanStruct
 
     @staticmethod
     def allocate(n_experts: int, max_slots: int, device="cuda") -> "Plan":
         i32 = dict(dtype=torch.int32, device=device)
         p = [torch.empty(n_experts, **i32), torch.empty(n_experts + 1, **i32),
-             torch.empty(max(max_slots, 1), **i32), torch.empty(n_experts, **i32), torch.empty(1, **i32)]
+             torch.empty(max(max_slots, 1), **i32), torch.empty(n_experts, **i32), torch.empty(1, **i32),
+             torch.empty((n_experts, 4), **i32)]
         st = PlanStruct(*[x.data_ptr() for x in p])
         return Plan(*p, st)
 
@@ -212,6 +216,25 @@ def expert_plan(idx: torch.Tensor, n_experts: int, plan: Optional[Plan] = None, 
     _check(lib().moe_expert_plan(_ptr(idx), B, n_experts, k, C.byref(plan.struct), _stream(stream)),
            "moe_expert_plan")
     return plan
+
+
+def route_plan(logits: torch.Tensor, top_k: int, plan: Optional[Plan] = None, idx: Optional[torch.Tensor] = None,
+               w: Optional[torch.Tensor] = None, stream=None):
+    """moe_route_plan: router and planner in one launch; returns (idx, w, plan)."""
+    if logits.dtype != torch.float32 or logits.dim() != 2 or not logits.is_contiguous():
+        raise ValueError("logits must be a contiguous fp32 [B, E] tensor")
+    B, E = logits.shape
+    if idx is None:
+        idx = torch.empty((B, top_k), dtype=torch.int32, device=logits.device)
+    if w is None:
+        w = torch.empty((B, top_k), dtype=torch.float32, device=logits.device)
+    if plan is None:
+        plan = Plan.allocate(E, B * top_k, device=logits.device)
+    if plan.sorted_slots.numel() < B * top_k or plan.counts.numel() < E:
+        raise ValueError("plan buffers are too small")
+    _check(lib().moe_route_plan(_ptr(logits), B, E, top_k, _ptr(idx), _ptr(w), C.byref(plan.struct),
+                                _stream(stream)), "moe_route_plan")
+    return idx, w, plan
 
 
 def workspace_size(layer: DeviceLayer, max_tokens: int) -> int:
@@ -262,9 +285,8 @@ def expert_down_combine(layer: DeviceLayer, n_tokens: int, idx: torch.Tensor, w:
 def decode_layer(layer: DeviceLayer, x: torch.Tensor, logits: torch.Tensor, plan: Optional[Plan] = None,
                  workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
                  residual: Optional[torch.Tensor] = None, bufs: Optional[dict] = None, stream=None):
-    """The three calls of one layer step: route, plan, expert block."""
+    """One layer step: router and planner (moe_route_plan), then the expert block."""
     bufs = bufs or {}
-    idx, w = route_topk(logits, layer.top_k, bufs.get("idx"), bufs.get("w"), stream=stream)
-    plan = expert_plan(idx, layer.n_experts, plan, stream=stream)
+    idx, w, plan = route_plan(logits, layer.top_k, plan, bufs.get("idx"), bufs.get("w"), stream=stream)
     out = decode_step(layer, x, idx, w, plan, out=out, workspace=workspace, residual=residual, stream=stream)
     return out, idx, w, plan

@@ -78,7 +78,8 @@ moe_status check_plan_args(const void *idx, int32_t n_tokens, int32_t n_experts,
                            const moe_plan_t *plan) {
     if (n_tokens < 0 || n_experts < 1 || top_k < 1 || top_k > n_experts) return MOE_ERR_INVALID_ARG;
     if (n_experts > MOE_MAX_EXPERTS || top_k > MOE_MAX_TOP_K) return MOE_ERR_UNSUPPORTED;
-    if (!plan || !plan->counts || !plan->offsets || !plan->unique_experts || !plan->n_unique)
+    if (!plan || !plan->counts || !plan->offsets || !plan->unique_experts || !plan->n_unique ||
+        !plan->work || (uintptr_t)plan->work % 16)
         return MOE_ERR_INVALID_ARG;
     if (n_tokens > 0 && (!idx || !plan->sorted_slots)) return MOE_ERR_INVALID_ARG;
     if ((int64_t)n_tokens * top_k > INT32_MAX / 2) return MOE_ERR_UNSUPPORTED;
@@ -116,6 +117,6 @@ const char *moe_status_str(moe_status s) {
     return "unknown status";
 }
 
-int32_t moe_abi_version(void) { return 1; }
+int32_t moe_abi_version(void) { return 2; }
 
 }  // extern "C"

@@ -36,10 +36,8 @@ namespace moe {
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
 
 struct PlanView {
-    const int *offsets;
+    const int4 *work;          // {expert, first, count, first slot} per distinct expert
     const int *sorted_slots;
-    const int *unique_experts;
-    const int *n_unique;
 };
 
 struct GateUpArgs {
@@ -62,19 +60,24 @@ struct DownArgs {
     int hidden, dff, n_experts, n_slots, slots_per_stage;
 };
 
-// Resolve the distinct expert of this workgroup; false when past the end or
-// when the plan is malformed (never indexes out of bounds).
-__device__ __forceinline__ bool plan_expert(const PlanView &p, int u, int n_experts, int n_slots,
-                                            int *e, int *first, int *count) {
-    if (u >= p.n_unique[0]) return false;
-    const int ex = p.unique_experts[u];
-    if ((unsigned)ex >= (unsigned)n_experts) return false;
-    const int a = p.offsets[ex], b = p.offsets[ex + 1];
-    if (a < 0 || b > n_slots || a > b) return false;
-    *e = ex;
-    *first = a;
-    *count = b - a;
+// The work record of the workgroup's distinct expert (one 16-byte load);
+// false past the last distinct expert or on a malformed record, so no kernel
+// ever indexes out of bounds.
+struct Work {
+    int e, first, count, slot0;
+};
+__device__ __forceinline__ bool plan_expert(const PlanView &p, int u, int n_experts, int n_slots, Work *w) {
+    const int4 r = p.work[u];
+    if ((unsigned)r.x >= (unsigned)n_experts) return false;
+    if (r.y < 0 || r.z < 1 || r.y > n_slots - r.z || (unsigned)r.w >= (unsigned)n_slots) return false;
+    *w = Work{r.x, r.y, r.z, r.w};
     return true;
+}
+
+// Slot i of the expert's list (the first one comes with the record).
+__device__ __forceinline__ int plan_slot(const PlanView &p, const Work &w, int i, int n_slots) {
+    const int s = i == 0 ? w.slot0 : p.sorted_slots[w.first + i];
+    return (unsigned)s < (unsigned)n_slots ? s : 0;  // malformed plan: stay in bounds
 }
 
 // Streaming 16-byte load of weights that are read once per step.
@@ -233,8 +236,9 @@ __global__ __launch_bounds__(kWave) void gate_up_kernel(GateUpArgs a) {
     constexpr int ROWS_WG = RPI * RI;
     constexpr int TCH = (XBF16 && NV == 1) ? 2 : 1;
     constexpr bool WAVE8 = (LPR == kWave && RI == 4);
-    int e, first, count;
-    if (!plan_expert(a.plan, blockIdx.y, a.n_experts, a.n_slots, &e, &first, &count)) return;
+    Work wk;
+    if (!plan_expert(a.plan, blockIdx.y, a.n_experts, a.n_slots, &wk)) return;
+    const int e = wk.e, count = wk.count;
 
     const int lane = threadIdx.x;
     const int sl = lane % LPR;
@@ -277,8 +281,7 @@ __global__ __launch_bounds__(kWave) void gate_up_kernel(GateUpArgs a) {
         for (int i = 0; i < TCH; ++i) {
             slot[i] = -1;
             if (i > 0 && t0 + i >= count) break;  // uniform: the chunk's tail is empty
-            slot[i] = a.plan.sorted_slots[first + t0 + i];
-            if ((unsigned)slot[i] >= (unsigned)a.n_slots) slot[i] = 0;  // malformed plan: stay in bounds
+            slot[i] = plan_slot(a.plan, wk, t0 + i, a.n_slots);
             const size_t xr = (size_t)(slot[i] / a.top_k) * H;
 #pragma unroll
             for (int v = 0; v < NV; ++v) {
@@ -342,8 +345,9 @@ __global__ __launch_bounds__(kBlock) void down_kernel(DownArgs a) {
     constexpr int RPI = kWave / LPR;
     constexpr int ROWS_WG = RPI * RI * (kBlock / kWave);
     extern __shared__ float lds[];
-    int e, first, count;
-    if (!plan_expert(a.plan, blockIdx.y, a.n_experts, a.n_slots, &e, &first, &count)) return;
+    Work wk;
+    if (!plan_expert(a.plan, blockIdx.y, a.n_experts, a.n_slots, &wk)) return;
+    const int e = wk.e, count = wk.count;
 
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
@@ -379,8 +383,7 @@ __global__ __launch_bounds__(kBlock) void down_kernel(DownArgs a) {
         const int f4 = F / 4;
         for (int i = threadIdx.x; i < ns * f4; i += kBlock) {
             const int j = i / f4, c = i - j * f4;
-            int slot = a.plan.sorted_slots[first + s0 + j];
-            if ((unsigned)slot >= (unsigned)a.n_slots) slot = 0;  // malformed plan: stay in bounds
+            const int slot = plan_slot(a.plan, wk, s0 + j, a.n_slots);
             ((float4 *)(hl + (size_t)j * F))[c] = ((const float4 *)(a.h + (size_t)slot * F))[c];
         }
         __syncthreads();
@@ -396,8 +399,7 @@ __global__ __launch_bounds__(kBlock) void down_kernel(DownArgs a) {
         }
         __syncthreads();
         for (int j = 0; j < ns; ++j) {
-            int slot = a.plan.sorted_slots[first + s0 + j];
-            if ((unsigned)slot >= (unsigned)a.n_slots) slot = 0;
+            const int slot = plan_slot(a.plan, wk, s0 + j, a.n_slots);
             float hv[NV][32], hsum[NV];
 #pragma unroll
             for (int v = 0; v < NV; ++v) {
@@ -522,7 +524,7 @@ static moe_status check_step(const moe_layer_t *layer, int32_t n_tokens, const m
     if (n_tokens < 0) return MOE_ERR_INVALID_ARG;
     if ((int64_t)n_tokens * layer->top_k > INT32_MAX / 2) return MOE_ERR_UNSUPPORTED;
     if (n_tokens == 0) return MOE_OK;
-    if (!plan || !plan->offsets || !plan->sorted_slots || !plan->unique_experts || !plan->n_unique)
+    if (!plan || !plan->work || !plan->sorted_slots || (uintptr_t)plan->work % 16)
         return MOE_ERR_INVALID_ARG;
     if (!workspace || (uintptr_t)workspace % 256) return MOE_ERR_INVALID_ARG;
     if (workspace_bytes < workspace_layout(layer, n_tokens).total) return MOE_ERR_WORKSPACE;
@@ -530,7 +532,7 @@ static moe_status check_step(const moe_layer_t *layer, int32_t n_tokens, const m
 }
 
 static PlanView plan_view(const moe_plan_t *plan) {
-    return PlanView{plan->offsets, plan->sorted_slots, plan->unique_experts, plan->n_unique};
+    return PlanView{(const int4 *)plan->work, plan->sorted_slots};
 }
 
 static int groups_y_of(const moe_layer_t *layer, int n_tokens) {

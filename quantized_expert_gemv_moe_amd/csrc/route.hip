@@ -1,20 +1,27 @@
 // Router and cohort planner kernels (gfx950) and their C-ABI entry points.
 //
 // Router: one wavefront per token.  Each lane holds E/64 logits; top-k is k
-// rounds of a wave-wide arg-max (butterfly shuffles, larger value first,
-// lower expert id on ties), then the kept logits get softmax weights.  The
-// router is the first of the three named parts of the per-token MoE cost
-// (page "perf(moe): attribute the MoE decode gap at the M = 1 expert
-// gather", Proposed Solution step 2).
+// rounds of a wave-wide arg-max whose six exchange steps are DPP quad
+// permutes and row mirrors inside 16-lane rows and v_permlane16/32_swap
+// across rows (larger value first, lower expert id on ties).  The winner of
+// round j is known to every lane, so the softmax denominator of the kept
+// logits accumulates in j order without any further exchange.  The router
+// is the first of the three named parts of the per-token MoE cost (page
+// "perf(moe): attribute the MoE decode gap at the M = 1 expert gather",
+// Proposed Solution step 2).
 //
 // Planner: one workgroup.  An LDS histogram of expert ids, a block-wide
 // exclusive scan into per-expert offsets and the list of distinct experts,
 // then a stable scatter of slot ids into per-expert lists by one wave in
-// slot order (ballot-based peer ranks).  This is the cross-cohort
-// deduplication of page "perf(moe): batched decode scales 1.55x against
-// 3.25x on dense" (Proposed Solution, second bullet): the expert kernels
-// walk the distinct experts, so each expert's weights are read once per
-// step whatever the number of (token, k) slots routed to it.
+// slot order (ballot-based peer ranks), and one 16-byte work record per
+// distinct expert.  This is the cross-cohort deduplication of page
+// "perf(moe): batched decode scales 1.55x against 3.25x on dense" (Proposed
+// Solution, second bullet): the expert kernels walk the distinct experts, so
+// each expert's weights are read once per step whatever the number of
+// (token, k) slots routed to it.
+//
+// moe_route_plan runs both in one workgroup when the batch is small, so the
+// indices stay in LDS and one launch disappears from the step.
 #include <hip/hip_runtime.h>
 #include <limits.h>
 #include <math.h>
@@ -26,65 +33,107 @@ namespace moe {
 
 // ----------------------------------------------------------------- router
 
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+    return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, false);
+}
+
+// Keep the better of (v, i) and (pv, pi): larger value, lower id on ties;
+// id INT_MAX marks an empty candidate.
+__device__ __forceinline__ void take_better(float &v, int &i, float pv, int pi) {
+    const bool take = pi != INT_MAX && (i == INT_MAX || pv > v || (pv == v && pi < i));
+    v = take ? pv : v;
+    i = take ? pi : i;
+}
+
+template <int CTRL>
+__device__ __forceinline__ void argmax_dpp(float &v, int &i) {
+    const float pv = __int_as_float(dpp_i<CTRL>(__float_as_int(v)));
+    const int pi = dpp_i<CTRL>(i);
+    take_better(v, i, pv, pi);
+}
+
+// Wave-wide arg-max; every lane ends with the same (value, id).
+__device__ __forceinline__ void wave_argmax(float &v, int &i) {
+    argmax_dpp<0xB1>(v, i);   // quad_perm [1,0,3,2]
+    argmax_dpp<0x4E>(v, i);   // quad_perm [2,3,0,1]
+    argmax_dpp<0x141>(v, i);  // row_half_mirror
+    argmax_dpp<0x140>(v, i);  // row_mirror
+    {   // rows (0,1) and (2,3): each lane sees both rows' candidates
+        const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+        const auto b = __builtin_amdgcn_permlane16_swap((unsigned)i, (unsigned)i, false, false);
+        float v0 = __uint_as_float(a[0]);
+        int i0 = (int)b[0];
+        take_better(v0, i0, __uint_as_float(a[1]), (int)b[1]);
+        v = v0;
+        i = i0;
+    }
+    {   // halves (0..31) and (32..63)
+        const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+        const auto b = __builtin_amdgcn_permlane32_swap((unsigned)i, (unsigned)i, false, false);
+        float v0 = __uint_as_float(a[0]);
+        int i0 = (int)b[0];
+        take_better(v0, i0, __uint_as_float(a[1]), (int)b[1]);
+        v = v0;
+        i = i0;
+    }
+}
+
+// Top-k of one token's logits by the calling wave.  Lane j < top_k returns
+// the j-th expert id in *id and its weight in *w; returns false for lanes
+// j >= top_k.
+template <int PER_LANE>
+__device__ __forceinline__ bool route_token(const float *__restrict__ row, int n_experts, int top_k,
+                                            int *id, float *w) {
+    const int lane = threadIdx.x & (kWave - 1);
+    float v[PER_LANE];
+    uint32_t avail = 0;
+#pragma unroll
+    for (int q = 0; q < PER_LANE; ++q) {
+        const int e = lane + kWave * q;
+        v[q] = e < n_experts ? row[e] : 0.f;
+        if (e < n_experts) avail |= 1u << q;
+    }
+    int my_id = 0;
+    float my_ex = 0.f, l0 = 0.f, den = 0.f;
+    for (int j = 0; j < top_k; ++j) {
+        float bv = -INFINITY;
+        int bi = INT_MAX;
+#pragma unroll
+        for (int q = 0; q < PER_LANE; ++q) {  // ids ascend with q: strict > keeps the lower id
+            if (((avail >> q) & 1u) && (bi == INT_MAX || v[q] > bv)) {
+                bv = v[q];
+                bi = lane + kWave * q;
+            }
+        }
+        wave_argmax(bv, bi);
+        if (lane == (bi & (kWave - 1))) avail &= ~(1u << (bi / kWave));
+        if (j == 0) l0 = bv;
+        const float ex = expf(bv - l0);  // the same on every lane
+        den += ex;                       // j order
+        if (lane == j) {
+            my_id = bi;
+            my_ex = ex;
+        }
+    }
+    *id = my_id;
+    *w = my_ex / den;
+    return lane < top_k;
+}
+
 template <int PER_LANE>
 __global__ __launch_bounds__(kBlock) void route_topk_kernel(const float *__restrict__ logits,
                                                             int n_tokens, int n_experts, int top_k,
                                                             int *__restrict__ topk_idx,
                                                             float *__restrict__ topk_w) {
-    const int lane = threadIdx.x & (kWave - 1);
     const int t = blockIdx.x * (kBlock / kWave) + (threadIdx.x / kWave);
     if (t >= n_tokens) return;  // uniform per wave
-
-    const float *row = logits + (size_t)t * n_experts;
-    float v[PER_LANE];
-    uint32_t avail = 0;
-#pragma unroll
-    for (int i = 0; i < PER_LANE; ++i) {
-        const int e = lane + kWave * i;
-        v[i] = e < n_experts ? row[e] : 0.f;
-        if (e < n_experts) avail |= 1u << i;
-    }
-
-    int my_id = 0;       // lane j < k ends holding the j-th selection
-    float my_val = 0.f;
-    for (int j = 0; j < top_k; ++j) {
-        // best remaining element of this lane: ids ascend with i, so a
-        // strict comparison keeps the lower id on equal values
-        float bv = 0.f;
-        int bi = INT_MAX;
-#pragma unroll
-        for (int i = 0; i < PER_LANE; ++i) {
-            if (((avail >> i) & 1u) && (bi == INT_MAX || v[i] > bv)) {
-                bv = v[i];
-                bi = lane + kWave * i;
-            }
-        }
-#pragma unroll
-        for (int off = kWave / 2; off >= 1; off >>= 1) {
-            const float ov = __shfl_xor(bv, off, kWave);
-            const int oi = __shfl_xor(bi, off, kWave);
-            const bool take = oi != INT_MAX &&
-                              (bi == INT_MAX || ov > bv || (ov == bv && oi < bi));
-            if (take) {
-                bv = ov;
-                bi = oi;
-            }
-        }
-        if (lane == (bi & (kWave - 1))) avail &= ~(1u << (bi / kWave));
-        if (lane == j) {
-            my_id = bi;
-            my_val = bv;
-        }
-    }
-
-    // softmax over the kept logits, relative to the largest one
-    const float l0 = __shfl(my_val, 0, kWave);
-    const float ex = lane < top_k ? expf(my_val - l0) : 0.f;
-    float den = 0.f;
-    for (int j = 0; j < top_k; ++j) den += __shfl(ex, j, kWave);  // fixed j order
-    if (lane < top_k) {
-        topk_idx[(size_t)t * top_k + lane] = my_id;
-        topk_w[(size_t)t * top_k + lane] = ex / den;
+    const int lane = threadIdx.x & (kWave - 1);
+    int id;
+    float w;
+    if (route_token<PER_LANE>(logits + (size_t)t * n_experts, n_experts, top_k, &id, &w)) {
+        topk_idx[(size_t)t * top_k + lane] = id;
+        topk_w[(size_t)t * top_k + lane] = w;
     }
 }
 
@@ -115,29 +164,37 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int *lds4, int *total
     return base + inc - v;
 }
 
-__global__ __launch_bounds__(kBlock) void expert_plan_kernel(const int *__restrict__ topk_idx,
-                                                             int n_slots, int n_experts,
-                                                             int *__restrict__ counts,
-                                                             int *__restrict__ offsets,
-                                                             int *__restrict__ sorted_slots,
-                                                             int *__restrict__ unique_experts,
-                                                             int *__restrict__ n_unique) {
+struct PlanOut {
+    int *counts, *offsets, *sorted_slots, *unique_experts, *n_unique;
+    int4 *work;
+};
+
+// The planner body for one 256-thread workgroup.  `idx` may live in global
+// memory or in LDS.
+__device__ __forceinline__ void plan_block(const int *idx, int n_slots, int n_experts, const PlanOut &p) {
     __shared__ int cnt[MOE_MAX_EXPERTS];
     __shared__ int cursor[MOE_MAX_EXPERTS];
+    __shared__ int first_slot[MOE_MAX_EXPERTS];
+    __shared__ int uniq[MOE_MAX_EXPERTS];
     __shared__ int lds4[kBlock / kWave];
     const int tid = threadIdx.x;
     const unsigned E = (unsigned)n_experts;
 
-    for (int e = tid; e < n_experts; e += kBlock) cnt[e] = 0;
+    for (int e = tid; e < n_experts; e += kBlock) {
+        cnt[e] = 0;
+        first_slot[e] = INT_MAX;
+    }
     __syncthreads();
     for (int s = tid; s < n_slots; s += kBlock) {
-        const int e = topk_idx[s];
-        if ((unsigned)e < E) atomicAdd(&cnt[e], 1);  // integer: order-free
+        const int e = idx[s];
+        if ((unsigned)e < E) {
+            atomicAdd(&cnt[e], 1);          // integer: order-free
+            atomicMin(&first_slot[e], s);
+        }
     }
     __syncthreads();
 
-    // each thread owns PER consecutive experts
-    constexpr int PER = MOE_MAX_EXPERTS / kBlock;
+    constexpr int PER = MOE_MAX_EXPERTS / kBlock;  // experts owned per thread
     int c[PER], nz = 0, sum = 0;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
@@ -153,17 +210,25 @@ __global__ __launch_bounds__(kBlock) void expert_plan_kernel(const int *__restri
     for (int i = 0; i < PER; ++i) {
         const int e = tid * PER + i;
         if (e < n_experts) {
-            counts[e] = c[i];
-            offsets[e] = run;
+            p.counts[e] = c[i];
+            p.offsets[e] = run;
             cursor[e] = run;
-            if (c[i] > 0) unique_experts[urun++] = e;
+            if (c[i] > 0) {
+                p.unique_experts[urun] = e;
+                p.work[urun] = make_int4(e, run, c[i], first_slot[e]);
+                uniq[urun] = e;
+                ++urun;
+            }
         }
         run += c[i];
     }
-    for (int e = total_unique + tid; e < n_experts; e += kBlock) unique_experts[e] = -1;
+    for (int u = total_unique + tid; u < n_experts; u += kBlock) {
+        p.unique_experts[u] = -1;
+        p.work[u] = make_int4(-1, total_slots, 0, 0);
+    }
     if (tid == 0) {
-        offsets[n_experts] = total_slots;
-        n_unique[0] = total_unique;
+        p.offsets[n_experts] = total_slots;
+        p.n_unique[0] = total_unique;
     }
     __syncthreads();
 
@@ -174,7 +239,7 @@ __global__ __launch_bounds__(kBlock) void expert_plan_kernel(const int *__restri
         const unsigned long long below = (1ull << lane) - 1ull;
         for (int base = 0; base < n_slots; base += kWave) {
             const int s = base + lane;
-            const int e = s < n_slots ? topk_idx[s] : -1;
+            const int e = s < n_slots ? idx[s] : -1;
             const bool ok = s < n_slots && (unsigned)e < E;
             unsigned long long peers = __ballot(ok);
             for (int b = 0; b < id_bits; ++b) {
@@ -182,11 +247,7 @@ __global__ __launch_bounds__(kBlock) void expert_plan_kernel(const int *__restri
                 const unsigned long long m = __ballot(bit);
                 peers &= bit ? m : ~m;
             }
-            int pos = 0;
-            if (ok) {
-                pos = cursor[e] + __popcll(peers & below);
-                sorted_slots[pos] = s;
-            }
+            if (ok) p.sorted_slots[cursor[e] + __popcll(peers & below)] = s;
             // every lane has read its cursor before the last peer moves it
             __builtin_amdgcn_wave_barrier();
             if (ok && lane == 63 - __clzll(peers)) cursor[e] += __popcll(peers);
@@ -195,9 +256,55 @@ __global__ __launch_bounds__(kBlock) void expert_plan_kernel(const int *__restri
     }
 }
 
+__global__ __launch_bounds__(kBlock) void expert_plan_kernel(const int *__restrict__ topk_idx, int n_slots,
+                                                             int n_experts, PlanOut p) {
+    plan_block(topk_idx, n_slots, n_experts, p);
+}
+
+// Router and planner in one workgroup: the four waves route the tokens, the
+// indices are kept in LDS (and written out), then the block plans them.
+template <int PER_LANE>
+__global__ __launch_bounds__(kBlock) void route_plan_kernel(const float *__restrict__ logits, int n_tokens,
+                                                            int n_experts, int top_k,
+                                                            int *__restrict__ topk_idx,
+                                                            float *__restrict__ topk_w, PlanOut p) {
+    __shared__ int idx_lds[kRoutePlanMaxSlots];
+    const int lane = threadIdx.x & (kWave - 1);
+    for (int t = threadIdx.x / kWave; t < n_tokens; t += kBlock / kWave) {
+        int id;
+        float w;
+        if (route_token<PER_LANE>(logits + (size_t)t * n_experts, n_experts, top_k, &id, &w)) {
+            topk_idx[(size_t)t * top_k + lane] = id;
+            topk_w[(size_t)t * top_k + lane] = w;
+            idx_lds[t * top_k + lane] = id;
+        }
+    }
+    __syncthreads();
+    plan_block(idx_lds, n_tokens * top_k, n_experts, p);
+}
+
+static int per_lane_bucket(int n_experts) {
+    const int per_lane = (n_experts + kWave - 1) / kWave;
+    return per_lane <= 1 ? 1 : per_lane <= 2 ? 2 : per_lane <= 4 ? 4 : per_lane <= 8 ? 8 : 16;
+}
+
+static PlanOut plan_out(const moe_plan_t *plan) {
+    return PlanOut{plan->counts, plan->offsets, plan->sorted_slots, plan->unique_experts,
+                   plan->n_unique, (int4 *)plan->work};
+}
+
 }  // namespace moe
 
 using namespace moe;
+
+#define MOE_PER_LANE_SWITCH(P, STMT) \
+    switch (P) {                     \
+        case 1: { constexpr int PL = 1; STMT; } break;  \
+        case 2: { constexpr int PL = 2; STMT; } break;  \
+        case 4: { constexpr int PL = 4; STMT; } break;  \
+        case 8: { constexpr int PL = 8; STMT; } break;  \
+        default: { constexpr int PL = 16; STMT; } break; \
+    }
 
 extern "C" moe_status moe_route_topk(const float *logits, int32_t n_tokens, int32_t n_experts,
                                      int32_t top_k, int32_t *topk_idx, float *topk_w,
@@ -207,20 +314,9 @@ extern "C" moe_status moe_route_topk(const float *logits, int32_t n_tokens, int3
     if (n_tokens == 0) return MOE_OK;
     hipStream_t stream = (hipStream_t)hip_stream;
     const dim3 grid((n_tokens + kBlock / kWave - 1) / (kBlock / kWave));
-    const int per_lane = (n_experts + kWave - 1) / kWave;
-#define MOE_ROUTE_CASE(P)                                                                      \
-    case P:                                                                                    \
-        hipLaunchKernelGGL(route_topk_kernel<P>, grid, dim3(kBlock), 0, stream, logits,       \
-                           n_tokens, n_experts, top_k, topk_idx, topk_w);                     \
-        break;
-    switch (per_lane <= 1 ? 1 : per_lane <= 2 ? 2 : per_lane <= 4 ? 4 : per_lane <= 8 ? 8 : 16) {
-        MOE_ROUTE_CASE(1)
-        MOE_ROUTE_CASE(2)
-        MOE_ROUTE_CASE(4)
-        MOE_ROUTE_CASE(8)
-        MOE_ROUTE_CASE(16)
-    }
-#undef MOE_ROUTE_CASE
+    MOE_PER_LANE_SWITCH(per_lane_bucket(n_experts),
+                        hipLaunchKernelGGL(route_topk_kernel<PL>, grid, dim3(kBlock), 0, stream, logits,
+                                           n_tokens, n_experts, top_k, topk_idx, topk_w))
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_DEVICE;
 }
 
@@ -230,7 +326,26 @@ extern "C" moe_status moe_expert_plan(const int32_t *topk_idx, int32_t n_tokens,
     if (st != MOE_OK) return st;
     hipStream_t stream = (hipStream_t)hip_stream;
     hipLaunchKernelGGL(expert_plan_kernel, dim3(1), dim3(kBlock), 0, stream, topk_idx,
-                       n_tokens * top_k, n_experts, plan->counts, plan->offsets,
-                       plan->sorted_slots, plan->unique_experts, plan->n_unique);
+                       n_tokens * top_k, n_experts, plan_out(plan));
+    return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_DEVICE;
+}
+
+extern "C" moe_status moe_route_plan(const float *logits, int32_t n_tokens, int32_t n_experts,
+                                     int32_t top_k, int32_t *topk_idx, float *topk_w,
+                                     const moe_plan_t *plan, void *hip_stream) {
+    moe_status st = check_route_args(logits, n_tokens, n_experts, top_k, topk_idx, topk_w);
+    if (st != MOE_OK) return st;
+    st = check_plan_args(topk_idx, n_tokens, n_experts, top_k, plan);
+    if (st != MOE_OK) return st;
+    hipStream_t stream = (hipStream_t)hip_stream;
+    if ((int64_t)n_tokens * top_k > kRoutePlanMaxSlots || n_tokens > kRoutePlanMaxTokens) {
+        // large batches: the two kernels, the same results
+        st = moe_route_topk(logits, n_tokens, n_experts, top_k, topk_idx, topk_w, hip_stream);
+        if (st != MOE_OK) return st;
+        return moe_expert_plan(topk_idx, n_tokens, n_experts, top_k, plan, hip_stream);
+    }
+    MOE_PER_LANE_SWITCH(per_lane_bucket(n_experts),
+                        hipLaunchKernelGGL(route_plan_kernel<PL>, dim3(1), dim3(kBlock), 0, stream, logits,
+                                           n_tokens, n_experts, top_k, topk_idx, topk_w, plan_out(plan)))
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_DEVICE;
 }

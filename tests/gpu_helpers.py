@@ -85,7 +85,7 @@ class GpuRun:
             counts=self.plan.counts.cpu().numpy(), offsets=self.plan.offsets.cpu().numpy(),
             sorted_slots=self.plan.sorted_slots[:n].cpu().numpy(),
             unique_experts=self.plan.unique_experts.cpu().numpy(),
-            n_unique=int(self.plan.n_unique.cpu().numpy()[0]))
+            n_unique=int(self.plan.n_unique.cpu().numpy()[0]), work=self.plan.work.cpu().numpy())
         # h sits at the start of the workspace: [slots][dff] fp32
         self.h = self.ws[: n * sh.dff * 4].view(torch.float32).view(n, sh.dff).cpu().numpy()
 

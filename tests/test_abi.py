@@ -32,7 +32,7 @@ def test_library_exports_every_declared_function():
     assert set(declared) == set(_lib.EXPORTS)
     for name in declared:
         assert hasattr(L, name), name
-    assert L.moe_abi_version() == 1
+    assert L.moe_abi_version() == 2
 
 
 def test_status_strings():
@@ -110,20 +110,29 @@ def test_route_validation_before_any_launch():
 
 def test_plan_validation_before_any_launch():
     L = moe.lib()
-    p = _lib.PlanStruct(FAKE, FAKE, FAKE, FAKE, FAKE)
+    p = _lib.PlanStruct(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
     f = L.moe_expert_plan
     assert f(FAKE, 1, 128, 8, None, None) == moe.MOE_ERR_INVALID_ARG
     assert f(FAKE, 1, 8, 9, C.byref(p), None) == moe.MOE_ERR_INVALID_ARG
     assert f(None, 1, 8, 2, C.byref(p), None) == moe.MOE_ERR_INVALID_ARG
-    bad = _lib.PlanStruct(FAKE, None, FAKE, FAKE, FAKE)
+    bad = _lib.PlanStruct(FAKE, None, FAKE, FAKE, FAKE, FAKE)
     assert f(FAKE, 1, 8, 2, C.byref(bad), None) == moe.MOE_ERR_INVALID_ARG
+    nowork = _lib.PlanStruct(FAKE, FAKE, FAKE, FAKE, FAKE, None)
+    assert f(FAKE, 1, 8, 2, C.byref(nowork), None) == moe.MOE_ERR_INVALID_ARG
+    unaligned = _lib.PlanStruct(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE + 4)
+    assert f(FAKE, 1, 8, 2, C.byref(unaligned), None) == moe.MOE_ERR_INVALID_ARG
     assert f(FAKE, 1, 4096, 2, C.byref(p), None) == moe.MOE_ERR_UNSUPPORTED
+    g = L.moe_route_plan
+    assert g(FAKE, 1, 8, 9, FAKE, FAKE, C.byref(p), None) == moe.MOE_ERR_INVALID_ARG
+    assert g(None, 1, 8, 2, FAKE, FAKE, C.byref(p), None) == moe.MOE_ERR_INVALID_ARG
+    assert g(FAKE, 1, 8, 2, FAKE, FAKE, C.byref(nowork), None) == moe.MOE_ERR_INVALID_ARG
+    assert g(FAKE, 1, 2048, 2, FAKE, FAKE, C.byref(p), None) == moe.MOE_ERR_UNSUPPORTED
 
 
 def test_decode_step_validation_before_any_launch():
     L = moe.lib()
     st = layer()
-    p = _lib.PlanStruct(FAKE, FAKE, FAKE, FAKE, FAKE)
+    p = _lib.PlanStruct(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
     ws_need = L.moe_workspace_size(C.byref(st), 4)
     f = L.moe_decode_step
     X, O, W = FAKE + 0x1000000, FAKE + 0x2000000, FAKE + 0x3000000
@@ -143,7 +152,8 @@ def test_decode_step_validation_before_any_launch():
     assert call(ws=None) == moe.MOE_ERR_INVALID_ARG
     assert call(wsb=ws_need - 1) == moe.MOE_ERR_WORKSPACE
     assert call(plan=None) == moe.MOE_ERR_INVALID_ARG
-    assert call(plan=_lib.PlanStruct(FAKE, FAKE, None, FAKE, FAKE)) == moe.MOE_ERR_INVALID_ARG
+    assert call(plan=_lib.PlanStruct(FAKE, FAKE, None, FAKE, FAKE, FAKE)) == moe.MOE_ERR_INVALID_ARG
+    assert call(plan=_lib.PlanStruct(FAKE, FAKE, FAKE, FAKE, FAKE, None)) == moe.MOE_ERR_INVALID_ARG
 
 
 def test_binding_raises_on_error_status():

@@ -70,7 +70,22 @@ def test_router_empty_batch_is_a_no_op():
 def plan_np(plan, n):
     return dict(counts=plan.counts.cpu().numpy(), offsets=plan.offsets.cpu().numpy(),
                 sorted_slots=plan.sorted_slots[:n].cpu().numpy(),
-                unique_experts=plan.unique_experts.cpu().numpy(), n_unique=int(plan.n_unique.item()))
+                unique_experts=plan.unique_experts.cpu().numpy(), n_unique=int(plan.n_unique.item()),
+                work=plan.work.cpu().numpy())
+
+
+def check_plan(got, ref, n_slots):
+    for key in ("counts", "offsets", "sorted_slots", "unique_experts"):
+        assert np.array_equal(got[key], ref[key]), key
+    assert got["n_unique"] == ref["n_unique"]
+    # work records: {expert, offsets[e], counts[e], first slot of e}; then {-1, n, 0, 0}
+    E = len(ref["counts"])
+    want = np.zeros((E, 4), np.int64)
+    want[:, 0], want[:, 1] = -1, n_slots
+    for u in range(ref["n_unique"]):
+        e = ref["unique_experts"][u]
+        want[u] = (e, ref["offsets"][e], ref["counts"][e], ref["sorted_slots"][ref["offsets"][e]])
+    assert np.array_equal(got["work"], want), "work records"
 
 
 @pytest.mark.parametrize("E,k,B,kind", [
@@ -87,11 +102,23 @@ def test_plan_matches_oracle(E, k, B, kind):
         regime = {"router": "normal"}.get(kind, kind)
         idx, _ = oracle.route_topk(make_logits(sh, B, regime=regime, seed=5), k)
     plan = moe.expert_plan(torch.from_numpy(idx).cuda(), E)
-    got = plan_np(plan, B * k)
-    ref = oracle.plan(idx, E)
-    for key in ("counts", "offsets", "sorted_slots", "unique_experts"):
-        assert np.array_equal(got[key], ref[key]), key
-    assert got["n_unique"] == ref["n_unique"]
+    check_plan(plan_np(plan, B * k), oracle.plan(idx, E), B * k)
+
+
+@pytest.mark.parametrize("E,k,B,regime", [
+    (128, 8, 1, "normal"), (8, 2, 1, "normal"), (128, 8, 4, "sharing"), (128, 8, 32, "zipf"),
+    (256, 6, 4, "normal"), (1024, 16, 64, "normal"), (128, 8, 65, "normal"), (64, 16, 200, "normal"),
+    (1, 1, 3, "normal"),
+])
+def test_route_plan_matches_oracle(E, k, B, regime):
+    """The fused router+planner (one workgroup up to 64 tokens, two kernels beyond)."""
+    sh = Shape("rp", 33, 64, 64, E, k, "f32")
+    lg = make_logits(sh, B, regime=regime, seed=E * k + B)
+    idx, w, plan = moe.route_plan(torch.from_numpy(lg).cuda(), k)
+    ridx, rw = oracle.route_topk(lg, k)
+    assert np.array_equal(idx.cpu().numpy(), ridx)
+    assert np.abs(w.cpu().numpy() - rw).max() <= 1e-6
+    check_plan(plan_np(plan, B * k), oracle.plan(ridx, E), B * k)
 
 
 def test_plan_empty_batch():
@@ -101,6 +128,7 @@ def test_plan_empty_batch():
     got = plan_np(plan, 0)
     assert got["n_unique"] == 0 and got["counts"].sum() == 0
     assert np.all(got["offsets"] == 0) and np.all(got["unique_experts"] == -1)
+    assert np.all(got["work"][:, 0] == -1)
 
 
 # ------------------------------------------------------- expert block parity
@@ -236,6 +264,9 @@ def test_invalid_expert_id_gives_nan_for_that_token_only():
     bad[1, 3] = 5000          # out of range: left out of the plan, NaN for token 1
     bad[2, 0] = -1
     it = torch.from_numpy(bad).cuda()
+    # the planner leaves the two bad slots out of every list
+    got = plan_np(moe.expert_plan(it, sh.n_experts), B * sh.top_k)
+    assert got["counts"].sum() == B * sh.top_k - 2 and got["offsets"][-1] == B * sh.top_k - 2
     wt = torch.from_numpy(w.astype(np.float32)).cuda()
     plan = moe.expert_plan(it, sh.n_experts)
     x = make_x(sh, B, seed=12)
