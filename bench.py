@@ -93,8 +93,11 @@ class Rotation:
             layers = []
             for l in range(R):
                 t = make_layer_device(shape, l, dev, seed=seed)
-                layers.append(moe.DeviceLayer.from_tensors(shape.hidden, shape.dff, shape.n_experts,
-                                                           shape.top_k, shape.act, shape.clamp, t))
+                rows = moe.DeviceLayer.from_tensors(shape.hidden, shape.dff, shape.n_experts,
+                                                    shape.top_k, shape.act, shape.clamp, t)
+                # load-time regrouping of the down projection (moe_pack_down)
+                layers.append(rows.pack_down())
+                del rows, t
             torch.cuda.synchronize()
             log(f"[bench] {R} layers of {shape.name} generated on device in {time.time() - t0:.1f}s")
         self.layers = layers
@@ -356,7 +359,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": desc, "hidden": sh.hidden, "dff": sh.dff, "n_experts": sh.n_experts,
                    "top_k": sh.top_k, "n_tokens": B, "routing": regime,
-                   "weights": "affine int4, group 64, fp16 scale+bias", "activations": sh.act,
+                   "weights": "affine int4, group 64, fp16 scale+bias; down projection packed by moe_pack_down",
+                   "activations": sh.act,
                    "accumulation": "f32", "rotation_layers": R},
         "unique_gbps": gbps,
         "hbm_frac": gbps / HBM_PEAK_GBPS,

@@ -58,6 +58,9 @@ typedef enum {
 
 typedef enum { MOE_DTYPE_F32 = 0, MOE_DTYPE_BF16 = 1 } moe_dtype;
 
+/* Storage of the down projection (see moe_layer_t and moe_pack_down). */
+typedef enum { MOE_DOWN_ROWS = 0, MOE_DOWN_COLS = 1 } moe_down_layout;
+
 /* Limits enforced by validation. */
 #define MOE_MAX_EXPERTS 1024
 #define MOE_MAX_TOP_K 16
@@ -78,6 +81,15 @@ typedef enum { MOE_DTYPE_F32 = 0, MOE_DTYPE_BF16 = 1 } moe_dtype;
  * 4-byte aligned.  The struct itself lives in host memory; the pointers it
  * holds are device pointers.
  *
+ * `down_layout` selects how the down projection is stored:
+ *   MOE_DOWN_ROWS  as above: down_q [E][hidden][dff/8], scales [E][hidden][dff/64]
+ *   MOE_DOWN_COLS  the same bytes regrouped by moe_pack_down so that one
+ *                  16-byte chunk (32 consecutive dff inputs) of 64
+ *                  consecutive hidden rows is contiguous:
+ *                  down_q [E][dff/32][hidden] 16-byte chunks,
+ *                  scales and biases [E][dff/64][hidden].
+ *                  Needs hidden % 64 == 0 and dff % 128 == 0.
+ *
  * `expert_scale` (optional, NULL = none) is one fp32 factor per expert that
  * multiplies the gate and up pre-activations (the expert-scale sidecars of
  * page "perf(moe): attribute ...", Problem / Background).  `clamp_limit`
@@ -93,6 +105,7 @@ typedef struct {
     int32_t group_size;  /* 64 */
     int32_t act_dtype;   /* moe_dtype of x, residual and out */
     float clamp_limit;   /* >= 0; 0 disables the clamp */
+    int32_t down_layout; /* moe_down_layout */
     const uint32_t *gate_q, *up_q, *down_q;
     const uint16_t *gate_s, *gate_b, *up_s, *up_b, *down_s, *down_b;
     const float *expert_scale; /* [E] or NULL */
@@ -199,6 +212,19 @@ moe_status moe_expert_down_combine(const moe_layer_t *layer, int32_t n_tokens,
                                    const int32_t *topk_idx, const float *topk_w,
                                    const moe_plan_t *plan, const void *residual, void *out,
                                    void *workspace, size_t workspace_bytes, void *hip_stream);
+
+/*
+ * Regroup a layer's down projection from MOE_DOWN_ROWS (as stored by the
+ * pages' 4-bit checkpoints) to MOE_DOWN_COLS, the layout the decode kernels
+ * read fastest: a wave then reads 64 consecutive output rows with one
+ * coalesced 1 KiB load per 32 inputs.  A one-time, load-time step; pure byte
+ * movement, nothing is re-quantised.  `layer` describes the source
+ * (down_layout must be MOE_DOWN_ROWS); dst_q (16-byte aligned, E*hidden*dff/2
+ * bytes), dst_s and dst_b (E*hidden*dff/64 fp16 each) are device buffers that
+ * must not overlap the source.  Asynchronous on hip_stream.
+ */
+moe_status moe_pack_down(const moe_layer_t *layer, uint32_t *dst_q, uint16_t *dst_s, uint16_t *dst_b,
+                         void *hip_stream);
 
 /* Host-only check of a layer descriptor (no device access):
  * MOE_OK, MOE_ERR_INVALID_ARG or MOE_ERR_UNSUPPORTED. */

@@ -19,6 +19,7 @@ from . import build as _build
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_DEVICE = range(5)
 MOE_DTYPE_F32, MOE_DTYPE_BF16 = 0, 1
+MOE_DOWN_ROWS, MOE_DOWN_COLS = 0, 1
 MOE_MAX_EXPERTS = 1024
 MOE_MAX_TOP_K = 16
 
@@ -33,7 +34,7 @@ class LayerStruct(C.Structure):
     _fields_ = [
         ("hidden", C.c_int32), ("dff", C.c_int32), ("n_experts", C.c_int32), ("top_k", C.c_int32),
         ("bits", C.c_int32), ("group_size", C.c_int32), ("act_dtype", C.c_int32),
-        ("clamp_limit", C.c_float),
+        ("clamp_limit", C.c_float), ("down_layout", C.c_int32),
         ("gate_q", C.c_void_p), ("up_q", C.c_void_p), ("down_q", C.c_void_p),
         ("gate_s", C.c_void_p), ("gate_b", C.c_void_p), ("up_s", C.c_void_p), ("up_b", C.c_void_p),
         ("down_s", C.c_void_p), ("down_b", C.c_void_p),
@@ -49,8 +50,8 @@ class PlanStruct(C.Structure):
 _lib = None
 
 EXPORTS = ("moe_route_topk", "moe_expert_plan", "moe_route_plan", "moe_workspace_size", "moe_decode_step",
-           "moe_expert_gate_up", "moe_expert_down_combine", "moe_layer_check", "moe_status_str",
-           "moe_abi_version")
+           "moe_expert_gate_up", "moe_expert_down_combine", "moe_pack_down", "moe_layer_check",
+           "moe_status_str", "moe_abi_version")
 
 
 def library_path() -> str:
@@ -85,6 +86,8 @@ def lib() -> C.CDLL:
         L.moe_expert_down_combine.argtypes = [C.POINTER(LayerStruct), i32, vp, vp, C.POINTER(PlanStruct), vp,
                                               vp, vp, C.c_size_t, vp]
         L.moe_expert_down_combine.restype = C.c_int
+        L.moe_pack_down.argtypes = [C.POINTER(LayerStruct), vp, vp, vp, vp]
+        L.moe_pack_down.restype = C.c_int
         L.moe_layer_check.argtypes = [C.POINTER(LayerStruct)]
         L.moe_layer_check.restype = C.c_int
         L.moe_status_str.argtypes = [C.c_int]
@@ -127,9 +130,11 @@ class DeviceLayer:
     clamp_limit: float
     tensors: dict
     struct: LayerStruct
+    down_layout: int = MOE_DOWN_ROWS
 
     @staticmethod
-    def from_tensors(hidden, dff, n_experts, top_k, act: str, clamp_limit: float, tensors: dict):
+    def from_tensors(hidden, dff, n_experts, top_k, act: str, clamp_limit: float, tensors: dict,
+                     down_layout: int = MOE_DOWN_ROWS):
         """``tensors``: gate_q/up_q/down_q (int32 or uint32 words), *_s/*_b (fp16 bits as
         int16/uint16), optional 'sidecar' (fp32 [E]); all on the same device."""
         t = {k: v for k, v in tensors.items() if v is not None}
@@ -138,12 +143,30 @@ class DeviceLayer:
                 raise ValueError(f"{k} must be contiguous")
         st = LayerStruct(hidden=hidden, dff=dff, n_experts=n_experts, top_k=top_k, bits=4,
                          group_size=64, act_dtype=MOE_DTYPE_BF16 if act == "bf16" else MOE_DTYPE_F32,
-                         clamp_limit=float(clamp_limit))
+                         clamp_limit=float(clamp_limit), down_layout=down_layout)
         for name in ("gate_q", "up_q", "down_q", "gate_s", "gate_b", "up_s", "up_b", "down_s", "down_b"):
             setattr(st, name, t[name].data_ptr())
         sc = t.get("sidecar")
         st.expert_scale = None if sc is None else sc.data_ptr()
-        return DeviceLayer(hidden, dff, n_experts, top_k, st.act_dtype, float(clamp_limit), t, st)
+        return DeviceLayer(hidden, dff, n_experts, top_k, st.act_dtype, float(clamp_limit), t, st, down_layout)
+
+    def pack_down(self, stream=None, free_rows: bool = False) -> "DeviceLayer":
+        """A copy of this layer whose down projection is regrouped to MOE_DOWN_COLS
+        (moe_pack_down); gate/up and the sidecar are shared."""
+        if self.down_layout != MOE_DOWN_ROWS:
+            raise ValueError("the down projection is already packed")
+        t = dict(self.tensors)
+        q = torch.empty_like(t["down_q"])
+        s = torch.empty_like(t["down_s"])
+        b = torch.empty_like(t["down_b"])
+        _check(lib().moe_pack_down(C.byref(self.struct), _ptr(q), _ptr(s), _ptr(b), _stream(stream)),
+               "moe_pack_down")
+        if free_rows:
+            torch.cuda.current_stream().synchronize() if stream is None else stream.synchronize()
+        t["down_q"], t["down_s"], t["down_b"] = q, s, b
+        act = "bf16" if self.act_dtype == MOE_DTYPE_BF16 else "f32"
+        return DeviceLayer.from_tensors(self.hidden, self.dff, self.n_experts, self.top_k, act, self.clamp_limit,
+                                        t, down_layout=MOE_DOWN_COLS)
 
     @staticmethod
     def from_host(layer, device="cuda"):

@@ -40,6 +40,18 @@ bool pick_geometry_gate_up(int K, Geometry *g) {
     return pick_geometry(K, g);
 }
 
+// Column-layout down projection: NW waves split the dff/32 chunks, CPW
+// chunks each; 16 waves when that leaves 2..4 chunks per wave, else 8, else 4.
+bool pick_down_cols(int dff, int *nw, int *cpw) {
+    if (dff <= 0 || dff % 128) return false;
+    const int C = dff / 32;
+    if (C % 16 == 0 && C / 16 >= 2 && C / 16 <= 4) *nw = 16;
+    else if (C % 8 == 0 && C / 8 <= 3) *nw = 8;
+    else *nw = 4;
+    *cpw = C / *nw;
+    return *cpw <= 7 && C % *nw == 0;
+}
+
 static bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 
 moe_status check_layer(const moe_layer_t *L) {
@@ -61,7 +73,15 @@ moe_status check_layer(const moe_layer_t *L) {
         if (!p || !aligned(p, 4)) return MOE_ERR_INVALID_ARG;
     if (L->expert_scale && !aligned(L->expert_scale, 4)) return MOE_ERR_INVALID_ARG;
     Geometry g;
-    if (!pick_geometry_gate_up(L->hidden, &g) || !pick_geometry(L->dff, &g)) return MOE_ERR_UNSUPPORTED;
+    if (!pick_geometry_gate_up(L->hidden, &g)) return MOE_ERR_UNSUPPORTED;
+    if (L->down_layout == MOE_DOWN_ROWS) {
+        if (!pick_geometry(L->dff, &g)) return MOE_ERR_UNSUPPORTED;
+    } else if (L->down_layout == MOE_DOWN_COLS) {
+        int nw, cpw;
+        if (!pick_down_cols(L->dff, &nw, &cpw)) return MOE_ERR_UNSUPPORTED;
+    } else {
+        return MOE_ERR_INVALID_ARG;
+    }
     return MOE_OK;
 }
 
@@ -117,6 +137,6 @@ const char *moe_status_str(moe_status s) {
     return "unknown status";
 }
 
-int32_t moe_abi_version(void) { return 2; }
+int32_t moe_abi_version(void) { return 3; }
 
 }  // extern "C"

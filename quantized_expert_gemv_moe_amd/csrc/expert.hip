@@ -216,6 +216,17 @@ __device__ __forceinline__ float wave_sum8(const float *v) {
     return m;
 }
 
+// Wave-wide sum; every lane gets the same total.
+__device__ __forceinline__ float wave_sum_all(float v) {
+    v += dpp<kDppQuad1032>(v);
+    v += dpp<kDppQuad2301>(v);
+    v += dpp<kDppHalfMirror>(v);
+    v += dpp<kDppMirror>(v);  // every lane: its 16-lane row total
+    v = swap16_sum(v, v);     // rows (0,1) and (2,3)
+    v = swap32_sum(v, v);     // halves
+    return v;
+}
+
 // ---------------------------------------------------------------- gate+up
 
 __device__ __forceinline__ float silu_mul(float g, float u, float sc, float lim) {
@@ -428,6 +439,99 @@ __global__ __launch_bounds__(kBlock) void down_kernel(DownArgs a) {
     }
 }
 
+// -------------------------------------------------- down, column layout
+
+// MOE_DOWN_COLS: lane = output row, so the 32 h values of a chunk are the
+// same for the whole wave and come in through scalar loads (no LDS staging,
+// no cross-lane dot reductions).  NW waves split dff, CPW chunks of 32
+// inputs each, and their partial sums meet in LDS, added in wave order.
+// Chunks are the outer loop and up to kDownColsStage slots the inner one:
+// a chunk's 32 weights are converted once for all the expert's tokens.
+constexpr int kDownColsStage = 8;  // slots per LDS stage
+
+template <int NW, int CPW>
+__global__ __launch_bounds__(NW * kWave) void down_cols_kernel(const uint4 *__restrict__ q,
+                                                               const uint16_t *__restrict__ sc,
+                                                               const uint16_t *__restrict__ bi,
+                                                               const float *__restrict__ h,
+                                                               float *__restrict__ y, PlanView plan,
+                                                               int hidden, int dff, int n_experts,
+                                                               int n_slots) {
+    constexpr int S = kDownColsStage;
+    __shared__ float part[NW][S][kWave];
+    Work wk;
+    if (!plan_expert(plan, blockIdx.y, n_experts, n_slots, &wk)) return;
+    const int lane = threadIdx.x & (kWave - 1);
+    // wave index as a scalar: addresses built from it stay wave-uniform
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int H = hidden, F = dff, C = F / 32, G = F / kGroup;
+    const int m = blockIdx.x * kWave + lane;  // hidden % 64 == 0: always a row
+    const int c0 = wave * CPW;
+
+    uint4 wq[CPW];
+    float ws[CPW], wb[CPW];
+#pragma unroll
+    for (int j = 0; j < CPW; ++j) {
+        const int c = c0 + j;
+        wq[j] = load_stream(q + ((size_t)wk.e * C + c) * H + m);
+        const size_t gi = ((size_t)wk.e * G + c / 2) * H + m;
+        ws[j] = f16_bits_to_f32(sc[gi]);
+        // a group's bias is applied once, with the sum of its 64 inputs, by its even chunk
+        wb[j] = (c & 1) ? 0.f : f16_bits_to_f32(bi[gi]);
+    }
+
+    for (int s0 = 0; s0 < wk.count; s0 += S) {
+        const int ns = wk.count - s0 < S ? wk.count - s0 : S;
+        const float *hs[S];
+#pragma unroll
+        for (int i = 0; i < S; ++i) hs[i] = h + (size_t)plan_slot(plan, wk, i < ns ? s0 + i : s0, n_slots) * F;
+        float acc[S];
+#pragma unroll
+        for (int i = 0; i < S; ++i) acc[i] = 0.f;
+#pragma unroll
+        for (int j = 0; j < CPW; ++j) {
+            const int c = c0 + j;
+            float wf[32];
+            const uint32_t wd[4] = {wq[j].x, wq[j].y, wq[j].z, wq[j].w};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {  // element 8k + i = nibble i of word k
+                const uint32_t lo = wd[k] & 0x0F0F0F0Fu, hi = (wd[k] >> 4) & 0x0F0F0F0Fu;
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    wf[8 * k + 2 * b] = (float)((lo >> (8 * b)) & 0xFFu);
+                    wf[8 * k + 2 * b + 1] = (float)((hi >> (8 * b)) & 0xFFu);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < S; ++i) {
+                if (i >= ns) break;  // uniform
+                const float gsum = (c & 1) ? 0.f : wave_sum_all(hs[i][(c / 2) * kGroup + lane]);
+                const float *hc = hs[i] + c * 32;  // wave-uniform: scalar loads
+                float d0 = 0.f, d1 = 0.f, d2 = 0.f, d3 = 0.f;
+#pragma unroll
+                for (int t = 0; t < 8; ++t) {
+                    d0 = fmaf(wf[t], hc[t], d0);
+                    d1 = fmaf(wf[8 + t], hc[8 + t], d1);
+                    d2 = fmaf(wf[16 + t], hc[16 + t], d2);
+                    d3 = fmaf(wf[24 + t], hc[24 + t], d3);
+                }
+                acc[i] += fmaf(ws[j], (d0 + d1) + (d2 + d3), wb[j] * gsum);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < S; ++i)
+            if (i < ns) part[wave][i][lane] = acc[i];
+        __syncthreads();
+        for (int i = wave; i < ns; i += NW) {
+            float v = part[0][i][lane];
+#pragma unroll
+            for (int w = 1; w < NW; ++w) v += part[w][i][lane];
+            y[(size_t)plan_slot(plan, wk, s0 + i, n_slots) * H + m] = v;
+        }
+        __syncthreads();
+    }
+}
+
 // ---------------------------------------------------------------- combine
 
 template <bool BF16>
@@ -490,6 +594,29 @@ static moe_status launch_down(DownArgs a, int groups_y, int max_count, hipStream
     a.slots_per_stage = S;
     const dim3 grid((a.hidden + rows - 1) / rows, groups_y);
     hipLaunchKernelGGL((down_kernel<LPR, NV, RI>), grid, dim3(kBlock), S * per_slot, s, a);
+    return MOE_OK;
+}
+
+template <int NW, int CPW>
+static void launch_down_cols_t(const moe_layer_t *L, const float *h, float *y, PlanView pv, int groups_y,
+                               int n_slots, hipStream_t s) {
+    const dim3 grid(L->hidden / kWave, groups_y);
+    hipLaunchKernelGGL((down_cols_kernel<NW, CPW>), grid, dim3(NW * kWave), 0, s, (const uint4 *)L->down_q,
+                       L->down_s, L->down_b, h, y, pv, L->hidden, L->dff, L->n_experts, n_slots);
+}
+
+static moe_status launch_down_cols(const moe_layer_t *L, const float *h, float *y, PlanView pv, int groups_y,
+                                   int n_slots, hipStream_t s) {
+    int nw, cpw;
+    if (!pick_down_cols(L->dff, &nw, &cpw)) return MOE_ERR_UNSUPPORTED;
+    switch (nw * 100 + cpw) {
+#define MOE_DC(NW, CPW) case NW * 100 + CPW: launch_down_cols_t<NW, CPW>(L, h, y, pv, groups_y, n_slots, s); break;
+        MOE_DC(4, 1) MOE_DC(4, 3) MOE_DC(4, 5) MOE_DC(4, 7)
+        MOE_DC(8, 1) MOE_DC(8, 2) MOE_DC(8, 3)
+        MOE_DC(16, 2) MOE_DC(16, 3) MOE_DC(16, 4)
+#undef MOE_DC
+        default: return MOE_ERR_UNSUPPORTED;
+    }
     return MOE_OK;
 }
 
@@ -560,15 +687,20 @@ static moe_status enqueue_down_combine(const moe_layer_t *layer, int n_tokens, c
                                        const float *topk_w, const moe_plan_t *plan,
                                        const void *residual, void *out, void *workspace,
                                        hipStream_t stream) {
-    Geometry gd;
-    pick_geometry(layer->dff, &gd);
     const Workspace ws = workspace_layout(layer, n_tokens);
     const float *h = (const float *)((char *)workspace + ws.h_off);
     float *y = (float *)((char *)workspace + ws.y_off);
-    DownArgs da{(const uint4 *)layer->down_q, layer->down_s, layer->down_b, h, plan_view(plan), y,
-                layer->hidden, layer->dff, layer->n_experts, n_tokens * layer->top_k, 1};
     moe_status st;
-    MOE_GEOMETRY_SWITCH(gd, st, launch_down, da, groups_y_of(layer, n_tokens), n_tokens, stream)
+    if (layer->down_layout == MOE_DOWN_COLS) {
+        st = launch_down_cols(layer, h, y, plan_view(plan), groups_y_of(layer, n_tokens),
+                              n_tokens * layer->top_k, stream);
+    } else {
+        Geometry gd;
+        pick_geometry(layer->dff, &gd);
+        DownArgs da{(const uint4 *)layer->down_q, layer->down_s, layer->down_b, h, plan_view(plan), y,
+                    layer->hidden, layer->dff, layer->n_experts, n_tokens * layer->top_k, 1};
+        MOE_GEOMETRY_SWITCH(gd, st, launch_down, da, groups_y_of(layer, n_tokens), n_tokens, stream)
+    }
     if (st != MOE_OK) return st;
     const dim3 cgrid((layer->hidden + kBlock - 1) / kBlock, n_tokens);
     if (layer->act_dtype == MOE_DTYPE_BF16)

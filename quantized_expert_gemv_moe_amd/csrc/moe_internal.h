@@ -17,6 +17,9 @@ struct Geometry {
 };
 bool pick_geometry(int K, Geometry *g);
 bool pick_geometry_gate_up(int K, Geometry *g);
+// Waves per workgroup and 32-input chunks per wave of the column-layout down
+// kernel; false when that layout has no kernel for this dff.
+bool pick_down_cols(int dff, int *nw, int *cpw);
 
 // Validation without device access.
 moe_status check_layer(const moe_layer_t *layer);

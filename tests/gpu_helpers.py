@@ -63,9 +63,13 @@ class GpuRun:
     """One layer step on the GPU through the C ABI, results as numpy."""
 
     def __init__(self, layer_np, x: np.ndarray, logits: np.ndarray, residual: np.ndarray = None,
-                 dl=None, max_tokens=None):
+                 dl=None, max_tokens=None, cols: bool = False):
         sh = layer_np.shape
-        self.dl = dl or moe.DeviceLayer.from_host(layer_np)
+        if dl is None:
+            dl = moe.DeviceLayer.from_host(layer_np)
+            if cols:
+                dl = dl.pack_down()
+        self.dl = dl
         B = x.shape[0]
         self.B = B
         mt = max(max_tokens or B, 1)

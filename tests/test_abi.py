@@ -32,7 +32,7 @@ def test_library_exports_every_declared_function():
     assert set(declared) == set(_lib.EXPORTS)
     for name in declared:
         assert hasattr(L, name), name
-    assert L.moe_abi_version() == 2
+    assert L.moe_abi_version() == 3
 
 
 def test_status_strings():
@@ -59,6 +59,8 @@ def check(**kw):
 
 def test_layer_check_accepts_the_workload_shapes():
     assert check() == moe.MOE_OK
+    assert check(down_layout=moe.MOE_DOWN_COLS) == moe.MOE_OK
+    assert check(hidden=4096, dff=2048, n_experts=256, top_k=6, down_layout=moe.MOE_DOWN_COLS) == moe.MOE_OK
     assert check(hidden=256, dff=128, n_experts=8, top_k=2, act_dtype=moe.MOE_DTYPE_F32) == moe.MOE_OK
     assert check(hidden=4096, dff=2048, n_experts=256, top_k=6, clamp_limit=10.0,
                  expert_scale=FAKE + 0x9000000) == moe.MOE_OK
@@ -80,6 +82,9 @@ def test_layer_check_accepts_the_workload_shapes():
     (dict(gate_q=None), moe.MOE_ERR_INVALID_ARG),
     (dict(down_q=FAKE + 8), moe.MOE_ERR_INVALID_ARG),  # not 16-byte aligned
     (dict(up_s=FAKE + 2), moe.MOE_ERR_INVALID_ARG),
+    (dict(down_layout=5), moe.MOE_ERR_INVALID_ARG),
+    (dict(dff=1152, down_layout=moe.MOE_DOWN_COLS), moe.MOE_ERR_UNSUPPORTED),  # 36 chunks: no column kernel
+    (dict(dff=192, down_layout=moe.MOE_DOWN_COLS), moe.MOE_ERR_UNSUPPORTED),   # dff % 128 != 0
 ])
 def test_layer_check_rejects(kw, want):
     assert check(**kw) == want
@@ -154,6 +159,22 @@ def test_decode_step_validation_before_any_launch():
     assert call(plan=None) == moe.MOE_ERR_INVALID_ARG
     assert call(plan=_lib.PlanStruct(FAKE, FAKE, None, FAKE, FAKE, FAKE)) == moe.MOE_ERR_INVALID_ARG
     assert call(plan=_lib.PlanStruct(FAKE, FAKE, FAKE, FAKE, FAKE, None)) == moe.MOE_ERR_INVALID_ARG
+
+
+def test_pack_down_validation_before_any_launch():
+    L = moe.lib()
+    f = L.moe_pack_down
+    D = FAKE + 0x40000000
+    assert f(C.byref(layer(down_layout=moe.MOE_DOWN_COLS)), D, D + 0x10000000, D + 0x20000000, None) == \
+        moe.MOE_ERR_INVALID_ARG                                                  # already packed
+    assert f(C.byref(layer(dff=1152)), D, D + 0x10000000, D + 0x20000000, None) == moe.MOE_ERR_UNSUPPORTED
+    assert f(C.byref(layer()), None, D + 0x10000000, D + 0x20000000, None) == moe.MOE_ERR_INVALID_ARG
+    assert f(C.byref(layer()), D + 4, D + 0x10000000, D + 0x20000000, None) == moe.MOE_ERR_INVALID_ARG
+    src = layer()
+    # destination overlapping the source down weights
+    assert f(C.byref(src), src.down_q, D + 0x10000000, D + 0x20000000, None) == moe.MOE_ERR_INVALID_ARG
+    # overlapping destinations
+    assert f(C.byref(src), D, D + 16, D + 0x20000000, None) == moe.MOE_ERR_INVALID_ARG
 
 
 def test_binding_raises_on_error_status():

@@ -149,15 +149,16 @@ DECODE_CASES = [
 ]
 
 
+@pytest.mark.parametrize("layout", ["rows", "cols"])
 @pytest.mark.parametrize("name,B,regime,xs", DECODE_CASES)
-def test_decode_step_matches_oracle(name, B, regime, xs):
+def test_decode_step_matches_oracle(name, B, regime, xs, layout):
     sh = SHAPES[name]
-    log(f"[case] decode {name} B={B} {regime} x*{xs}")
+    log(f"[case] decode {name} B={B} {regime} x*{xs} down={layout}")
     lg = make_logits(sh, B, regime=regime, seed=3)
     L = layer_for(sh, lg, seed=3) if sh.n_experts > 8 else make_layer(sh, seed=3)
     x = make_x(sh, B, seed=3, scale=xs)
-    run = GpuRun(L, x, lg)
-    check_against_oracle(L, x, lg, run, f"{name}/B{B}/{regime}/x{xs}")
+    run = GpuRun(L, x, lg, cols=layout == "cols")
+    check_against_oracle(L, x, lg, run, f"{name}/B{B}/{regime}/x{xs}/{layout}")
     if xs > 1.0:
         h64 = oracle.decode_step(L, x, *oracle.route_topk(lg, sh.top_k), want_h=True)[1]
         lim = 10.0 / (1 + np.exp(-10.0)) * 10.0
@@ -182,8 +183,41 @@ def test_decode_step_other_shapes(H, F, E, k, act):
     check_against_oracle(L, x, lg, run, f"{H}x{F}x{E}x{k}/{act}")
 
 
+@pytest.mark.parametrize("E,H,F", [(3, 128, 128), (2, 256, 768), (4, 64, 2048), (1, 128, 384)])
+def test_pack_down_is_the_stated_byte_permutation(E, H, F):
+    sh = Shape(f"pk{H}x{F}", 34, H, F, E, 1, "bf16")
+    L = make_layer(sh, seed=F)
+    dl = moe.DeviceLayer.from_host(L)
+    pk = dl.pack_down()
+    torch.cuda.synchronize()
+    q = pk.tensors["down_q"].cpu().numpy().view(np.uint32).reshape(E, F // 32, H, 4)
+    want = L.down_q.reshape(E, H, F // 32, 4).transpose(0, 2, 1, 3)
+    assert np.array_equal(q, want)
+    for n in ("down_s", "down_b"):
+        got = pk.tensors[n].cpu().numpy().view(np.uint16).reshape(E, F // 64, H)
+        assert np.array_equal(got, getattr(L, n).transpose(0, 2, 1))
+    # the source is untouched and gate/up are shared
+    assert np.array_equal(dl.tensors["down_q"].cpu().numpy().view(np.uint32), L.down_q)
+    assert pk.tensors["gate_q"].data_ptr() == dl.tensors["gate_q"].data_ptr()
+
+
+@pytest.mark.parametrize("H,F,E,k", [(512, 128, 8, 2), (256, 256, 4, 4), (128, 512, 4, 2), (256, 1536, 4, 2),
+                                     (128, 640, 2, 1), (128, 896, 2, 2), (128, 384, 2, 2), (128, 1024, 2, 2),
+                                     (256, 768, 1, 1)])
+def test_decode_step_column_layout_geometries(H, F, E, k):
+    """Every (waves, chunks per wave) pairing of the column-layout down kernel."""
+    sh = Shape(f"c{H}x{F}", 35, H, F, E, k, "bf16")
+    B = 9  # more slots than one LDS stage (8) for some experts; all 9 when E = 1
+    lg = make_logits(sh, B, seed=H * F)
+    L = make_layer(sh, seed=H * F)
+    x = make_x(sh, B, seed=H * F)
+    run = GpuRun(L, x, lg, cols=True)
+    check_against_oracle(L, x, lg, run, f"cols {H}x{F}x{E}x{k}")
+
+
 # --------------------------------------------------------------- invariants
-def test_determinism_batch_invariance_permutation_and_duplicates():
+@pytest.mark.parametrize("layout", ["rows", "cols"])
+def test_determinism_batch_invariance_permutation_and_duplicates(layout):
     sh = SHAPES["cohort"]
     B = 8
     lg = make_logits(sh, B, regime="sharing", seed=9)
@@ -191,6 +225,8 @@ def test_determinism_batch_invariance_permutation_and_duplicates():
     dup_lg = np.repeat(lg[2:3], 4, axis=0)
     L = layer_for(sh, np.concatenate([lg, dup_lg]), seed=9)
     dl = moe.DeviceLayer.from_host(L)
+    if layout == "cols":
+        dl = dl.pack_down()
     a = GpuRun(L, x, lg, dl=dl)
     b = GpuRun(L, x, lg, dl=dl)
     assert np.array_equal(a.out, b.out), "run-to-run results differ"
