@@ -44,11 +44,13 @@ using namespace moe;
 
 extern "C" moe_status moe_pack_down(const moe_layer_t *layer, uint32_t *dst_q, uint16_t *dst_s,
                                     uint16_t *dst_b, void *hip_stream) {
-    moe_status st = check_layer(layer);
-    if (st != MOE_OK) return st;
+    if (!layer) return MOE_ERR_INVALID_ARG;
     if (layer->down_layout != MOE_DOWN_ROWS) return MOE_ERR_INVALID_ARG;
-    int nw, cpw;
-    if (!pick_down_cols(layer->dff, &nw, &cpw)) return MOE_ERR_UNSUPPORTED;  // no column kernel for this dff
+    // the packed layer must be one the column kernels serve
+    moe_layer_t packed = *layer;
+    packed.down_layout = MOE_DOWN_COLS;
+    moe_status st = check_layer(&packed);
+    if (st != MOE_OK) return st;
     if (!dst_q || !dst_s || !dst_b || (uintptr_t)dst_q % 16 || (uintptr_t)dst_s % 4 || (uintptr_t)dst_b % 4)
         return MOE_ERR_INVALID_ARG;
     const int E = layer->n_experts, H = layer->hidden, F = layer->dff;
