@@ -10,11 +10,12 @@
 // "perf(moe): attribute the MoE decode gap at the M = 1 expert gather",
 // Proposed Solution step 2).
 //
-// Planner: one workgroup.  An LDS histogram of expert ids, a block-wide
-// exclusive scan into per-expert offsets and the list of distinct experts,
-// then a stable scatter of slot ids into per-expert lists by one wave in
-// slot order (ballot-based peer ranks), and one 16-byte work record per
-// distinct expert.  This is the cross-cohort deduplication of page
+// Planner: one workgroup.  Up to 64 slots, one wave does it all without a
+// barrier (ballot-ranked peers, one DPP wave scan).  Beyond that, an LDS
+// histogram of expert ids, a block-wide exclusive scan into per-expert
+// offsets and the list of distinct experts, then a stable scatter of slot
+// ids into per-expert lists by one wave in slot order.  Both write one
+// 16-byte work record per distinct expert.  This is the cross-cohort deduplication of page
 // "perf(moe): batched decode scales 1.55x against 3.25x on dense" (Proposed
 // Solution, second bullet): the expert kernels walk the distinct experts, so
 // each expert's weights are read once per step whatever the number of
@@ -256,9 +257,106 @@ __device__ __forceinline__ void plan_block(const int *idx, int n_slots, int n_ex
     }
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave (DPP: row shifts, then
+// row broadcasts of lanes 15 and 31).  Lanes whose source is out of range
+// add 0.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ int dpp_add_src(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, 0xF, false);
+}
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+    v += dpp_add_src<0x111, 0xF>(v);  // row_shr:1
+    v += dpp_add_src<0x112, 0xF>(v);  // row_shr:2
+    v += dpp_add_src<0x114, 0xF>(v);  // row_shr:4
+    v += dpp_add_src<0x118, 0xF>(v);  // row_shr:8
+    v += dpp_add_src<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+    v += dpp_add_src<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
+    return v;
+}
+
+// Planner for at most 64 slots by a single wave, without barriers: lane s
+// holds slot s.  Peer masks come from ballots over the expert-id bits; lane
+// l owns experts l*P .. l*P+P-1 for counts, offsets and the distinct list,
+// whose per-lane sums (count << 16 | nonzero) go through one wave scan.
+// LDS operations of one wave complete in order, so values one lane writes
+// are visible to the others at their next LDS read.
+// `cnt`, `off`, `uix`: LDS scratch of n_experts ints each.
+__device__ __forceinline__ void plan_wave_small(const int *idx, int n_slots, int n_experts, const PlanOut &p,
+                                                int *cnt, int *off, int *uix) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const unsigned E = (unsigned)n_experts;
+    const int P = (n_experts + kWave - 1) / kWave;  // experts owned per lane, <= 16
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+        const int e = lane * P + q;
+        if (q < P && e < n_experts) cnt[e] = 0;
+    }
+    const int id = lane < n_slots ? idx[lane] : -1;
+    const bool ok = lane < n_slots && (unsigned)id < E;
+    unsigned long long peers = __ballot(ok);
+    const int id_bits = n_experts > 1 ? 32 - __clz(n_experts - 1) : 0;
+    for (int b = 0; b < id_bits; ++b) {
+        const bool bit = ok && ((id >> b) & 1);
+        const unsigned long long m = __ballot(bit);
+        peers &= bit ? m : ~m;
+    }
+    const int rank = __popcll(peers & ((1ull << lane) - 1ull));
+    const int n_peer = __popcll(peers);
+    __builtin_amdgcn_wave_barrier();
+    if (ok && rank == 0) cnt[id] = n_peer;  // the lowest peer lane is the expert's first slot
+    __builtin_amdgcn_wave_barrier();
+    int c[16], sum = 0;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+        const int e = lane * P + q;
+        c[q] = (q < P && e < n_experts) ? cnt[e] : 0;
+        sum += (c[q] << 16) + (c[q] > 0 ? 1 : 0);
+    }
+    const int inc = wave_inclusive_scan(sum);
+    const int tot = __builtin_amdgcn_readlane(inc, kWave - 1);
+    const int total_slots = tot >> 16, total_unique = tot & 0xFFFF;
+    const int excl = inc - sum;  // both fields non-negative: no borrow between them
+    int run = excl >> 16, urun = excl & 0xFFFF;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+        const int e = lane * P + q;
+        if (q < P && e < n_experts) {
+            p.counts[e] = c[q];
+            p.offsets[e] = run;
+            off[e] = run;
+            if (c[q] > 0) {
+                p.unique_experts[urun] = e;
+                uix[e] = urun;
+                ++urun;
+            }
+            run += c[q];
+        }
+    }
+    __builtin_amdgcn_wave_barrier();
+    if (ok) {
+        const int base = off[id];
+        p.sorted_slots[base + rank] = lane;
+        if (rank == 0) p.work[uix[id]] = make_int4(id, base, n_peer, lane);
+    }
+    for (int u = total_unique + lane; u < n_experts; u += kWave) {
+        p.unique_experts[u] = -1;
+        p.work[u] = make_int4(-1, total_slots, 0, 0);
+    }
+    if (lane == 0) {
+        p.offsets[n_experts] = total_slots;
+        p.n_unique[0] = total_unique;
+    }
+}
+
+// Small plans (<= 64 slots) run on one wave; larger ones on 256 threads.
 __global__ __launch_bounds__(kBlock) void expert_plan_kernel(const int *__restrict__ topk_idx, int n_slots,
                                                              int n_experts, PlanOut p) {
-    plan_block(topk_idx, n_slots, n_experts, p);
+    if (n_slots <= kWave) {
+        __shared__ int cnt[MOE_MAX_EXPERTS], off[MOE_MAX_EXPERTS], uix[MOE_MAX_EXPERTS];
+        if (threadIdx.x < kWave) plan_wave_small(topk_idx, n_slots, n_experts, p, cnt, off, uix);
+    } else {
+        plan_block(topk_idx, n_slots, n_experts, p);
+    }
 }
 
 // Router and planner in one workgroup: the four waves route the tokens, the
@@ -270,7 +368,8 @@ __global__ __launch_bounds__(kBlock) void route_plan_kernel(const float *__restr
                                                             float *__restrict__ topk_w, PlanOut p) {
     __shared__ int idx_lds[kRoutePlanMaxSlots];
     const int lane = threadIdx.x & (kWave - 1);
-    for (int t = threadIdx.x / kWave; t < n_tokens; t += kBlock / kWave) {
+    const int n_waves = blockDim.x / kWave;
+    for (int t = threadIdx.x / kWave; t < n_tokens; t += n_waves) {
         int id;
         float w;
         if (route_token<PER_LANE>(logits + (size_t)t * n_experts, n_experts, top_k, &id, &w)) {
@@ -280,7 +379,13 @@ __global__ __launch_bounds__(kBlock) void route_plan_kernel(const float *__restr
         }
     }
     __syncthreads();
-    plan_block(idx_lds, n_tokens * top_k, n_experts, p);
+    const int n_slots = n_tokens * top_k;
+    if (n_slots <= kWave) {  // launched with one wave per token, at most four
+        __shared__ int cnt[MOE_MAX_EXPERTS], off[MOE_MAX_EXPERTS], uix[MOE_MAX_EXPERTS];
+        if (threadIdx.x < kWave) plan_wave_small(idx_lds, n_slots, n_experts, p, cnt, off, uix);
+    } else {                 // launched with 256 threads
+        plan_block(idx_lds, n_slots, n_experts, p);
+    }
 }
 
 static int per_lane_bucket(int n_experts) {
@@ -325,8 +430,9 @@ extern "C" moe_status moe_expert_plan(const int32_t *topk_idx, int32_t n_tokens,
     const moe_status st = check_plan_args(topk_idx, n_tokens, n_experts, top_k, plan);
     if (st != MOE_OK) return st;
     hipStream_t stream = (hipStream_t)hip_stream;
-    hipLaunchKernelGGL(expert_plan_kernel, dim3(1), dim3(kBlock), 0, stream, topk_idx,
-                       n_tokens * top_k, n_experts, plan_out(plan));
+    const int n_slots = n_tokens * top_k;
+    hipLaunchKernelGGL(expert_plan_kernel, dim3(1), dim3(n_slots <= kWave ? kWave : kBlock), 0, stream,
+                       topk_idx, n_slots, n_experts, plan_out(plan));
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_DEVICE;
 }
 
@@ -344,8 +450,11 @@ extern "C" moe_status moe_route_plan(const float *logits, int32_t n_tokens, int3
         if (st != MOE_OK) return st;
         return moe_expert_plan(topk_idx, n_tokens, n_experts, top_k, plan, hip_stream);
     }
+    // small batches: one wave per token (at most four); else a full block for the planner
+    const int n_slots = n_tokens * top_k;
+    const int threads = n_slots <= kWave ? kWave * (n_tokens < 4 ? (n_tokens > 0 ? n_tokens : 1) : 4) : kBlock;
     MOE_PER_LANE_SWITCH(per_lane_bucket(n_experts),
-                        hipLaunchKernelGGL(route_plan_kernel<PL>, dim3(1), dim3(kBlock), 0, stream, logits,
+                        hipLaunchKernelGGL(route_plan_kernel<PL>, dim3(1), dim3(threads), 0, stream, logits,
                                            n_tokens, n_experts, top_k, topk_idx, topk_w, plan_out(plan)))
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_DEVICE;
 }
