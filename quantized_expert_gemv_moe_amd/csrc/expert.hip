@@ -114,23 +114,29 @@ __device__ __forceinline__ float dot32_q4_bf16(uint4 q, const uint32_t *xp) {
     return (a0 + a1) + (a2 + a3);
 }
 
-// 32 bf16 activations starting at element c0 of row xr: the 16 pairs used by
-// dot8_q4_bf16 and their fp32 sum.
-__device__ __forceinline__ float load_x32_bf16_pairs(const uint16_t *x, size_t xr, int c0,
-                                                     uint32_t *xp) {
+// 32 bf16 activations starting at element c0 of row xr, as loaded 16-byte
+// words.
+__device__ __forceinline__ void load_x32_bf16(const uint16_t *x, size_t xr, int c0, uint4 *raw) {
     const uint4 *p = (const uint4 *)(x + xr + c0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) raw[i] = p[i];
+}
+
+// The 16 pairs used by dot8_q4_bf16 from the loaded words, and the sum of
+// the 32 activations (dot2 against the pair (1, 1): exact products, fp32
+// accumulation).
+__device__ __forceinline__ float x32_pairs(const uint4 *raw, uint32_t *xp) {
+    const uint32_t ones = 0x3F803F80u;  // bf16 (1.0, 1.0)
     float s0 = 0.f, s1 = 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const uint4 w = p[i];  // elements 8i .. 8i+7 as (x0,x1),(x2,x3),(x4,x5),(x6,x7)
+        const uint4 w = raw[i];  // elements 8i .. 8i+7 as (x0,x1),(x2,x3),(x4,x5),(x6,x7)
         xp[4 * i + 0] = (w.x & 0xFFFFu) | (w.z << 16);
         xp[4 * i + 1] = (w.x >> 16) | (w.z & 0xFFFF0000u);
         xp[4 * i + 2] = (w.y & 0xFFFFu) | (w.w << 16);
         xp[4 * i + 3] = (w.y >> 16) | (w.w & 0xFFFF0000u);
-        s0 += (bf16_bits_to_f32(w.x & 0xFFFFu) + bf16_bits_to_f32(w.x >> 16)) +
-              (bf16_bits_to_f32(w.y & 0xFFFFu) + bf16_bits_to_f32(w.y >> 16));
-        s1 += (bf16_bits_to_f32(w.z & 0xFFFFu) + bf16_bits_to_f32(w.z >> 16)) +
-              (bf16_bits_to_f32(w.w & 0xFFFFu) + bf16_bits_to_f32(w.w >> 16));
+        s0 = dot2_bf16(w.x, ones, dot2_bf16(w.y, ones, s0));
+        s1 = dot2_bf16(w.z, ones, dot2_bf16(w.w, ones, s1));
     }
     return s0 + s1;
 }
@@ -247,12 +253,23 @@ __global__ __launch_bounds__(kWave) void gate_up_kernel(GateUpArgs a) {
     constexpr int ROWS_WG = RPI * RI;
     constexpr int TCH = (XBF16 && NV == 1) ? 2 : 1;
     constexpr bool WAVE8 = (LPR == kWave && RI == 4);
+    const int lane = threadIdx.x;
+    const int sl = lane % LPR;
+    // With one token in the batch its activations are known before the plan
+    // record arrives: issue those loads now, so the record's round trip and
+    // theirs overlap.
+    const bool one_token = XBF16 && a.n_slots == a.top_k;
+    uint4 xraw0[XBF16 ? NV : 1][4];
+    if constexpr (XBF16) {
+        if (one_token) {
+#pragma unroll
+            for (int v = 0; v < NV; ++v) load_x32_bf16((const uint16_t *)a.x, 0, (v * LPR + sl) * 32, xraw0[v]);
+        }
+    }
     Work wk;
     if (!plan_expert(a.plan, blockIdx.y, a.n_experts, a.n_slots, &wk)) return;
     const int e = wk.e, count = wk.count;
 
-    const int lane = threadIdx.x;
-    const int sl = lane % LPR;
     const int row0 = blockIdx.x * ROWS_WG + lane / LPR;
     const int H = a.hidden, F = a.dff;
     const int qrow = H / 32, grow = H / kGroup;
@@ -297,10 +314,18 @@ __global__ __launch_bounds__(kWave) void gate_up_kernel(GateUpArgs a) {
 #pragma unroll
             for (int v = 0; v < NV; ++v) {
                 const int c0 = (v * LPR + sl) * 32;
-                if constexpr (XBF16)
-                    xs[i][v] = load_x32_bf16_pairs((const uint16_t *)a.x, xr, c0, xp[i][v]);
-                else
+                if constexpr (XBF16) {
+                    uint4 raw[4];
+                    if (one_token) {
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) raw[q] = xraw0[v][q];
+                    } else {
+                        load_x32_bf16((const uint16_t *)a.x, xr, c0, raw);
+                    }
+                    xs[i][v] = x32_pairs(raw, xp[i][v]);
+                } else {
                     xs[i][v] = load_x32_f32((const float *)a.x, xr, c0, xf[i][v]);
+                }
             }
         }
 #pragma unroll
