@@ -34,91 +34,82 @@ namespace moe {
 
 // ----------------------------------------------------------------- router
 
+// A candidate is one 64-bit key: order-preserving bits of the logit in the
+// high word (+0 and -0 made equal first) and the complement of the expert
+// id in the low word, so the unsigned maximum is the larger logit and, on
+// equal logits, the lower id.  Key 0 is "no candidate".
+__device__ __forceinline__ unsigned long long route_key(float v, int id) {
+    const uint32_t u = __float_as_uint(v + 0.0f);
+    const uint32_t hi = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return ((unsigned long long)hi << 32) | (uint32_t)~(uint32_t)id;
+}
+__device__ __forceinline__ float key_value(unsigned long long k) {
+    const uint32_t hi = (uint32_t)(k >> 32);
+    return __uint_as_float((hi & 0x80000000u) ? (hi & 0x7FFFFFFFu) : ~hi);
+}
+__device__ __forceinline__ int key_id(unsigned long long k) { return (int)~(uint32_t)k; }
+
+__device__ __forceinline__ unsigned long long umax64(unsigned long long a, unsigned long long b) {
+    return a > b ? a : b;
+}
+
 template <int CTRL>
-__device__ __forceinline__ int dpp_i(int v) {
-    return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, false);
+__device__ __forceinline__ unsigned long long dpp64(unsigned long long k) {
+    const int lo = __builtin_amdgcn_mov_dpp((int)(uint32_t)k, CTRL, 0xF, 0xF, false);
+    const int hi = __builtin_amdgcn_mov_dpp((int)(uint32_t)(k >> 32), CTRL, 0xF, 0xF, false);
+    return ((unsigned long long)(uint32_t)hi << 32) | (uint32_t)lo;
 }
 
-// Keep the better of (v, i) and (pv, pi): larger value, lower id on ties;
-// id INT_MAX marks an empty candidate.
-__device__ __forceinline__ void take_better(float &v, int &i, float pv, int pi) {
-    const bool take = pi != INT_MAX && (i == INT_MAX || pv > v || (pv == v && pi < i));
-    v = take ? pv : v;
-    i = take ? pi : i;
-}
-
-template <int CTRL>
-__device__ __forceinline__ void argmax_dpp(float &v, int &i) {
-    const float pv = __int_as_float(dpp_i<CTRL>(__float_as_int(v)));
-    const int pi = dpp_i<CTRL>(i);
-    take_better(v, i, pv, pi);
-}
-
-// Wave-wide arg-max; every lane ends with the same (value, id).
-__device__ __forceinline__ void wave_argmax(float &v, int &i) {
-    argmax_dpp<0xB1>(v, i);   // quad_perm [1,0,3,2]
-    argmax_dpp<0x4E>(v, i);   // quad_perm [2,3,0,1]
-    argmax_dpp<0x141>(v, i);  // row_half_mirror
-    argmax_dpp<0x140>(v, i);  // row_mirror
-    {   // rows (0,1) and (2,3): each lane sees both rows' candidates
-        const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-        const auto b = __builtin_amdgcn_permlane16_swap((unsigned)i, (unsigned)i, false, false);
-        float v0 = __uint_as_float(a[0]);
-        int i0 = (int)b[0];
-        take_better(v0, i0, __uint_as_float(a[1]), (int)b[1]);
-        v = v0;
-        i = i0;
+// Wave-wide maximum of the keys; every lane ends with the same key.
+__device__ __forceinline__ unsigned long long wave_max_key(unsigned long long k) {
+    k = umax64(k, dpp64<0xB1>(k));   // quad_perm [1,0,3,2]
+    k = umax64(k, dpp64<0x4E>(k));   // quad_perm [2,3,0,1]
+    k = umax64(k, dpp64<0x141>(k));  // row_half_mirror
+    k = umax64(k, dpp64<0x140>(k));  // row_mirror: each lane holds its 16-lane row maximum
+    {   // rows (0,1) and (2,3)
+        const auto lo = __builtin_amdgcn_permlane16_swap((uint32_t)k, (uint32_t)k, false, false);
+        const auto hi = __builtin_amdgcn_permlane16_swap((uint32_t)(k >> 32), (uint32_t)(k >> 32), false, false);
+        k = umax64(((unsigned long long)hi[0] << 32) | lo[0], ((unsigned long long)hi[1] << 32) | lo[1]);
     }
-    {   // halves (0..31) and (32..63)
-        const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-        const auto b = __builtin_amdgcn_permlane32_swap((unsigned)i, (unsigned)i, false, false);
-        float v0 = __uint_as_float(a[0]);
-        int i0 = (int)b[0];
-        take_better(v0, i0, __uint_as_float(a[1]), (int)b[1]);
-        v = v0;
-        i = i0;
+    {   // halves
+        const auto lo = __builtin_amdgcn_permlane32_swap((uint32_t)k, (uint32_t)k, false, false);
+        const auto hi = __builtin_amdgcn_permlane32_swap((uint32_t)(k >> 32), (uint32_t)(k >> 32), false, false);
+        k = umax64(((unsigned long long)hi[0] << 32) | lo[0], ((unsigned long long)hi[1] << 32) | lo[1]);
     }
+    return k;
 }
 
-// Top-k of one token's logits by the calling wave.  Lane j < top_k returns
-// the j-th expert id in *id and its weight in *w; returns false for lanes
-// j >= top_k.
+// Top-k of one token's logits by the calling wave: k rounds of a wave-wide
+// key maximum.  Lane j < top_k returns the j-th expert id in *id and its
+// weight in *w (softmax of the kept logits relative to the largest, the
+// denominator summed in j order); returns false for lanes j >= top_k.
 template <int PER_LANE>
 __device__ __forceinline__ bool route_token(const float *__restrict__ row, int n_experts, int top_k,
                                             int *id, float *w) {
     const int lane = threadIdx.x & (kWave - 1);
-    float v[PER_LANE];
-    uint32_t avail = 0;
+    unsigned long long key[PER_LANE];
 #pragma unroll
     for (int q = 0; q < PER_LANE; ++q) {
         const int e = lane + kWave * q;
-        v[q] = e < n_experts ? row[e] : 0.f;
-        if (e < n_experts) avail |= 1u << q;
+        key[q] = e < n_experts ? route_key(row[e], e) : 0ull;
     }
-    int my_id = 0;
-    float my_ex = 0.f, l0 = 0.f, den = 0.f;
+    unsigned long long mine = 0ull;
     for (int j = 0; j < top_k; ++j) {
-        float bv = -INFINITY;
-        int bi = INT_MAX;
+        unsigned long long best = key[0];
 #pragma unroll
-        for (int q = 0; q < PER_LANE; ++q) {  // ids ascend with q: strict > keeps the lower id
-            if (((avail >> q) & 1u) && (bi == INT_MAX || v[q] > bv)) {
-                bv = v[q];
-                bi = lane + kWave * q;
-            }
-        }
-        wave_argmax(bv, bi);
-        if (lane == (bi & (kWave - 1))) avail &= ~(1u << (bi / kWave));
-        if (j == 0) l0 = bv;
-        const float ex = expf(bv - l0);  // the same on every lane
-        den += ex;                       // j order
-        if (lane == j) {
-            my_id = bi;
-            my_ex = ex;
-        }
+        for (int q = 1; q < PER_LANE; ++q) best = umax64(best, key[q]);
+        best = wave_max_key(best);
+#pragma unroll
+        for (int q = 0; q < PER_LANE; ++q) key[q] = key[q] == best ? 0ull : key[q];  // taken
+        mine = lane == j ? best : mine;
     }
-    *id = my_id;
-    *w = my_ex / den;
+    const float v = key_value(mine);
+    const float v0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    const float ex = lane < top_k ? expf(v - v0) : 0.f;
+    float den = 0.f;
+    for (int j = 0; j < top_k; ++j) den += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ex), j));
+    *id = key_id(mine);
+    *w = ex / den;
     return lane < top_k;
 }
 
@@ -281,15 +272,15 @@ __device__ __forceinline__ int wave_inclusive_scan(int v) {
 // LDS operations of one wave complete in order, so values one lane writes
 // are visible to the others at their next LDS read.
 // `cnt`, `off`, `uix`: LDS scratch of n_experts ints each.
+template <int P>  // experts owned per lane: P >= ceil(n_experts / 64)
 __device__ __forceinline__ void plan_wave_small(const int *idx, int n_slots, int n_experts, const PlanOut &p,
                                                 int *cnt, int *off, int *uix) {
     const int lane = threadIdx.x & (kWave - 1);
     const unsigned E = (unsigned)n_experts;
-    const int P = (n_experts + kWave - 1) / kWave;  // experts owned per lane, <= 16
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
+    for (int q = 0; q < P; ++q) {
         const int e = lane * P + q;
-        if (q < P && e < n_experts) cnt[e] = 0;
+        if (e < n_experts) cnt[e] = 0;
     }
     const int id = lane < n_slots ? idx[lane] : -1;
     const bool ok = lane < n_slots && (unsigned)id < E;
@@ -305,11 +296,11 @@ __device__ __forceinline__ void plan_wave_small(const int *idx, int n_slots, int
     __builtin_amdgcn_wave_barrier();
     if (ok && rank == 0) cnt[id] = n_peer;  // the lowest peer lane is the expert's first slot
     __builtin_amdgcn_wave_barrier();
-    int c[16], sum = 0;
+    int c[P], sum = 0;
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
+    for (int q = 0; q < P; ++q) {
         const int e = lane * P + q;
-        c[q] = (q < P && e < n_experts) ? cnt[e] : 0;
+        c[q] = e < n_experts ? cnt[e] : 0;
         sum += (c[q] << 16) + (c[q] > 0 ? 1 : 0);
     }
     const int inc = wave_inclusive_scan(sum);
@@ -318,9 +309,9 @@ __device__ __forceinline__ void plan_wave_small(const int *idx, int n_slots, int
     const int excl = inc - sum;  // both fields non-negative: no borrow between them
     int run = excl >> 16, urun = excl & 0xFFFF;
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
+    for (int q = 0; q < P; ++q) {
         const int e = lane * P + q;
-        if (q < P && e < n_experts) {
+        if (e < n_experts) {
             p.counts[e] = c[q];
             p.offsets[e] = run;
             off[e] = run;
@@ -349,11 +340,12 @@ __device__ __forceinline__ void plan_wave_small(const int *idx, int n_slots, int
 }
 
 // Small plans (<= 64 slots) run on one wave; larger ones on 256 threads.
+template <int PER_LANE>
 __global__ __launch_bounds__(kBlock) void expert_plan_kernel(const int *__restrict__ topk_idx, int n_slots,
                                                              int n_experts, PlanOut p) {
     if (n_slots <= kWave) {
         __shared__ int cnt[MOE_MAX_EXPERTS], off[MOE_MAX_EXPERTS], uix[MOE_MAX_EXPERTS];
-        if (threadIdx.x < kWave) plan_wave_small(topk_idx, n_slots, n_experts, p, cnt, off, uix);
+        if (threadIdx.x < kWave) plan_wave_small<PER_LANE>(topk_idx, n_slots, n_experts, p, cnt, off, uix);
     } else {
         plan_block(topk_idx, n_slots, n_experts, p);
     }
@@ -382,7 +374,7 @@ __global__ __launch_bounds__(kBlock) void route_plan_kernel(const float *__restr
     const int n_slots = n_tokens * top_k;
     if (n_slots <= kWave) {  // launched with one wave per token, at most four
         __shared__ int cnt[MOE_MAX_EXPERTS], off[MOE_MAX_EXPERTS], uix[MOE_MAX_EXPERTS];
-        if (threadIdx.x < kWave) plan_wave_small(idx_lds, n_slots, n_experts, p, cnt, off, uix);
+        if (threadIdx.x < kWave) plan_wave_small<PER_LANE>(idx_lds, n_slots, n_experts, p, cnt, off, uix);
     } else {                 // launched with 256 threads
         plan_block(idx_lds, n_slots, n_experts, p);
     }
@@ -431,8 +423,9 @@ extern "C" moe_status moe_expert_plan(const int32_t *topk_idx, int32_t n_tokens,
     if (st != MOE_OK) return st;
     hipStream_t stream = (hipStream_t)hip_stream;
     const int n_slots = n_tokens * top_k;
-    hipLaunchKernelGGL(expert_plan_kernel, dim3(1), dim3(n_slots <= kWave ? kWave : kBlock), 0, stream,
-                       topk_idx, n_slots, n_experts, plan_out(plan));
+    MOE_PER_LANE_SWITCH(per_lane_bucket(n_experts),
+                        hipLaunchKernelGGL(expert_plan_kernel<PL>, dim3(1), dim3(n_slots <= kWave ? kWave : kBlock),
+                                           0, stream, topk_idx, n_slots, n_experts, plan_out(plan)))
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_DEVICE;
 }
 
