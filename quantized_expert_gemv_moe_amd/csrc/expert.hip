@@ -26,6 +26,7 @@
 //             LDS; exact fp32 FMAs (h is never rounded to bf16).
 //   combine : out[t] = sum_j w[t][j] * y[t*k+j] in j order, one rounding.
 #include <hip/hip_runtime.h>
+#include <limits.h>
 #include <math.h>
 
 #include "device_util.h"
@@ -49,6 +50,7 @@ struct GateUpArgs {
     PlanView plan;
     float *h;
     int hidden, dff, n_experts, top_k, n_slots;
+    int max_count;  // the VALU kernel leaves experts with more slots to the MFMA kernel
 };
 
 struct DownArgs {
@@ -268,6 +270,7 @@ __global__ __launch_bounds__(kWave) void gate_up_kernel(GateUpArgs a) {
     }
     Work wk;
     if (!plan_expert(a.plan, blockIdx.y, a.n_experts, a.n_slots, &wk)) return;
+    if (wk.count > a.max_count) return;  // the MFMA kernel's expert
     const int e = wk.e, count = wk.count;
 
     const int row0 = blockIdx.x * ROWS_WG + lane / LPR;
@@ -369,6 +372,163 @@ __global__ __launch_bounds__(kWave) void gate_up_kernel(GateUpArgs a) {
                 }
             }
         }
+    }
+}
+
+// ----------------------------------------------------- gate+up, MFMA tiles
+
+// Experts with many tokens: v_mfma_f32_16x16x32_bf16.  A workgroup of four
+// waves owns 16 * RT rows of the expert and all of hidden; wave w takes a
+// quarter of the 64-groups.  Per group and 16-row tile, each lane holds two
+// words of its row (16 nibbles) as bf16 pairs of value 128 + q, the same
+// nibble pairing as the dot2 path, and its token's activations in the same
+// pairing; two MFMAs then sum exactly one group, so the fp32 group scale
+// and the folded bias (b - 128 s) * sum(x) apply per group after the MFMA.
+// Output lane l holds token l % 16 and rows 4 * (l / 16) .. + 3.  The four
+// waves' partial sums meet in LDS and are added in wave order; tokens go in
+// tiles of 16.
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+
+__device__ __forceinline__ f32x4_t mfma16x16x32(const uint32_t *a, const uint32_t *b, f32x4_t c) {
+    typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
+    const u32x4_t av = {a[0], a[1], a[2], a[3]};
+    const u32x4_t bv = {b[0], b[1], b[2], b[3]};
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av),
+                                                   __builtin_bit_cast(bf16x8_t, bv), c, 0, 0, 0);
+}
+
+// Nibbles of one word as the four bf16 pairs (128 + q_p, 128 + q_{p+4}).
+__device__ __forceinline__ void q4_pairs(uint32_t w, uint32_t *o) {
+    const uint32_t M = 0x000F000Fu, B = 0x43004300u;
+    o[0] = (w & M) | B;
+    o[1] = ((w >> 4) & M) | B;
+    o[2] = ((w >> 8) & M) | B;
+    o[3] = ((w >> 12) & M) | B;
+}
+
+// Eight bf16 activations (one 16-byte word) as the pairs (x_p, x_{p+4}),
+// and their sum added into *acc.
+__device__ __forceinline__ void x8_pairs(uint4 w, uint32_t *o, float *acc) {
+    const uint32_t ones = 0x3F803F80u;
+    o[0] = (w.x & 0xFFFFu) | (w.z << 16);
+    o[1] = (w.x >> 16) | (w.z & 0xFFFF0000u);
+    o[2] = (w.y & 0xFFFFu) | (w.w << 16);
+    o[3] = (w.y >> 16) | (w.w & 0xFFFF0000u);
+    *acc = dot2_bf16(w.x, ones, dot2_bf16(w.y, ones, dot2_bf16(w.z, ones, dot2_bf16(w.w, ones, *acc))));
+}
+
+constexpr int kMfmaTokens = 16;  // token tile
+
+template <int RT>
+__global__ __launch_bounds__(kBlock) void gate_up_mfma_kernel(GateUpArgs a, int min_count) {
+    constexpr int ROWS = 16 * RT;
+    extern __shared__ float smem[];
+    Work wk;
+    if (!plan_expert(a.plan, blockIdx.y, a.n_experts, a.n_slots, &wk)) return;
+    if (wk.count < min_count) return;  // the expert belongs to the VALU kernel
+    const int H = a.hidden, F = a.dff, G = H / kGroup;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int r16 = lane & 15, kq = lane >> 4;
+    const int row0 = blockIdx.x * ROWS;
+    const int GW = G / 4, g0 = wave * GW;
+    // scales [group][row] in fp32, biases already shifted by -128 * scale
+    float *sg = smem, *bg = smem + G * ROWS, *su = smem + 2 * G * ROWS, *bu = smem + 3 * G * ROWS;
+    float *part = smem + 4 * G * ROWS;  // [wave][lane][8 * RT]
+
+    for (int i = threadIdx.x; i < ROWS * G; i += kBlock) {
+        const int r = i / G, g = i - r * G;
+        const int row = row0 + r < F ? row0 + r : F - 1;
+        const size_t si = ((size_t)wk.e * F + row) * G + g;
+        const float s1 = f16_bits_to_f32(a.gate_s[si]), s2 = f16_bits_to_f32(a.up_s[si]);
+        sg[g * ROWS + r] = s1;
+        bg[g * ROWS + r] = fmaf(-128.f, s1, f16_bits_to_f32(a.gate_b[si]));
+        su[g * ROWS + r] = s2;
+        bu[g * ROWS + r] = fmaf(-128.f, s2, f16_bits_to_f32(a.up_b[si]));
+    }
+    __syncthreads();
+    const float sc = a.expert_scale ? a.expert_scale[wk.e] : 1.f;
+    const float lim = a.clamp_limit;
+    const uint2 *gq = (const uint2 *)a.gate_q, *uq = (const uint2 *)a.up_q;
+
+    for (int t0 = 0; t0 < wk.count; t0 += kMfmaTokens) {
+        const int nt = wk.count - t0 < kMfmaTokens ? wk.count - t0 : kMfmaTokens;
+        const bool live = r16 < nt;  // this lane's token column
+        const int slot = live ? plan_slot(a.plan, wk, t0 + r16, a.n_slots) : 0;
+        const uint16_t *xr = (const uint16_t *)a.x + (size_t)(slot / a.top_k) * H;
+        f32x4_t accg[RT], accu[RT];
+#pragma unroll
+        for (int t = 0; t < RT; ++t) {
+            accg[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            accu[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
+        for (int gi = 0; gi < GW; ++gi) {
+            const int g = g0 + gi;
+            // elements 64g + 16kq .. + 15 of the token: the two MFMA steps' B operands
+            uint32_t xb[2][4];
+            float xs = 0.f;
+            const uint4 *xp = (const uint4 *)(xr + g * kGroup + 16 * kq);
+            const uint4 w0 = live ? xp[0] : make_uint4(0, 0, 0, 0);
+            const uint4 w1 = live ? xp[1] : make_uint4(0, 0, 0, 0);
+            x8_pairs(w0, xb[0], &xs);
+            x8_pairs(w1, xb[1], &xs);
+            xs = swap16_sum(xs, xs);  // add the four lanes of the token
+            xs = swap32_sum(xs, xs);
+#pragma unroll
+            for (int t = 0; t < RT; ++t) {
+                const int row = row0 + 16 * t + r16;
+                const size_t ri = ((size_t)wk.e * F + (row < F ? row : F - 1)) * (H / 16) + g * 4 + kq;
+                const uint2 wg = gq[ri], wu = uq[ri];  // words 2kq and 2kq+1 of the row's group
+                uint32_t ag[2][4], au[2][4];
+                q4_pairs(wg.x, ag[0]);
+                q4_pairs(wg.y, ag[1]);
+                q4_pairs(wu.x, au[0]);
+                q4_pairs(wu.y, au[1]);
+                f32x4_t dg = mfma16x16x32(ag[0], xb[0], f32x4_t{0.f, 0.f, 0.f, 0.f});
+                dg = mfma16x16x32(ag[1], xb[1], dg);
+                f32x4_t du = mfma16x16x32(au[0], xb[0], f32x4_t{0.f, 0.f, 0.f, 0.f});
+                du = mfma16x16x32(au[1], xb[1], du);
+                const float4 s1 = *(const float4 *)(sg + g * ROWS + 16 * t + 4 * kq);
+                const float4 b1 = *(const float4 *)(bg + g * ROWS + 16 * t + 4 * kq);
+                const float4 s2 = *(const float4 *)(su + g * ROWS + 16 * t + 4 * kq);
+                const float4 b2 = *(const float4 *)(bu + g * ROWS + 16 * t + 4 * kq);
+                accg[t][0] += fmaf(s1.x, dg[0], b1.x * xs);
+                accg[t][1] += fmaf(s1.y, dg[1], b1.y * xs);
+                accg[t][2] += fmaf(s1.z, dg[2], b1.z * xs);
+                accg[t][3] += fmaf(s1.w, dg[3], b1.w * xs);
+                accu[t][0] += fmaf(s2.x, du[0], b2.x * xs);
+                accu[t][1] += fmaf(s2.y, du[1], b2.y * xs);
+                accu[t][2] += fmaf(s2.z, du[2], b2.z * xs);
+                accu[t][3] += fmaf(s2.w, du[3], b2.w * xs);
+            }
+        }
+        float *mine = part + ((size_t)wave * kWave + lane) * (8 * RT);
+#pragma unroll
+        for (int t = 0; t < RT; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                mine[t * 8 + i] = accg[t][i];
+                mine[t * 8 + 4 + i] = accu[t][i];
+            }
+        __syncthreads();
+        if (wave == 0 && live) {  // add the four partials in wave order and finish the rows
+#pragma unroll
+            for (int t = 0; t < RT; ++t)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    float g = 0.f, u = 0.f;
+#pragma unroll
+                    for (int w = 0; w < 4; ++w) {
+                        const float *pw = part + ((size_t)w * kWave + lane) * (8 * RT);
+                        g += pw[t * 8 + i];
+                        u += pw[t * 8 + 4 + i];
+                    }
+                    const int row = row0 + 16 * t + 4 * kq + i;
+                    if (row < F) a.h[(size_t)slot * F + row] = silu_mul(g, u, sc, lim);
+                }
+        }
+        __syncthreads();
     }
 }
 
@@ -692,20 +852,42 @@ static int groups_y_of(const moe_layer_t *layer, int n_tokens) {
     return n_slots < layer->n_experts ? n_slots : layer->n_experts;
 }
 
+// Experts with at least this many slots take the MFMA kernel (when the batch
+// can have such experts at all and the layer suits it).
+constexpr int kMfmaMinCount = 3;
+constexpr int kMfmaRowTiles = 2;
+
+static bool mfma_gate_up_ok(const moe_layer_t *layer) {
+    return layer->act_dtype == MOE_DTYPE_BF16 && layer->hidden % 256 == 0 && layer->hidden <= 4096;
+}
+
+static size_t mfma_gate_up_lds(const moe_layer_t *layer) {
+    const int G = layer->hidden / kGroup, ROWS = 16 * kMfmaRowTiles;
+    return ((size_t)4 * G * ROWS + (size_t)4 * kWave * 8 * kMfmaRowTiles) * sizeof(float);
+}
+
 static moe_status enqueue_gate_up(const moe_layer_t *layer, const void *x, int n_tokens,
                                   const moe_plan_t *plan, void *workspace, hipStream_t stream) {
     Geometry gu;
     pick_geometry_gate_up(layer->hidden, &gu);
     const Workspace ws = workspace_layout(layer, n_tokens);
     float *h = (float *)((char *)workspace + ws.h_off);
+    const bool use_mfma = mfma_gate_up_ok(layer) && n_tokens >= kMfmaMinCount;
     GateUpArgs ga{(const uint4 *)layer->gate_q, (const uint4 *)layer->up_q, layer->gate_s,
                   layer->gate_b, layer->up_s, layer->up_b, layer->expert_scale,
                   layer->clamp_limit, x, plan_view(plan), h, layer->hidden, layer->dff,
-                  layer->n_experts, layer->top_k, n_tokens * layer->top_k};
+                  layer->n_experts, layer->top_k, n_tokens * layer->top_k,
+                  use_mfma ? kMfmaMinCount - 1 : INT_MAX};
     const bool bf16 = layer->act_dtype == MOE_DTYPE_BF16;
+    const int groups_y = groups_y_of(layer, n_tokens);
     moe_status st;
-    MOE_GEOMETRY_SWITCH(gu, st, launch_gate_up, ga, bf16, groups_y_of(layer, n_tokens), stream)
-    return st;
+    MOE_GEOMETRY_SWITCH(gu, st, launch_gate_up, ga, bf16, groups_y, stream)
+    if (st != MOE_OK || !use_mfma) return st;
+    const int rows = 16 * kMfmaRowTiles;
+    const dim3 grid((layer->dff + rows - 1) / rows, groups_y);
+    hipLaunchKernelGGL(gate_up_mfma_kernel<kMfmaRowTiles>, grid, dim3(kBlock), mfma_gate_up_lds(layer), stream,
+                       ga, kMfmaMinCount);
+    return MOE_OK;
 }
 
 static moe_status enqueue_down_combine(const moe_layer_t *layer, int n_tokens, const int32_t *topk_idx,
