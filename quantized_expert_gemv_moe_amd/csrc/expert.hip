@@ -420,24 +420,50 @@ __device__ __forceinline__ void x8_pairs(uint4 w, uint32_t *o, float *acc) {
 
 constexpr int kMfmaTokens = 16;  // token tile
 
-template <int RT>
-__global__ __launch_bounds__(kBlock) void gate_up_mfma_kernel(GateUpArgs a, int min_count) {
+// Streaming 8-byte load (two words of one row).
+__device__ __forceinline__ uint2 load_stream2(const uint2 *p) {
+    typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+    const v2u v = __builtin_nontemporal_load((const v2u *)p);
+    return make_uint2(v.x, v.y);
+}
+
+// NW waves, GW 64-groups per wave (NW * GW = hidden / 64), RT 16-row tiles.
+// Every weight load of a wave is issued before its first MFMA, and every
+// activation load of a token tile before that tile's first MFMA.
+template <int NW, int GW, int RT>
+__global__ __launch_bounds__(NW * kWave) void gate_up_mfma_kernel(GateUpArgs a, int min_count) {
     constexpr int ROWS = 16 * RT;
+    constexpr int G = NW * GW;
     extern __shared__ float smem[];
     Work wk;
     if (!plan_expert(a.plan, blockIdx.y, a.n_experts, a.n_slots, &wk)) return;
     if (wk.count < min_count) return;  // the expert belongs to the VALU kernel
-    const int H = a.hidden, F = a.dff, G = H / kGroup;
+    const int H = a.hidden, F = a.dff;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int r16 = lane & 15, kq = lane >> 4;
     const int row0 = blockIdx.x * ROWS;
-    const int GW = G / 4, g0 = wave * GW;
+    const int g0 = wave * GW;
+
+    // this wave's weights: words 2kq and 2kq+1 of each group, per row tile
+    uint2 wgq[GW][RT], wuq[GW][RT];
+    {
+        const uint2 *gq = (const uint2 *)a.gate_q, *uq = (const uint2 *)a.up_q;
+#pragma unroll
+        for (int t = 0; t < RT; ++t) {
+            const int row = row0 + 16 * t + r16;
+            const size_t rb = ((size_t)wk.e * F + (row < F ? row : F - 1)) * (H / 16) + g0 * 4 + kq;
+#pragma unroll
+            for (int gi = 0; gi < GW; ++gi) {
+                wgq[gi][t] = load_stream2(gq + rb + gi * 4);
+                wuq[gi][t] = load_stream2(uq + rb + gi * 4);
+            }
+        }
+    }
     // scales [group][row] in fp32, biases already shifted by -128 * scale
     float *sg = smem, *bg = smem + G * ROWS, *su = smem + 2 * G * ROWS, *bu = smem + 3 * G * ROWS;
     float *part = smem + 4 * G * ROWS;  // [wave][lane][8 * RT]
-
-    for (int i = threadIdx.x; i < ROWS * G; i += kBlock) {
+    for (int i = threadIdx.x; i < ROWS * G; i += NW * kWave) {
         const int r = i / G, g = i - r * G;
         const int row = row0 + r < F ? row0 + r : F - 1;
         const size_t si = ((size_t)wk.e * F + row) * G + g;
@@ -450,41 +476,42 @@ __global__ __launch_bounds__(kBlock) void gate_up_mfma_kernel(GateUpArgs a, int 
     __syncthreads();
     const float sc = a.expert_scale ? a.expert_scale[wk.e] : 1.f;
     const float lim = a.clamp_limit;
-    const uint2 *gq = (const uint2 *)a.gate_q, *uq = (const uint2 *)a.up_q;
 
     for (int t0 = 0; t0 < wk.count; t0 += kMfmaTokens) {
         const int nt = wk.count - t0 < kMfmaTokens ? wk.count - t0 : kMfmaTokens;
         const bool live = r16 < nt;  // this lane's token column
         const int slot = live ? plan_slot(a.plan, wk, t0 + r16, a.n_slots) : 0;
         const uint16_t *xr = (const uint16_t *)a.x + (size_t)(slot / a.top_k) * H;
+        // elements 64g + 16kq .. + 15 of the token for each group: the B operands
+        uint4 xw[GW][2];
+#pragma unroll
+        for (int gi = 0; gi < GW; ++gi) {
+            const uint4 *xp = (const uint4 *)(xr + (g0 + gi) * kGroup + 16 * kq);
+            xw[gi][0] = live ? xp[0] : make_uint4(0, 0, 0, 0);
+            xw[gi][1] = live ? xp[1] : make_uint4(0, 0, 0, 0);
+        }
         f32x4_t accg[RT], accu[RT];
 #pragma unroll
         for (int t = 0; t < RT; ++t) {
             accg[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
             accu[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         }
+#pragma unroll
         for (int gi = 0; gi < GW; ++gi) {
             const int g = g0 + gi;
-            // elements 64g + 16kq .. + 15 of the token: the two MFMA steps' B operands
             uint32_t xb[2][4];
             float xs = 0.f;
-            const uint4 *xp = (const uint4 *)(xr + g * kGroup + 16 * kq);
-            const uint4 w0 = live ? xp[0] : make_uint4(0, 0, 0, 0);
-            const uint4 w1 = live ? xp[1] : make_uint4(0, 0, 0, 0);
-            x8_pairs(w0, xb[0], &xs);
-            x8_pairs(w1, xb[1], &xs);
+            x8_pairs(xw[gi][0], xb[0], &xs);
+            x8_pairs(xw[gi][1], xb[1], &xs);
             xs = swap16_sum(xs, xs);  // add the four lanes of the token
             xs = swap32_sum(xs, xs);
 #pragma unroll
             for (int t = 0; t < RT; ++t) {
-                const int row = row0 + 16 * t + r16;
-                const size_t ri = ((size_t)wk.e * F + (row < F ? row : F - 1)) * (H / 16) + g * 4 + kq;
-                const uint2 wg = gq[ri], wu = uq[ri];  // words 2kq and 2kq+1 of the row's group
                 uint32_t ag[2][4], au[2][4];
-                q4_pairs(wg.x, ag[0]);
-                q4_pairs(wg.y, ag[1]);
-                q4_pairs(wu.x, au[0]);
-                q4_pairs(wu.y, au[1]);
+                q4_pairs(wgq[gi][t].x, ag[0]);
+                q4_pairs(wgq[gi][t].y, ag[1]);
+                q4_pairs(wuq[gi][t].x, au[0]);
+                q4_pairs(wuq[gi][t].y, au[1]);
                 f32x4_t dg = mfma16x16x32(ag[0], xb[0], f32x4_t{0.f, 0.f, 0.f, 0.f});
                 dg = mfma16x16x32(ag[1], xb[1], dg);
                 f32x4_t du = mfma16x16x32(au[0], xb[0], f32x4_t{0.f, 0.f, 0.f, 0.f});
@@ -512,14 +539,14 @@ __global__ __launch_bounds__(kBlock) void gate_up_mfma_kernel(GateUpArgs a, int 
                 mine[t * 8 + 4 + i] = accu[t][i];
             }
         __syncthreads();
-        if (wave == 0 && live) {  // add the four partials in wave order and finish the rows
+        if (wave == 0 && live) {  // add the partials in wave order and finish the rows
 #pragma unroll
             for (int t = 0; t < RT; ++t)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     float g = 0.f, u = 0.f;
 #pragma unroll
-                    for (int w = 0; w < 4; ++w) {
+                    for (int w = 0; w < NW; ++w) {
                         const float *pw = part + ((size_t)w * kWave + lane) * (8 * RT);
                         g += pw[t * 8 + i];
                         u += pw[t * 8 + 4 + i];
@@ -855,15 +882,24 @@ static int groups_y_of(const moe_layer_t *layer, int n_tokens) {
 // Experts with at least this many slots take the MFMA kernel (when the batch
 // can have such experts at all and the layer suits it).
 constexpr int kMfmaMinCount = 3;
-constexpr int kMfmaRowTiles = 2;
+// 16-row tiles per workgroup: two, or one where a wave's registers would not
+// hold two (more than eight waves, i.e. hidden above 2048).
+static int mfma_row_tiles(int nw) { return nw > 8 ? 1 : 2; }
 
-static bool mfma_gate_up_ok(const moe_layer_t *layer) {
-    return layer->act_dtype == MOE_DTYPE_BF16 && layer->hidden % 256 == 0 && layer->hidden <= 4096;
+// Waves (NW) and 64-groups per wave (GW) of the MFMA gate+up kernel for a
+// hidden size; false when it has no instance.
+static bool mfma_gate_up_shape(const moe_layer_t *layer, int *nw, int *gw) {
+    if (layer->act_dtype != MOE_DTYPE_BF16 || layer->hidden % kGroup) return false;
+    const int G = layer->hidden / kGroup;
+    if (G % 4 || G / 4 > 16) return false;
+    *gw = 4;
+    *nw = G / 4;
+    return true;
 }
 
-static size_t mfma_gate_up_lds(const moe_layer_t *layer) {
-    const int G = layer->hidden / kGroup, ROWS = 16 * kMfmaRowTiles;
-    return ((size_t)4 * G * ROWS + (size_t)4 * kWave * 8 * kMfmaRowTiles) * sizeof(float);
+static size_t mfma_gate_up_lds(const moe_layer_t *layer, int nw) {
+    const int G = layer->hidden / kGroup, rt = mfma_row_tiles(nw), ROWS = 16 * rt;
+    return ((size_t)4 * G * ROWS + (size_t)nw * kWave * 8 * rt) * sizeof(float);
 }
 
 static moe_status enqueue_gate_up(const moe_layer_t *layer, const void *x, int n_tokens,
@@ -872,7 +908,8 @@ static moe_status enqueue_gate_up(const moe_layer_t *layer, const void *x, int n
     pick_geometry_gate_up(layer->hidden, &gu);
     const Workspace ws = workspace_layout(layer, n_tokens);
     float *h = (float *)((char *)workspace + ws.h_off);
-    const bool use_mfma = mfma_gate_up_ok(layer) && n_tokens >= kMfmaMinCount;
+    int nw = 0, gw = 0;
+    const bool use_mfma = n_tokens >= kMfmaMinCount && mfma_gate_up_shape(layer, &nw, &gw);
     GateUpArgs ga{(const uint4 *)layer->gate_q, (const uint4 *)layer->up_q, layer->gate_s,
                   layer->gate_b, layer->up_s, layer->up_b, layer->expert_scale,
                   layer->clamp_limit, x, plan_view(plan), h, layer->hidden, layer->dff,
@@ -883,10 +920,19 @@ static moe_status enqueue_gate_up(const moe_layer_t *layer, const void *x, int n
     moe_status st;
     MOE_GEOMETRY_SWITCH(gu, st, launch_gate_up, ga, bf16, groups_y, stream)
     if (st != MOE_OK || !use_mfma) return st;
-    const int rows = 16 * kMfmaRowTiles;
+    const int rows = 16 * mfma_row_tiles(nw);
     const dim3 grid((layer->dff + rows - 1) / rows, groups_y);
-    hipLaunchKernelGGL(gate_up_mfma_kernel<kMfmaRowTiles>, grid, dim3(kBlock), mfma_gate_up_lds(layer), stream,
-                       ga, kMfmaMinCount);
+    const size_t lds = mfma_gate_up_lds(layer, nw);
+    switch (nw * 100 + gw) {
+#define MOE_GUM(NW, GW)                                                                                  \
+    case NW * 100 + GW:                                                                                  \
+        hipLaunchKernelGGL((gate_up_mfma_kernel<NW, GW, NW <= 8 ? 2 : 1>), grid, dim3(NW * kWave), lds, stream, \
+                           ga, kMfmaMinCount);                                                           \
+        break;
+        MOE_GUM(1, 4) MOE_GUM(2, 4) MOE_GUM(4, 4) MOE_GUM(6, 4) MOE_GUM(8, 4) MOE_GUM(12, 4) MOE_GUM(16, 4)
+#undef MOE_GUM
+        default: return MOE_ERR_UNSUPPORTED;
+    }
     return MOE_OK;
 }
 

