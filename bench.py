@@ -1,9 +1,11 @@
 #!/usr/bin/env python3
 """Decode-step benchmark of the quantized-expert MoE block on one MI355X.
 
-A step is one pass of the whole hot path over one batch: moe_route_plan
-(router and cohort planner in one launch) -> moe_expert_gate_up ->
-moe_expert_down_combine.  The
+A step is one pass of the whole hot path over one batch, moe_decode_layer:
+router, cohort planner, fused gate+up, down projection and combine.  For
+one token that is two launches (a gate+up kernel that routes for itself,
+then down + combine); for a batch, moe_route_plan (router and planner in
+one launch), the gate+up kernels and the down and combine kernels.  The
 default workload is the single-token decode layer (hidden 2048, dff 768, 128
 experts, top-8, B = 1, affine int4 g64 weights, bf16 activations).  Steps
 rotate over R layer instances resident in HBM (48 by default, 16.3 GB of
@@ -15,8 +17,9 @@ device.
 Timed passes (HIP graphs of one rotation, replayed; HIP events on the
 capturing stream):
   1. headline: K whole steps  -> steps/s, unique-expert GB/s
-  2. kernels : R launches of each stage alone on precomputed plans -> the
-     average duration of the dominant kernel for the roofline entry
+  2. kernels : R launches of each half of the step alone (moe_route_gate_up,
+     moe_expert_down_combine) -> the average duration of the dominant
+     kernel (gate+up: two thirds of the bytes) for the roofline entry
   3. ladder  : B = 4 / 8 (30 % sharing) and B = 32 (Zipf 1.1) on the same
      layers -> sublinearity of the step time in B
 The oracle (plain fp64 C, OpenMP) is timed on a bounded sample of the same
@@ -117,11 +120,9 @@ class Rotation:
         self.moe = moe
 
     def step(self, i):
-        m = self.moe
-        L = self.layers[i]
-        m.route_plan(self.logits[i], self.shape.top_k, self.plans[i], self.idx[i], self.w[i])
-        m.expert_gate_up(L, self.x[i], self.plans[i], self.ws)
-        m.expert_down_combine(L, self.B, self.idx[i], self.w[i], self.plans[i], self.out[i], self.ws)
+        """One layer step from the router logits (moe_decode_layer)."""
+        self.moe.decode_layer(self.layers[i], self.x[i], self.logits[i], self.plans[i], self.ws, self.out[i],
+                              bufs={"idx": self.idx[i], "w": self.w[i]})
 
     def n_unique(self):
         return [int(p.n_unique.item()) for p in self.plans]
@@ -188,9 +189,9 @@ def run_kernel_pass(rot, reps=4):
     m = rot.moe
     R = rot.R
     stages = {
-        "route_plan": lambda: [m.route_plan(rot.logits[i], rot.shape.top_k, rot.plans[i], rot.idx[i], rot.w[i])
-                               for i in range(R)],
-        "gate_up": lambda: [m.expert_gate_up(rot.layers[i], rot.x[i], rot.plans[i], rot.ws) for i in range(R)],
+        # router + planner + gate/up: one launch for a single token
+        "route_gate_up": lambda: [m.route_gate_up(rot.layers[i], rot.x[i], rot.logits[i], rot.idx[i], rot.w[i],
+                                                  rot.plans[i], rot.ws) for i in range(R)],
         "down_combine": lambda: [m.expert_down_combine(rot.layers[i], rot.B, rot.idx[i], rot.w[i], rot.plans[i],
                                                        rot.out[i], rot.ws) for i in range(R)],
     }
@@ -318,10 +319,11 @@ def main():
     gu_bytes = gate_up_bytes(sh, avg_unique)
     dn_bytes = avg_unique * sh.hidden * sh.dff * BYTES_PER_WEIGHT
     kernels = {k: {"us": v * 1e6} for k, v in kt.items()}
-    kernels["gate_up"]["gbps"] = gu_bytes / kt["gate_up"] / 1e9
+    kernels["route_gate_up"]["gbps"] = gu_bytes / kt["route_gate_up"] / 1e9
     kernels["down_combine"]["gbps"] = dn_bytes / kt["down_combine"] / 1e9
     log(f"[bench] kernels: " + ", ".join(f"{k} {v['us']:.2f} us" for k, v in kernels.items()))
-    ach = gu_bytes / kt["gate_up"] / 1e9
+    ach = gu_bytes / kt["route_gate_up"] / 1e9
+    gu_kernel = "gate_up_route_kernel" if B == 1 else "route_plan_kernel + gate_up kernels"
 
     ladder = []
     if not args.no_ladder and sh.name in ("decode", "cohort", "stack"):
@@ -365,9 +367,9 @@ def main():
         "unique_gbps": gbps,
         "hbm_frac": gbps / HBM_PEAK_GBPS,
         "unique_experts_per_step": avg_unique,
-        "roofline": {"bound": "hbm", "kernel": "gate_up_kernel", "achieved": ach, "peak": HBM_PEAK_GBPS,
+        "roofline": {"bound": "hbm", "kernel": gu_kernel, "achieved": ach, "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": ach / HBM_PEAK_GBPS, "traffic": None,
-                     "bytes_per_launch": gu_bytes, "us_per_launch": kt["gate_up"] * 1e6},
+                     "bytes_per_launch": gu_bytes, "us_per_launch": kt["route_gate_up"] * 1e6},
         "kernels": kernels,
         "ladder": ladder,
         "cpu_baseline": cpu,

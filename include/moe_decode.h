@@ -196,6 +196,37 @@ moe_status moe_decode_step(const moe_layer_t *layer, const void *x, int32_t n_to
                            void *workspace, size_t workspace_bytes, void *hip_stream);
 
 /*
+ * One layer step from router logits: moe_route_plan, then moe_decode_step,
+ * with the same checks and results; topk_idx, topk_w and the plan are
+ * outputs here (the plan as moe_route_plan writes it).
+ *   logits  fp32 [n_tokens][n_experts], device
+ * The pages split a decoded token's MoE time into router, expert GEMV and
+ * combine (page "perf(moe): attribute the MoE decode gap at the M = 1
+ * expert gather", Proposed Solution); at one token each of those is a
+ * short, latency-bound kernel.  So a batch of one token takes two launches
+ * instead of three: every gate+up workgroup selects its own expert from the
+ * logits (one of them also writes topk_idx, topk_w and the plan), and one
+ * kernel does the down projection and the combine.  Results are bitwise
+ * those of the longer path.
+ */
+moe_status moe_decode_layer(const moe_layer_t *layer, const float *logits, const void *x,
+                            int32_t n_tokens, int32_t *topk_idx, float *topk_w,
+                            const moe_plan_t *plan, const void *residual, void *out,
+                            void *workspace, size_t workspace_bytes, void *hip_stream);
+
+/*
+ * The first half of moe_decode_layer: routes, plans and writes h into the
+ * workspace (one launch for a single token, else moe_route_plan and the
+ * gate+up kernels); moe_expert_down_combine with the same workspace, plan,
+ * topk_idx and topk_w is the second half.  Same checks as moe_decode_layer
+ * (out and residual aside).
+ */
+moe_status moe_route_gate_up(const moe_layer_t *layer, const float *logits, const void *x,
+                             int32_t n_tokens, int32_t *topk_idx, float *topk_w,
+                             const moe_plan_t *plan, void *workspace, size_t workspace_bytes,
+                             void *hip_stream);
+
+/*
  * The two halves of moe_decode_step, for callers that instrument or overlap
  * the stages (the pages' fused decode kernel is likewise a gate/up kernel
  * followed by a down kernel: page "perf(moe): batched decode scales 1.55x

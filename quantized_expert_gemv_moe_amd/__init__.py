@@ -26,6 +26,7 @@ from ._lib import (  # noqa: F401
     decode_step,
     expert_down_combine,
     expert_gate_up,
+    route_gate_up,
     expert_plan,
     lib,
     library_path,

@@ -50,8 +50,8 @@ class PlanStruct(C.Structure):
 _lib = None
 
 EXPORTS = ("moe_route_topk", "moe_expert_plan", "moe_route_plan", "moe_workspace_size", "moe_decode_step",
-           "moe_expert_gate_up", "moe_expert_down_combine", "moe_pack_down", "moe_layer_check",
-           "moe_status_str", "moe_abi_version")
+           "moe_decode_layer", "moe_route_gate_up", "moe_expert_gate_up", "moe_expert_down_combine", "moe_pack_down",
+           "moe_layer_check", "moe_status_str", "moe_abi_version")
 
 
 def library_path() -> str:
@@ -80,6 +80,12 @@ def lib() -> C.CDLL:
         L.moe_decode_step.argtypes = [C.POINTER(LayerStruct), vp, i32, vp, vp, C.POINTER(PlanStruct),
                                       vp, vp, vp, C.c_size_t, vp]
         L.moe_decode_step.restype = C.c_int
+        L.moe_decode_layer.argtypes = [C.POINTER(LayerStruct), vp, vp, i32, vp, vp, C.POINTER(PlanStruct),
+                                       vp, vp, vp, C.c_size_t, vp]
+        L.moe_decode_layer.restype = C.c_int
+        L.moe_route_gate_up.argtypes = [C.POINTER(LayerStruct), vp, vp, i32, vp, vp, C.POINTER(PlanStruct),
+                                        vp, C.c_size_t, vp]
+        L.moe_route_gate_up.restype = C.c_int
         L.moe_expert_gate_up.argtypes = [C.POINTER(LayerStruct), vp, i32, C.POINTER(PlanStruct), vp,
                                          C.c_size_t, vp]
         L.moe_expert_gate_up.restype = C.c_int
@@ -289,6 +295,15 @@ def decode_step(layer: DeviceLayer, x: torch.Tensor, idx: torch.Tensor, w: torch
     return out
 
 
+def route_gate_up(layer: DeviceLayer, x: torch.Tensor, logits: torch.Tensor, idx: torch.Tensor, w: torch.Tensor,
+                  plan: Plan, workspace: torch.Tensor, stream=None):
+    """moe_route_gate_up: first half of decode_layer (routing, plan, h into the workspace)."""
+    _check(lib().moe_route_gate_up(C.byref(layer.struct), _ptr(logits), _ptr(x), x.shape[0], _ptr(idx), _ptr(w),
+                                   C.byref(plan.struct), _ptr(workspace), workspace.numel(), _stream(stream)),
+           "moe_route_gate_up")
+    return idx, w, plan
+
+
 def expert_gate_up(layer: DeviceLayer, x: torch.Tensor, plan: Plan, workspace: torch.Tensor, stream=None):
     """moe_expert_gate_up: first half of decode_step (h into the workspace)."""
     _check(lib().moe_expert_gate_up(C.byref(layer.struct), _ptr(x), x.shape[0], C.byref(plan.struct),
@@ -308,8 +323,33 @@ def expert_down_combine(layer: DeviceLayer, n_tokens: int, idx: torch.Tensor, w:
 def decode_layer(layer: DeviceLayer, x: torch.Tensor, logits: torch.Tensor, plan: Optional[Plan] = None,
                  workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
                  residual: Optional[torch.Tensor] = None, bufs: Optional[dict] = None, stream=None):
-    """One layer step: router and planner (moe_route_plan), then the expert block."""
+    """moe_decode_layer: one layer step from router logits (router, planner,
+    expert block); returns (out, idx, w, plan)."""
+    want = torch.bfloat16 if layer.act_dtype == MOE_DTYPE_BF16 else torch.float32
+    if x.dtype != want or x.dim() != 2 or not x.is_contiguous():
+        raise ValueError(f"x must be a contiguous {want} [B, H] tensor")
+    if logits.dtype != torch.float32 or logits.dim() != 2 or not logits.is_contiguous():
+        raise ValueError("logits must be a contiguous fp32 [B, E] tensor")
+    B, E = logits.shape
+    if x.shape[0] != B or E != layer.n_experts:
+        raise ValueError("x, logits and the layer disagree on the batch or the expert count")
     bufs = bufs or {}
-    idx, w, plan = route_plan(logits, layer.top_k, plan, bufs.get("idx"), bufs.get("w"), stream=stream)
-    out = decode_step(layer, x, idx, w, plan, out=out, workspace=workspace, residual=residual, stream=stream)
+    k = layer.top_k
+    idx = bufs.get("idx")
+    w = bufs.get("w")
+    if idx is None:
+        idx = torch.empty((B, k), dtype=torch.int32, device=logits.device)
+    if w is None:
+        w = torch.empty((B, k), dtype=torch.float32, device=logits.device)
+    if plan is None:
+        plan = Plan.allocate(E, B * k, device=logits.device)
+    if plan.sorted_slots.numel() < B * k or plan.counts.numel() < E:
+        raise ValueError("plan buffers are too small")
+    if out is None:
+        out = torch.empty_like(x)
+    if workspace is None:
+        workspace = alloc_workspace(layer, B, device=x.device)
+    _check(lib().moe_decode_layer(C.byref(layer.struct), _ptr(logits), _ptr(x), B, _ptr(idx), _ptr(w),
+                                  C.byref(plan.struct), _ptr(residual), _ptr(out), _ptr(workspace),
+                                  workspace.numel(), _stream(stream)), "moe_decode_layer")
     return out, idx, w, plan

@@ -31,6 +31,7 @@
 
 #include "device_util.h"
 #include "moe_internal.h"
+#include "route_device.h"
 
 namespace moe {
 
@@ -247,6 +248,122 @@ __device__ __forceinline__ float silu_mul(float g, float u, float sc, float lim)
     return g / (1.f + expf(-g)) * u;
 }
 
+// A lane's share of RI rows of one expert: its NV 16-byte chunks of each
+// gate and up row with their scales and biases (as fp32; with bf16
+// activations the bias also carries the -128 * scale of the nibble trick).
+template <int RI, int NV>
+struct GateUpRows {
+    uint4 wg[RI][NV], wu[RI][NV];
+    float sg[RI][NV], bg[RI][NV], su[RI][NV], bu[RI][NV];
+};
+
+template <int LPR, int NV, int RI, bool XBF16>
+__device__ __forceinline__ void load_gate_up_rows(const GateUpArgs &a, int e, int row0, int sl,
+                                                  GateUpRows<RI, NV> &w) {
+    constexpr int RPI = kWave / LPR;
+    const int H = a.hidden, F = a.dff;
+    const int qrow = H / 32, grow = H / kGroup;
+#pragma unroll
+    for (int r = 0; r < RI; ++r) {
+        const int row = row0 + r * RPI;
+        const int rr = row < F ? row : F - 1;
+        const size_t rq = ((size_t)e * F + rr) * qrow;
+        const size_t rs = ((size_t)e * F + rr) * grow;
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+            const int ch = v * LPR + sl;
+            w.wg[r][v] = load_stream(a.gate_q + rq + ch);
+            w.wu[r][v] = load_stream(a.up_q + rq + ch);
+            w.sg[r][v] = f16_bits_to_f32(a.gate_s[rs + ch / 2]);
+            w.bg[r][v] = f16_bits_to_f32(a.gate_b[rs + ch / 2]);
+            w.su[r][v] = f16_bits_to_f32(a.up_s[rs + ch / 2]);
+            w.bu[r][v] = f16_bits_to_f32(a.up_b[rs + ch / 2]);
+            if constexpr (XBF16) {  // fold the +128 of the bf16 nibble trick into the bias
+                w.bg[r][v] = fmaf(-128.f, w.sg[r][v], w.bg[r][v]);
+                w.bu[r][v] = fmaf(-128.f, w.su[r][v], w.bu[r][v]);
+            }
+        }
+    }
+}
+
+// One token's activations for this lane's chunks: bf16 pairs (or fp32
+// values) and the sum of each chunk's 32 activations.
+template <int LPR, int NV, bool XBF16>
+struct GateUpX {
+    uint32_t xp[XBF16 ? NV : 1][XBF16 ? 16 : 1];
+    float xf[XBF16 ? 1 : NV][XBF16 ? 1 : 32];
+    float xs[NV];
+};
+
+template <int LPR, int NV, bool XBF16>
+__device__ __forceinline__ void load_gate_up_x(const GateUpArgs &a, int token, int sl, GateUpX<LPR, NV, XBF16> &x,
+                                               const uint4 (*pre)[4] = nullptr) {
+    const size_t xr = (size_t)token * a.hidden;
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+        const int c0 = (v * LPR + sl) * 32;
+        if constexpr (XBF16) {
+            uint4 raw[4];
+            if (pre) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) raw[q] = pre[v][q];
+            } else {
+                load_x32_bf16((const uint16_t *)a.x, xr, c0, raw);
+            }
+            x.xs[v] = x32_pairs(raw, x.xp[v]);
+        } else {
+            x.xs[v] = load_x32_f32((const float *)a.x, xr, c0, x.xf[v]);
+        }
+    }
+}
+
+// h = silu(g) * u of one token for the segment's RI rows, into slot `slot`.
+template <int LPR, int NV, int RI, bool XBF16>
+__device__ __forceinline__ void gate_up_token_rows(const GateUpArgs &a, const GateUpRows<RI, NV> &w,
+                                                   const GateUpX<LPR, NV, XBF16> &x, int slot, int row0,
+                                                   float sc, float lim) {
+    constexpr int RPI = kWave / LPR;
+    constexpr bool WAVE8 = (LPR == kWave && RI == 4);
+    const int lane = threadIdx.x & (kWave - 1);
+    const int sl = lane % LPR;
+    const int F = a.dff;
+    float part[2 * RI];
+#pragma unroll
+    for (int r = 0; r < RI; ++r) {
+        float g = 0.f, u = 0.f;
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+            float dg, du;
+            if constexpr (XBF16) {
+                dg = dot32_q4_bf16(w.wg[r][v], x.xp[v]);
+                du = dot32_q4_bf16(w.wu[r][v], x.xp[v]);
+            } else {
+                dg = dot32_q4(w.wg[r][v], x.xf[v]);
+                du = dot32_q4(w.wu[r][v], x.xf[v]);
+            }
+            g += fmaf(w.sg[r][v], dg, w.bg[r][v] * x.xs[v]);
+            u += fmaf(w.su[r][v], du, w.bu[r][v] * x.xs[v]);
+        }
+        part[2 * r] = g;
+        part[2 * r + 1] = u;
+    }
+    if constexpr (WAVE8) {
+        const float tot = wave_sum8(part);
+        const float other = dpp<kDppMirror>(tot);  // lane 16r reads lane 16r+15 (the u)
+        const int r = lane >> 4;
+        const int row = row0 + r * RPI;
+        if ((lane & 15) == 0 && row < F) a.h[(size_t)slot * F + row] = silu_mul(tot, other, sc, lim);
+    } else {
+#pragma unroll
+        for (int r = 0; r < RI; ++r) {
+            const float g = seg_sum<LPR>(part[2 * r]);
+            const float u = seg_sum<LPR>(part[2 * r + 1]);
+            const int row = row0 + r * RPI;
+            if (sl == 0 && row < F) a.h[(size_t)slot * F + row] = silu_mul(g, u, sc, lim);
+        }
+    }
+}
+
 // One wave per workgroup.  LPR lanes per row, NV chunks per lane, RI rows
 // per segment; TCH tokens' activations in registers at a time.
 template <int LPR, int NV, int RI, bool XBF16>
@@ -254,7 +371,6 @@ __global__ __launch_bounds__(kWave) void gate_up_kernel(GateUpArgs a) {
     constexpr int RPI = kWave / LPR;  // rows per wave-wide pass
     constexpr int ROWS_WG = RPI * RI;
     constexpr int TCH = (XBF16 && NV == 1) ? 2 : 1;
-    constexpr bool WAVE8 = (LPR == kWave && RI == 4);
     const int lane = threadIdx.x;
     const int sl = lane % LPR;
     // With one token in the batch its activations are known before the plan
@@ -272,107 +388,75 @@ __global__ __launch_bounds__(kWave) void gate_up_kernel(GateUpArgs a) {
     if (!plan_expert(a.plan, blockIdx.y, a.n_experts, a.n_slots, &wk)) return;
     if (wk.count > a.max_count) return;  // the MFMA kernel's expert
     const int e = wk.e, count = wk.count;
-
     const int row0 = blockIdx.x * ROWS_WG + lane / LPR;
-    const int H = a.hidden, F = a.dff;
-    const int qrow = H / 32, grow = H / kGroup;
 
-    uint4 wg[RI][NV], wu[RI][NV];
-    float sg[RI][NV], bg[RI][NV], su[RI][NV], bu[RI][NV];
-#pragma unroll
-    for (int r = 0; r < RI; ++r) {
-        const int row = row0 + r * RPI;
-        const int rr = row < F ? row : F - 1;
-        const size_t rq = ((size_t)e * F + rr) * qrow;
-        const size_t rs = ((size_t)e * F + rr) * grow;
-#pragma unroll
-        for (int v = 0; v < NV; ++v) {
-            const int ch = v * LPR + sl;
-            wg[r][v] = load_stream(a.gate_q + rq + ch);
-            wu[r][v] = load_stream(a.up_q + rq + ch);
-            sg[r][v] = f16_bits_to_f32(a.gate_s[rs + ch / 2]);
-            bg[r][v] = f16_bits_to_f32(a.gate_b[rs + ch / 2]);
-            su[r][v] = f16_bits_to_f32(a.up_s[rs + ch / 2]);
-            bu[r][v] = f16_bits_to_f32(a.up_b[rs + ch / 2]);
-            if constexpr (XBF16) {  // fold the +128 of the bf16 nibble trick into the bias
-                bg[r][v] = fmaf(-128.f, sg[r][v], bg[r][v]);
-                bu[r][v] = fmaf(-128.f, su[r][v], bu[r][v]);
-            }
-        }
-    }
+    GateUpRows<RI, NV> w;
+    load_gate_up_rows<LPR, NV, RI, XBF16>(a, e, row0, sl, w);
     const float sc = a.expert_scale ? a.expert_scale[e] : 1.f;
     const float lim = a.clamp_limit;
 
     for (int t0 = 0; t0 < count; t0 += TCH) {
         int slot[TCH];
-        float xs[TCH][NV];
-        uint32_t xp[XBF16 ? TCH : 1][XBF16 ? NV : 1][16];
-        float xf[XBF16 ? 1 : TCH][XBF16 ? 1 : NV][32];
+        GateUpX<LPR, NV, XBF16> x[TCH];
 #pragma unroll
         for (int i = 0; i < TCH; ++i) {
             slot[i] = -1;
             if (i > 0 && t0 + i >= count) break;  // uniform: the chunk's tail is empty
             slot[i] = plan_slot(a.plan, wk, t0 + i, a.n_slots);
-            const size_t xr = (size_t)(slot[i] / a.top_k) * H;
-#pragma unroll
-            for (int v = 0; v < NV; ++v) {
-                const int c0 = (v * LPR + sl) * 32;
-                if constexpr (XBF16) {
-                    uint4 raw[4];
-                    if (one_token) {
-#pragma unroll
-                        for (int q = 0; q < 4; ++q) raw[q] = xraw0[v][q];
-                    } else {
-                        load_x32_bf16((const uint16_t *)a.x, xr, c0, raw);
-                    }
-                    xs[i][v] = x32_pairs(raw, xp[i][v]);
-                } else {
-                    xs[i][v] = load_x32_f32((const float *)a.x, xr, c0, xf[i][v]);
-                }
-            }
+            load_gate_up_x<LPR, NV, XBF16>(a, slot[i] / a.top_k, sl, x[i], one_token ? xraw0 : nullptr);
         }
 #pragma unroll
         for (int i = 0; i < TCH; ++i) {
             if (i > 0 && t0 + i >= count) break;
-            float part[2 * RI];
-#pragma unroll
-            for (int r = 0; r < RI; ++r) {
-                float g = 0.f, u = 0.f;
-#pragma unroll
-                for (int v = 0; v < NV; ++v) {
-                    float dg, du;
-                    if constexpr (XBF16) {
-                        dg = dot32_q4_bf16(wg[r][v], xp[i][v]);
-                        du = dot32_q4_bf16(wu[r][v], xp[i][v]);
-                    } else {
-                        dg = dot32_q4(wg[r][v], xf[i][v]);
-                        du = dot32_q4(wu[r][v], xf[i][v]);
-                    }
-                    g += fmaf(sg[r][v], dg, bg[r][v] * xs[i][v]);
-                    u += fmaf(su[r][v], du, bu[r][v] * xs[i][v]);
-                }
-                part[2 * r] = g;
-                part[2 * r + 1] = u;
-            }
-            if constexpr (WAVE8) {
-                const float tot = wave_sum8(part);
-                const float other = dpp<kDppMirror>(tot);  // lane 16r reads lane 16r+15 (the u)
-                const int r = lane >> 4;
-                const int row = row0 + r * RPI;
-                if ((lane & 15) == 0 && row < F)
-                    a.h[(size_t)slot[i] * F + row] = silu_mul(tot, other, sc, lim);
-            } else {
-#pragma unroll
-                for (int r = 0; r < RI; ++r) {
-                    const float g = seg_sum<LPR>(part[2 * r]);
-                    const float u = seg_sum<LPR>(part[2 * r + 1]);
-                    const int row = row0 + r * RPI;
-                    if (sl == 0 && row < F)
-                        a.h[(size_t)slot[i] * F + row] = silu_mul(g, u, sc, lim);
-                }
-            }
+            gate_up_token_rows<LPR, NV, RI, XBF16>(a, w, x[i], slot[i], row0, sc, lim);
         }
     }
+}
+
+// A batch of one token, routed here: workgroup (row block, j) finds the
+// token's expert of rank j itself from the logits (j + 1 selection rounds)
+// instead of waiting for a router launch and a plan.  Workgroup (0, 0)
+// routes in full and writes topk_idx, topk_w and the plan, exactly as
+// moe_route_plan would.  The arithmetic per row is gate_up_kernel's, so h
+// is bitwise the same as on the batched path.
+template <int LPR, int NV, int RI, bool XBF16, int PL>
+__global__ __launch_bounds__(kWave) void gate_up_route_kernel(GateUpArgs a, const float *__restrict__ logits,
+                                                              int *__restrict__ topk_idx,
+                                                              float *__restrict__ topk_w, PlanOut p) {
+    constexpr int RPI = kWave / LPR;
+    constexpr int ROWS_WG = RPI * RI;
+    const int lane = threadIdx.x;
+    const int sl = lane % LPR;
+    const int j = blockIdx.y;
+    uint4 xraw0[XBF16 ? NV : 1][4];
+    if constexpr (XBF16) {
+#pragma unroll
+        for (int v = 0; v < NV; ++v) load_x32_bf16((const uint16_t *)a.x, 0, (v * LPR + sl) * 32, xraw0[v]);
+    }
+    int e;
+    if (blockIdx.x == 0 && j == 0) {
+        __shared__ int idx_lds[kWave];
+        __shared__ int cnt[MOE_MAX_EXPERTS], off[MOE_MAX_EXPERTS], uix[MOE_MAX_EXPERTS];
+        int id;
+        float wt;
+        if (route_token<PL>(logits, a.n_experts, a.top_k, &id, &wt)) {
+            topk_idx[lane] = id;
+            topk_w[lane] = wt;
+            idx_lds[lane] = id;
+        }
+        e = __builtin_amdgcn_readfirstlane(id);
+        __builtin_amdgcn_wave_barrier();
+        plan_wave_small<PL>(idx_lds, a.top_k, a.n_experts, p, cnt, off, uix);
+    } else {
+        e = route_rank<PL>(logits, a.n_experts, j);
+    }
+    const int row0 = blockIdx.x * ROWS_WG + lane / LPR;
+    GateUpRows<RI, NV> w;
+    load_gate_up_rows<LPR, NV, RI, XBF16>(a, e, row0, sl, w);
+    const float sc = a.expert_scale ? a.expert_scale[e] : 1.f;
+    GateUpX<LPR, NV, XBF16> x;
+    load_gate_up_x<LPR, NV, XBF16>(a, 0, sl, x, XBF16 ? xraw0 : nullptr);
+    gate_up_token_rows<LPR, NV, RI, XBF16>(a, w, x, j, row0, sc, a.clamp_limit);
 }
 
 // ----------------------------------------------------- gate+up, MFMA tiles
@@ -746,6 +830,25 @@ __global__ __launch_bounds__(NW * kWave) void down_cols_kernel(const uint4 *__re
 
 // ---------------------------------------------------------------- combine
 
+// The output element from the fp32 sum o: one rounding to the output dtype;
+// with a residual, act(residual + act(o)) in fp32 (NaN stays NaN).
+template <bool BF16>
+__device__ __forceinline__ void store_out(float o, const void *residual, void *out, size_t i) {
+    if constexpr (BF16) {
+        uint16_t r = f32_to_bf16_rne(o);
+        if (residual) {
+            const float sum = bf16_bits_to_f32(((const uint16_t *)residual)[i]) + bf16_bits_to_f32(r);
+            r = f32_to_bf16_rne(sum);
+        }
+        ((uint16_t *)out)[i] = r;
+    } else {
+        if (residual) o = ((const float *)residual)[i] + o;
+        ((float *)out)[i] = o;
+    }
+}
+
+// out[t][m] = sum_j w[t][j] * y[t * k + j][m]: fp32 FMAs in j order; a
+// token with an invalid expert id gets NaN.
 template <bool BF16>
 __global__ __launch_bounds__(kBlock) void combine_kernel(const float *__restrict__ y,
                                                          const int *__restrict__ topk_idx,
@@ -763,33 +866,190 @@ __global__ __launch_bounds__(kBlock) void combine_kernel(const float *__restrict
         acc = fmaf(topk_w[s], y[(size_t)s * hidden + m], acc);
     }
     if (bad) acc = __builtin_nanf("");
-    const size_t o = (size_t)t * hidden + m;
-    if constexpr (BF16) {
-        uint16_t r = f32_to_bf16_rne(acc);
-        if (residual) {
-            const float sum = bf16_bits_to_f32(((const uint16_t *)residual)[o]) + bf16_bits_to_f32(r);
-            r = f32_to_bf16_rne(sum);
+    store_out<BF16>(acc, residual, out, (size_t)t * hidden + m);
+}
+
+// ------------------------------------------- down + combine, one token
+
+// A token alone has nothing to deduplicate: one workgroup per block of RW
+// output rows takes all k of the token's experts, lane (j, r) = expert j,
+// row r (RW = 64 / KP, KP = top_k rounded up to a power of two), and
+// combines the k results in LDS, so no combine launch follows.  Waves split
+// dff exactly as down_cols_kernel<NW, CPW> does and every sum is formed in
+// the same order (chunk dot products, per-wave chunk sums, wave-ordered
+// totals, group sums from the same wave reduction, then the j-ordered
+// combine), so a token's output is bitwise that of the batched kernels.
+constexpr int kHPad = 4;  // floats between the LDS rows of h (bank spread)
+
+// Workgroups are dealt to the 8 XCDs round robin by id.  Give each XCD a
+// contiguous range of blocks instead, so neighbouring row blocks, which
+// share cache lines of the weights' scales and biases, share one L2.
+constexpr int kXcds = 8;
+__device__ __forceinline__ int xcd_block(int b, int n) {
+    if (n % kXcds) return b;
+    return (b % kXcds) * (n / kXcds) + b / kXcds;
+}
+
+template <int NW, int CPW, int KP, bool BF16>
+__global__ __launch_bounds__(NW * kWave) void down_token_kernel(const uint4 *__restrict__ q,
+                                                                const uint16_t *__restrict__ sc,
+                                                                const uint16_t *__restrict__ bi,
+                                                                const float *__restrict__ h,
+                                                                const int *__restrict__ topk_idx,
+                                                                const float *__restrict__ topk_w,
+                                                                const void *residual, void *out,
+                                                                int hidden, int dff, int n_experts, int top_k) {
+    constexpr int RW = kWave / KP;
+    // dff = 32 * NW * CPW (the geometry's own shape): compile-time strides
+    constexpr int C = NW * CPW, F = 32 * C, G = C / 2, HS = F + kHPad;
+    extern __shared__ float smem[];
+    const int H = hidden;
+    float *hl = smem;                        // [k][HS]   h of the token's slots
+    float *gs = smem + top_k * HS;           // [k][G]    sums of h over each 64-group
+    float *part = gs + top_k * G;            // [NW][64]  per-wave sums
+    const int t = blockIdx.y;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int j = lane / RW, r = lane % RW;
+    const bool live = j < top_k;
+    const int m = xcd_block(blockIdx.x, gridDim.x) * RW + r;
+    const int e_raw = live ? topk_idx[t * top_k + j] : 0;
+    const float wj = live ? topk_w[t * top_k + j] : 0.f;  // read now, used by the combine
+    const int e = (unsigned)e_raw < (unsigned)n_experts ? e_raw : 0;  // invalid: NaN below
+    const int c0 = wave * CPW;
+
+    uint4 wq[CPW];
+    float ws[CPW], wb[CPW];
+#pragma unroll
+    for (int jj = 0; jj < CPW; ++jj) {
+        const int c = c0 + jj;
+        wq[jj] = load_stream(q + ((size_t)e * C + c) * H + m);
+        const size_t gi = ((size_t)e * G + c / 2) * H + m;
+        ws[jj] = f16_bits_to_f32(sc[gi]);
+        wb[jj] = (c & 1) ? 0.f : f16_bits_to_f32(bi[gi]);
+    }
+    // stage h and its group sums: wave w takes the (slot, group) pairs
+    // w, w + NW, ... (at most MAXP of them), all loads in flight at once
+    constexpr int MAXP = (KP * CPW + 1) / 2;  // k * G / NW <= KP * (NW * CPW / 2) / NW
+    const float *ht = h + (size_t)t * top_k * F;
+    const int n_pairs = top_k * G;
+    float hv0[MAXP];
+#pragma unroll
+    for (int i = 0; i < MAXP; ++i) {
+        const int p = wave + i * NW;
+        const int jp = p / G, g = p - jp * G;
+        hv0[i] = p < n_pairs ? ht[(size_t)jp * F + g * kGroup + lane] : 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < MAXP; ++i) {
+        const int p = wave + i * NW;
+        if (p < n_pairs) {
+            const int jp = p / G, g = p - jp * G;
+            hl[jp * HS + g * kGroup + lane] = hv0[i];
+            const float sum = wave_sum_all(hv0[i]);
+            if (lane == 0) gs[jp * G + g] = sum;
         }
-        ((uint16_t *)out)[o] = r;
-    } else {
-        if (residual) acc = ((const float *)residual)[o] + acc;
-        ((float *)out)[o] = acc;
+    }
+    __syncthreads();
+
+    float acc = 0.f;
+    if (live) {
+#pragma unroll
+        for (int jj = 0; jj < CPW; ++jj) {
+            const int c = c0 + jj;
+            float wf[32];
+            const uint32_t wd[4] = {wq[jj].x, wq[jj].y, wq[jj].z, wq[jj].w};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const uint32_t lo = wd[k] & 0x0F0F0F0Fu, hi = (wd[k] >> 4) & 0x0F0F0F0Fu;
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    wf[8 * k + 2 * b] = (float)((lo >> (8 * b)) & 0xFFu);
+                    wf[8 * k + 2 * b + 1] = (float)((hi >> (8 * b)) & 0xFFu);
+                }
+            }
+            const float gsum = (c & 1) ? 0.f : gs[j * G + c / 2];
+            const float4 *hc = (const float4 *)(hl + j * HS + c * 32);
+            float hv[32];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float4 v = hc[i];
+                hv[4 * i] = v.x;
+                hv[4 * i + 1] = v.y;
+                hv[4 * i + 2] = v.z;
+                hv[4 * i + 3] = v.w;
+            }
+            float d0 = 0.f, d1 = 0.f, d2 = 0.f, d3 = 0.f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                d0 = fmaf(wf[i], hv[i], d0);
+                d1 = fmaf(wf[8 + i], hv[8 + i], d1);
+                d2 = fmaf(wf[16 + i], hv[16 + i], d2);
+                d3 = fmaf(wf[24 + i], hv[24 + i], d3);
+            }
+            acc += fmaf(ws[jj], (d0 + d1) + (d2 + d3), wb[jj] * gsum);
+        }
+    }
+    const bool bad = __builtin_amdgcn_ballot_w64(live && (unsigned)e_raw >= (unsigned)n_experts) != 0;
+    part[wave * kWave + lane] = acc;
+    __syncthreads();
+    if (wave == 0) {  // lane r < RW: row r's k results, then the combine in j order
+        float o = 0.f;
+        for (int jk = 0; jk < top_k; ++jk) {
+            float y = part[jk * RW + r];
+#pragma unroll
+            for (int w = 1; w < NW; ++w) y += part[w * kWave + jk * RW + r];
+            const float wk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wj), jk * RW));
+            o = fmaf(wk, y, o);
+        }
+        if (bad) o = __builtin_nanf("");
+        if (lane < RW) store_out<BF16>(o, residual, out, (size_t)t * H + m);
     }
 }
 
 // ------------------------------------------------------------ dispatching
 
+// Rows per lane segment of the gate+up kernels: four for the whole-wave rows
+// (the 8-value transposed reduction), fewer when a lane holds many chunks.
+// Both gate+up kernels take the same value, so they reduce in the same order.
+template <int LPR, int NV>
+constexpr int gate_up_ri() {
+    return (LPR == kWave) ? (NV <= 2 ? 4 : 2) : (NV <= 2 ? 2 : 1);
+}
+
 template <int LPR, int NV>
 static moe_status launch_gate_up(const GateUpArgs &a, bool bf16, int groups_y, hipStream_t s) {
-    // rows per lane segment: four for the whole-wave rows (the 8-value
-    // transposed reduction), fewer when a lane holds many chunks
-    constexpr int RI = (LPR == kWave) ? (NV <= 2 ? 4 : 2) : (NV <= 2 ? 2 : 1);
+    constexpr int RI = gate_up_ri<LPR, NV>();
     constexpr int rows = (kWave / LPR) * RI;
     const dim3 grid((a.dff + rows - 1) / rows, groups_y);
     if (bf16)
         hipLaunchKernelGGL((gate_up_kernel<LPR, NV, RI, true>), grid, dim3(kWave), 0, s, a);
     else
         hipLaunchKernelGGL((gate_up_kernel<LPR, NV, RI, false>), grid, dim3(kWave), 0, s, a);
+    return MOE_OK;
+}
+
+// The routing gate+up kernel of a one-token batch: grid (row blocks, top_k).
+template <int LPR, int NV>
+static moe_status launch_gate_up_route(const GateUpArgs &a, bool bf16, int pl, const float *logits,
+                                       int32_t *idx, float *w, const PlanOut &p, hipStream_t s) {
+    constexpr int RI = gate_up_ri<LPR, NV>();
+    constexpr int rows = (kWave / LPR) * RI;
+    const dim3 grid((a.dff + rows - 1) / rows, a.top_k);
+#define MOE_GUR(PL)                                                                                        \
+    if (bf16)                                                                                              \
+        hipLaunchKernelGGL((gate_up_route_kernel<LPR, NV, RI, true, PL>), grid, dim3(kWave), 0, s, a, logits, \
+                           idx, w, p);                                                                     \
+    else                                                                                                   \
+        hipLaunchKernelGGL((gate_up_route_kernel<LPR, NV, RI, false, PL>), grid, dim3(kWave), 0, s, a, logits, \
+                           idx, w, p);
+    switch (pl) {
+        case 1: MOE_GUR(1) break;
+        case 2: MOE_GUR(2) break;
+        case 4: MOE_GUR(4) break;
+        default: return MOE_ERR_UNSUPPORTED;
+    }
+#undef MOE_GUR
     return MOE_OK;
 }
 
@@ -830,6 +1090,67 @@ static moe_status launch_down_cols(const moe_layer_t *L, const float *h, float *
         default: return MOE_ERR_UNSUPPORTED;
     }
     return MOE_OK;
+}
+
+// Smallest power of two >= top_k (1..16).
+static int pow2_at_least(int k) {
+    int p = 1;
+    while (p < k) p *= 2;
+    return p;
+}
+
+static size_t down_token_lds(const moe_layer_t *L, int nw) {
+    const int F = L->dff;
+    return ((size_t)L->top_k * (F + kHPad) + (size_t)L->top_k * (F / kGroup) + (size_t)nw * kWave) * sizeof(float);
+}
+
+template <int NW, int CPW, int KP>
+static void launch_down_token_t(const moe_layer_t *L, int n_tokens, const float *h, const int32_t *idx,
+                                const float *w, const void *residual, void *out, size_t lds, hipStream_t s) {
+    const dim3 grid(L->hidden / (kWave / KP), n_tokens);
+    const uint4 *q = (const uint4 *)L->down_q;
+    if (L->act_dtype == MOE_DTYPE_BF16)
+        hipLaunchKernelGGL((down_token_kernel<NW, CPW, KP, true>), grid, dim3(NW * kWave), lds, s, q, L->down_s,
+                           L->down_b, h, idx, w, residual, out, L->hidden, L->dff, L->n_experts, L->top_k);
+    else
+        hipLaunchKernelGGL((down_token_kernel<NW, CPW, KP, false>), grid, dim3(NW * kWave), lds, s, q, L->down_s,
+                           L->down_b, h, idx, w, residual, out, L->hidden, L->dff, L->n_experts, L->top_k);
+}
+
+template <int NW, int CPW>
+static moe_status launch_down_token_k(const moe_layer_t *L, int n_tokens, const float *h, const int32_t *idx,
+                                      const float *w, const void *residual, void *out, size_t lds,
+                                      hipStream_t s) {
+    switch (pow2_at_least(L->top_k)) {
+        case 1: launch_down_token_t<NW, CPW, 1>(L, n_tokens, h, idx, w, residual, out, lds, s); break;
+        case 2: launch_down_token_t<NW, CPW, 2>(L, n_tokens, h, idx, w, residual, out, lds, s); break;
+        case 4: launch_down_token_t<NW, CPW, 4>(L, n_tokens, h, idx, w, residual, out, lds, s); break;
+        case 8: launch_down_token_t<NW, CPW, 8>(L, n_tokens, h, idx, w, residual, out, lds, s); break;
+        case 16: launch_down_token_t<NW, CPW, 16>(L, n_tokens, h, idx, w, residual, out, lds, s); break;
+        default: return MOE_ERR_UNSUPPORTED;
+    }
+    return MOE_OK;
+}
+
+// The one-token down + combine kernel, when the layer has column-layout
+// down weights and its LDS fits; MOE_ERR_UNSUPPORTED otherwise (the caller
+// then takes the batched kernels).
+static moe_status launch_down_token(const moe_layer_t *L, int n_tokens, const float *h, const int32_t *idx,
+                                    const float *w, const void *residual, void *out, hipStream_t s) {
+    int nw, cpw;
+    if (L->down_layout != MOE_DOWN_COLS || !pick_down_cols(L->dff, &nw, &cpw)) return MOE_ERR_UNSUPPORTED;
+    if (L->hidden % (kWave / pow2_at_least(L->top_k))) return MOE_ERR_UNSUPPORTED;
+    const size_t lds = down_token_lds(L, nw);
+    if (lds > 65536) return MOE_ERR_UNSUPPORTED;
+    switch (nw * 100 + cpw) {
+#define MOE_DT(NW, CPW) \
+    case NW * 100 + CPW: return launch_down_token_k<NW, CPW>(L, n_tokens, h, idx, w, residual, out, lds, s);
+        MOE_DT(4, 1) MOE_DT(4, 3) MOE_DT(4, 5) MOE_DT(4, 7)
+        MOE_DT(8, 1) MOE_DT(8, 2) MOE_DT(8, 3)
+        MOE_DT(16, 2) MOE_DT(16, 3) MOE_DT(16, 4)
+#undef MOE_DT
+        default: return MOE_ERR_UNSUPPORTED;
+    }
 }
 
 // Every (lanes per row, chunks per lane) pair that the geometry pickers return.
@@ -936,6 +1257,11 @@ static moe_status enqueue_gate_up(const moe_layer_t *layer, const void *x, int n
     return MOE_OK;
 }
 
+// Batches up to this many tokens take the one-token down + combine kernel
+// (one workgroup row per token): with so few slots deduplication saves
+// little, and the combine launch goes away.
+constexpr int kTokenMajorMaxTokens = 1;
+
 static moe_status enqueue_down_combine(const moe_layer_t *layer, int n_tokens, const int32_t *topk_idx,
                                        const float *topk_w, const moe_plan_t *plan,
                                        const void *residual, void *out, void *workspace,
@@ -944,6 +1270,10 @@ static moe_status enqueue_down_combine(const moe_layer_t *layer, int n_tokens, c
     const float *h = (const float *)((char *)workspace + ws.h_off);
     float *y = (float *)((char *)workspace + ws.y_off);
     moe_status st;
+    if (n_tokens <= kTokenMajorMaxTokens) {
+        st = launch_down_token(layer, n_tokens, h, topk_idx, topk_w, residual, out, stream);
+        if (st != MOE_ERR_UNSUPPORTED) return st;
+    }
     if (layer->down_layout == MOE_DOWN_COLS) {
         st = launch_down_cols(layer, h, y, plan_view(plan), groups_y_of(layer, n_tokens),
                               n_tokens * layer->top_k, stream);
@@ -1019,6 +1349,57 @@ extern "C" moe_status moe_decode_step(const moe_layer_t *layer, const void *x, i
     st = enqueue_gate_up(layer, x, n_tokens, plan, workspace, stream);
     if (st != MOE_OK) return st;
     st = enqueue_down_combine(layer, n_tokens, topk_idx, topk_w, plan, residual, out, workspace, stream);
+    if (st != MOE_OK) return st;
+    return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_DEVICE;
+}
+
+extern "C" moe_status moe_route_gate_up(const moe_layer_t *layer, const float *logits, const void *x,
+                                        int32_t n_tokens, int32_t *topk_idx, float *topk_w,
+                                        const moe_plan_t *plan, void *workspace, size_t workspace_bytes,
+                                        void *hip_stream) {
+    moe_status st = check_step(layer, n_tokens, plan, workspace, workspace_bytes);
+    if (st != MOE_OK || n_tokens == 0) return st;
+    if ((st = check_route_args(logits, n_tokens, layer->n_experts, layer->top_k, topk_idx, topk_w)) != MOE_OK)
+        return st;
+    if ((st = check_plan_args(topk_idx, n_tokens, layer->n_experts, layer->top_k, plan)) != MOE_OK) return st;
+    if ((st = check_x(x)) != MOE_OK) return st;
+    hipStream_t stream = (hipStream_t)hip_stream;
+    const int pl = per_lane_bucket(layer->n_experts);
+    if (n_tokens > 1 || pl > 4) {  // router + planner launch, then gate+up
+        st = moe_route_plan(logits, n_tokens, layer->n_experts, layer->top_k, topk_idx, topk_w, plan, hip_stream);
+        if (st != MOE_OK) return st;
+        st = enqueue_gate_up(layer, x, n_tokens, plan, workspace, stream);
+    } else {  // one token: a single launch that routes for itself
+        Geometry gu;
+        pick_geometry_gate_up(layer->hidden, &gu);
+        const Workspace ws = workspace_layout(layer, n_tokens);
+        float *h = (float *)((char *)workspace + ws.h_off);
+        const GateUpArgs ga{(const uint4 *)layer->gate_q, (const uint4 *)layer->up_q, layer->gate_s,
+                            layer->gate_b, layer->up_s, layer->up_b, layer->expert_scale,
+                            layer->clamp_limit, x, plan_view(plan), h, layer->hidden, layer->dff,
+                            layer->n_experts, layer->top_k, layer->top_k, INT_MAX};
+        const PlanOut po{plan->counts, plan->offsets, plan->sorted_slots, plan->unique_experts, plan->n_unique,
+                         (int4 *)plan->work};
+        MOE_GEOMETRY_SWITCH(gu, st, launch_gate_up_route, ga, layer->act_dtype == MOE_DTYPE_BF16, pl, logits,
+                            topk_idx, topk_w, po, stream)
+    }
+    if (st != MOE_OK) return st;
+    return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_DEVICE;
+}
+
+extern "C" moe_status moe_decode_layer(const moe_layer_t *layer, const float *logits, const void *x,
+                                       int32_t n_tokens, int32_t *topk_idx, float *topk_w,
+                                       const moe_plan_t *plan, const void *residual, void *out,
+                                       void *workspace, size_t workspace_bytes, void *hip_stream) {
+    moe_status st = check_step(layer, n_tokens, plan, workspace, workspace_bytes);
+    if (st != MOE_OK || n_tokens == 0) return st;
+    if ((st = check_x(x)) != MOE_OK) return st;
+    if ((st = check_out(x, topk_idx, topk_w, residual, out)) != MOE_OK) return st;
+    st = moe_route_gate_up(layer, logits, x, n_tokens, topk_idx, topk_w, plan, workspace, workspace_bytes,
+                           hip_stream);
+    if (st != MOE_OK) return st;
+    st = enqueue_down_combine(layer, n_tokens, topk_idx, topk_w, plan, residual, out, workspace,
+                              (hipStream_t)hip_stream);
     if (st != MOE_OK) return st;
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_DEVICE;
 }

@@ -37,4 +37,11 @@ Workspace workspace_layout(const moe_layer_t *layer, int64_t max_tokens);
 
 constexpr size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
+// Logits per lane of the router's wave: the smallest of 1, 2, 4, 8, 16 that
+// holds n_experts / 64.
+inline int per_lane_bucket(int n_experts) {
+    const int per_lane = (n_experts + 63) / 64;
+    return per_lane <= 1 ? 1 : per_lane <= 2 ? 2 : per_lane <= 4 ? 4 : per_lane <= 8 ? 8 : 16;
+}
+
 }  // namespace moe

@@ -32,7 +32,7 @@ def test_library_exports_every_declared_function():
     assert set(declared) == set(_lib.EXPORTS)
     for name in declared:
         assert hasattr(L, name), name
-    assert L.moe_abi_version() == 3
+    assert L.moe_abi_version() == 4
 
 
 def test_status_strings():
@@ -159,6 +159,39 @@ def test_decode_step_validation_before_any_launch():
     assert call(plan=None) == moe.MOE_ERR_INVALID_ARG
     assert call(plan=_lib.PlanStruct(FAKE, FAKE, None, FAKE, FAKE, FAKE)) == moe.MOE_ERR_INVALID_ARG
     assert call(plan=_lib.PlanStruct(FAKE, FAKE, FAKE, FAKE, FAKE, None)) == moe.MOE_ERR_INVALID_ARG
+
+
+def test_decode_layer_validation_before_any_launch():
+    L = moe.lib()
+    st = layer()
+    p = _lib.PlanStruct(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+    ws_need = L.moe_workspace_size(C.byref(st), 1)
+    f = L.moe_decode_layer
+    G, X, O, W, I, WT = (FAKE + 0x5000000, FAKE + 0x1000000, FAKE + 0x2000000, FAKE + 0x3000000,
+                         FAKE + 0x6000000, FAKE + 0x7000000)
+
+    def call(lay=st, lg=G, x=X, n=1, idx=I, wt=WT, plan=p, res=None, out=O, ws=W, wsb=ws_need):
+        return f(C.byref(lay), lg, x, n, idx, wt, C.byref(plan) if plan is not None else None,
+                 res, out, ws, wsb, None)
+
+    assert call(n=0) == moe.MOE_OK  # empty batch: nothing launched
+    assert call(lg=None) == moe.MOE_ERR_INVALID_ARG
+    assert call(idx=None) == moe.MOE_ERR_INVALID_ARG
+    assert call(wt=None) == moe.MOE_ERR_INVALID_ARG
+    assert call(x=None) == moe.MOE_ERR_INVALID_ARG
+    assert call(out=X) == moe.MOE_ERR_INVALID_ARG
+    assert call(lay=layer(bits=3)) == moe.MOE_ERR_UNSUPPORTED
+    assert call(wsb=ws_need - 1) == moe.MOE_ERR_WORKSPACE
+    assert call(plan=None) == moe.MOE_ERR_INVALID_ARG
+    assert call(plan=_lib.PlanStruct(None, FAKE, FAKE, FAKE, FAKE, FAKE)) == moe.MOE_ERR_INVALID_ARG
+    assert call(plan=_lib.PlanStruct(FAKE, FAKE, FAKE, FAKE, None, FAKE)) == moe.MOE_ERR_INVALID_ARG
+    g = L.moe_route_gate_up
+    assert g(C.byref(st), G, X, 0, I, WT, C.byref(p), W, ws_need, None) == moe.MOE_OK
+    assert g(C.byref(st), None, X, 1, I, WT, C.byref(p), W, ws_need, None) == moe.MOE_ERR_INVALID_ARG
+    assert g(C.byref(st), G, None, 1, I, WT, C.byref(p), W, ws_need, None) == moe.MOE_ERR_INVALID_ARG
+    assert g(C.byref(st), G, X, 1, I, WT, C.byref(p), W, ws_need - 1, None) == moe.MOE_ERR_WORKSPACE
+    assert g(C.byref(layer(group_size=128)), G, X, 1, I, WT, C.byref(p), W, ws_need, None) == \
+        moe.MOE_ERR_UNSUPPORTED
 
 
 def test_pack_down_validation_before_any_launch():

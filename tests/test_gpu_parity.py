@@ -50,11 +50,14 @@ def test_router_shapes_and_ties(E, k):
     lg[0] = 0.0                      # all tied: ids ascending
     lg[1, ::3] = 1.0                 # partial ties
     lg[2] = -lg[2]
+    lg[3] = 0.0
+    lg[3, ::2] = -0.0                # -0 and +0 tie: ids ascending
     idx, w = moe.route_topk(torch.from_numpy(lg).cuda(), k)
     ridx, rw = oracle.route_topk(lg, k)
     assert np.array_equal(idx.cpu().numpy(), ridx)
     assert np.abs(w.cpu().numpy() - rw).max() <= 1e-6
     assert idx.cpu().numpy()[0].tolist() == list(range(k))
+    assert idx.cpu().numpy()[3].tolist() == list(range(k))
     if k == 1:
         assert np.all(w.cpu().numpy() == 1.0)
 
@@ -231,6 +234,43 @@ def test_gate_up_mfma_path(H, F, E, k, B):
     run = GpuRun(L, x, lg)
     check_against_oracle(L, x, lg, run, f"mfma {H}x{F}x{E}x{k} B{B}")
     assert run.plan_np["counts"].max() >= 3
+
+
+@pytest.mark.parametrize("layout", ["rows", "cols"])
+@pytest.mark.parametrize("H,F,E,k,act", [
+    (2048, 768, 128, 8, "bf16"),    # the single-token decode layer
+    (4096, 2048, 256, 6, "bf16"),   # four logits per router lane, sidecar and clamp
+    (256, 128, 8, 2, "f32"),
+    (512, 256, 16, 1, "bf16"),      # k = 1
+    (256, 256, 4, 4, "bf16"),       # k = E
+    (128, 384, 512, 16, "bf16"),    # 512 experts: routed by the router launch instead
+])
+def test_decode_layer_one_token_is_bitwise_the_two_call_path(H, F, E, k, act, layout):
+    """moe_decode_layer at B = 1 (gate+up routes for itself) against
+    moe_route_plan + moe_decode_step: outputs, routing and plan identical."""
+    wide = (H, E) == (4096, 256)
+    sh = Shape(f"l{H}x{F}x{E}", 37, H, F, E, k, act, sidecar=wide, clamp=10.0 if wide else 0.0)
+    log(f"[case] decode_layer B=1 {H}x{F}x{E}x{k} {act} down={layout}")
+    lg = make_logits(sh, 1, seed=E + k)
+    L = layer_for(sh, lg, seed=E + k)
+    x = make_x(sh, 1, seed=E + k)
+    res = make_x(sh, 1, seed=E + k + 1)
+    dl = moe.DeviceLayer.from_host(L)
+    if layout == "cols":
+        dl = dl.pack_down()
+    lgt = torch.from_numpy(lg).cuda()
+    xt, rt = dev_x(x), dev_x(res)
+    out1, idx1, w1, plan1 = moe.decode_layer(dl, xt, lgt, residual=rt)
+    idx2, w2, plan2 = moe.route_plan(lgt, k)
+    out2 = moe.decode_step(dl, xt, idx2, w2, plan2, residual=rt)
+    torch.cuda.synchronize()
+    assert torch.equal(idx1, idx2) and torch.equal(w1, w2)
+    for f in ("counts", "offsets", "unique_experts", "n_unique", "work"):
+        assert torch.equal(getattr(plan1, f), getattr(plan2, f)), f
+    assert torch.equal(plan1.sorted_slots[:k], plan2.sorted_slots[:k])
+    assert np.array_equal(host_bits(out1), host_bits(out2))
+    ridx, _ = oracle.route_topk(lg, k)
+    assert np.array_equal(idx1.cpu().numpy(), ridx)
 
 
 # --------------------------------------------------------------- invariants
