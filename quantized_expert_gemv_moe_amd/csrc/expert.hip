@@ -413,28 +413,22 @@ __global__ __launch_bounds__(kWave) void gate_up_kernel(GateUpArgs a) {
     }
 }
 
-// A batch of one token, routed here: workgroup (row block, j) finds the
-// token's expert of rank j itself from the logits (j + 1 selection rounds)
-// instead of waiting for a router launch and a plan.  Workgroup (0, 0)
-// routes in full and writes topk_idx, topk_w and the plan, exactly as
-// moe_route_plan would.  The arithmetic per row is gate_up_kernel's, so h
-// is bitwise the same as on the batched path.
+// A batch of one token, routed here, on a 1-D grid: block 0 routes in full
+// and writes topk_idx, topk_w and the plan, exactly as moe_route_plan would;
+// every other block (row block, j) finds the token's expert of rank j itself
+// from the logits (j + 1 selection rounds) instead of waiting for a router
+// launch and a plan.  The arithmetic per row is gate_up_kernel's, so h is
+// bitwise the same as on the batched path.
 template <int LPR, int NV, int RI, bool XBF16, int PL>
 __global__ __launch_bounds__(kWave) void gate_up_route_kernel(GateUpArgs a, const float *__restrict__ logits,
                                                               int *__restrict__ topk_idx,
-                                                              float *__restrict__ topk_w, PlanOut p) {
+                                                              float *__restrict__ topk_w, PlanOut p,
+                                                              int row_blocks) {
     constexpr int RPI = kWave / LPR;
     constexpr int ROWS_WG = RPI * RI;
     const int lane = threadIdx.x;
     const int sl = lane % LPR;
-    const int j = blockIdx.y;
-    uint4 xraw0[XBF16 ? NV : 1][4];
-    if constexpr (XBF16) {
-#pragma unroll
-        for (int v = 0; v < NV; ++v) load_x32_bf16((const uint16_t *)a.x, 0, (v * LPR + sl) * 32, xraw0[v]);
-    }
-    int e;
-    if (blockIdx.x == 0 && j == 0) {
+    if (blockIdx.x == 0) {
         __shared__ int idx_lds[kWave];
         __shared__ int cnt[MOE_MAX_EXPERTS], off[MOE_MAX_EXPERTS], uix[MOE_MAX_EXPERTS];
         int id;
@@ -444,13 +438,19 @@ __global__ __launch_bounds__(kWave) void gate_up_route_kernel(GateUpArgs a, cons
             topk_w[lane] = wt;
             idx_lds[lane] = id;
         }
-        e = __builtin_amdgcn_readfirstlane(id);
         __builtin_amdgcn_wave_barrier();
         plan_wave_small<PL>(idx_lds, a.top_k, a.n_experts, p, cnt, off, uix);
-    } else {
-        e = route_rank<PL>(logits, a.n_experts, j);
+        return;
     }
-    const int row0 = blockIdx.x * ROWS_WG + lane / LPR;
+    const int bb = blockIdx.x - 1;
+    const int rb = bb % row_blocks, j = bb / row_blocks;
+    const int row0 = rb * ROWS_WG + lane / LPR;
+    uint4 xraw0[XBF16 ? NV : 1][4];
+    if constexpr (XBF16) {
+#pragma unroll
+        for (int v = 0; v < NV; ++v) load_x32_bf16((const uint16_t *)a.x, 0, (v * LPR + sl) * 32, xraw0[v]);
+    }
+    const int e = route_rank<PL>(logits, a.n_experts, j);
     GateUpRows<RI, NV> w;
     load_gate_up_rows<LPR, NV, RI, XBF16>(a, e, row0, sl, w);
     const float sc = a.expert_scale ? a.expert_scale[e] : 1.f;
@@ -1029,20 +1029,22 @@ static moe_status launch_gate_up(const GateUpArgs &a, bool bf16, int groups_y, h
     return MOE_OK;
 }
 
-// The routing gate+up kernel of a one-token batch: grid (row blocks, top_k).
+// The routing gate+up kernel of a one-token batch: a planner block, then
+// row blocks x top_k.
 template <int LPR, int NV>
 static moe_status launch_gate_up_route(const GateUpArgs &a, bool bf16, int pl, const float *logits,
                                        int32_t *idx, float *w, const PlanOut &p, hipStream_t s) {
     constexpr int RI = gate_up_ri<LPR, NV>();
     constexpr int rows = (kWave / LPR) * RI;
-    const dim3 grid((a.dff + rows - 1) / rows, a.top_k);
+    const int row_blocks = (a.dff + rows - 1) / rows;
+    const dim3 grid(1 + row_blocks * a.top_k);
 #define MOE_GUR(PL)                                                                                        \
     if (bf16)                                                                                              \
         hipLaunchKernelGGL((gate_up_route_kernel<LPR, NV, RI, true, PL>), grid, dim3(kWave), 0, s, a, logits, \
-                           idx, w, p);                                                                     \
+                           idx, w, p, row_blocks);                                                         \
     else                                                                                                   \
         hipLaunchKernelGGL((gate_up_route_kernel<LPR, NV, RI, false, PL>), grid, dim3(kWave), 0, s, a, logits, \
-                           idx, w, p);
+                           idx, w, p, row_blocks);
     switch (pl) {
         case 1: MOE_GUR(1) break;
         case 2: MOE_GUR(2) break;

@@ -58,14 +58,17 @@ __global__ __launch_bounds__(kBlock) void expert_plan_kernel(const int *__restri
         __shared__ int cnt[MOE_MAX_EXPERTS], off[MOE_MAX_EXPERTS], uix[MOE_MAX_EXPERTS];
         if (threadIdx.x < kWave) plan_wave_small<PER_LANE>(topk_idx, n_slots, n_experts, p, cnt, off, uix);
     } else {
-        plan_block(topk_idx, n_slots, n_experts, p);
+        plan_block<kBlock>(topk_idx, n_slots, n_experts, p);
     }
 }
 
-// Router and planner in one workgroup: the four waves route the tokens, the
-// indices are kept in LDS (and written out), then the block plans them.
+// Router and planner in one workgroup: its waves (up to 16) route the
+// tokens, the indices are kept in LDS (and written out), then one wave (up
+// to 64 slots) or the whole block plans them.
+constexpr int kRoutePlanThreads = 1024;
+
 template <int PER_LANE>
-__global__ __launch_bounds__(kBlock) void route_plan_kernel(const float *__restrict__ logits, int n_tokens,
+__global__ __launch_bounds__(kRoutePlanThreads) void route_plan_kernel(const float *__restrict__ logits, int n_tokens,
                                                             int n_experts, int top_k,
                                                             int *__restrict__ topk_idx,
                                                             float *__restrict__ topk_w, PlanOut p) {
@@ -83,11 +86,11 @@ __global__ __launch_bounds__(kBlock) void route_plan_kernel(const float *__restr
     }
     __syncthreads();
     const int n_slots = n_tokens * top_k;
-    if (n_slots <= kWave) {  // launched with one wave per token, at most four
+    if (n_slots <= kWave) {  // launched with one wave per token
         __shared__ int cnt[MOE_MAX_EXPERTS], off[MOE_MAX_EXPERTS], uix[MOE_MAX_EXPERTS];
         if (threadIdx.x < kWave) plan_wave_small<PER_LANE>(idx_lds, n_slots, n_experts, p, cnt, off, uix);
-    } else {                 // launched with 256 threads
-        plan_block(idx_lds, n_slots, n_experts, p);
+    } else {                 // launched with kRoutePlanThreads threads
+        plan_block<kRoutePlanThreads>(idx_lds, n_slots, n_experts, p);
     }
 }
 
@@ -149,9 +152,11 @@ extern "C" moe_status moe_route_plan(const float *logits, int32_t n_tokens, int3
         if (st != MOE_OK) return st;
         return moe_expert_plan(topk_idx, n_tokens, n_experts, top_k, plan, hip_stream);
     }
-    // small batches: one wave per token (at most four); else a full block for the planner
+    // one wave per token (at most 16); the block planner takes all 1024 threads
     const int n_slots = n_tokens * top_k;
-    const int threads = n_slots <= kWave ? kWave * (n_tokens < 4 ? (n_tokens > 0 ? n_tokens : 1) : 4) : kBlock;
+    const int max_waves = kRoutePlanThreads / kWave;
+    const int threads = n_slots <= kWave ? kWave * (n_tokens < max_waves ? (n_tokens > 0 ? n_tokens : 1) : max_waves)
+                                         : kRoutePlanThreads;
     MOE_PER_LANE_SWITCH(per_lane_bucket(n_experts),
                         hipLaunchKernelGGL(route_plan_kernel<PL>, dim3(1), dim3(threads), 0, stream, logits,
                                            n_tokens, n_experts, top_k, topk_idx, topk_w, plan_out(plan)))

@@ -128,9 +128,11 @@ __device__ __forceinline__ int route_rank(const float *__restrict__ row, int n_e
 
 // ---------------------------------------------------------------- planner
 
-// Exclusive scan of one int per thread over the 256-thread block; returns
-// this thread's prefix and writes the block total to *total.
-__device__ __forceinline__ int block_exclusive_scan(int v, int *lds4, int *total) {
+// Exclusive scan of one int per thread over a block of NT threads; returns
+// this thread's prefix and writes the block total to *total.  `lds` holds
+// NT / 64 ints.
+template <int NT>
+__device__ __forceinline__ int block_exclusive_scan(int v, int *lds, int *total) {
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
     int inc = v;
@@ -139,12 +141,12 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int *lds4, int *total
         const int o = __shfl_up(inc, off, kWave);
         if (lane >= off) inc += o;
     }
-    if (lane == kWave - 1) lds4[wave] = inc;
+    if (lane == kWave - 1) lds[wave] = inc;
     __syncthreads();
     int base = 0, tot = 0;
 #pragma unroll
-    for (int w = 0; w < kBlock / kWave; ++w) {
-        const int s = lds4[w];
+    for (int w = 0; w < NT / kWave; ++w) {
+        const int s = lds[w];
         if (w < wave) base += s;
         tot += s;
     }
@@ -158,23 +160,24 @@ struct PlanOut {
     int4 *work;
 };
 
-// The planner body for one 256-thread workgroup.  `idx` may live in global
-// memory or in LDS.
+// The planner body for one workgroup of NT threads (256 or 1024).  `idx`
+// may live in global memory or in LDS.
+template <int NT>
 __device__ __forceinline__ void plan_block(const int *idx, int n_slots, int n_experts, const PlanOut &p) {
     __shared__ int cnt[MOE_MAX_EXPERTS];
     __shared__ int cursor[MOE_MAX_EXPERTS];
     __shared__ int first_slot[MOE_MAX_EXPERTS];
     __shared__ int uniq[MOE_MAX_EXPERTS];
-    __shared__ int lds4[kBlock / kWave];
+    __shared__ int lds_scan[NT / kWave];
     const int tid = threadIdx.x;
     const unsigned E = (unsigned)n_experts;
 
-    for (int e = tid; e < n_experts; e += kBlock) {
+    for (int e = tid; e < n_experts; e += NT) {
         cnt[e] = 0;
         first_slot[e] = INT_MAX;
     }
     __syncthreads();
-    for (int s = tid; s < n_slots; s += kBlock) {
+    for (int s = tid; s < n_slots; s += NT) {
         const int e = idx[s];
         if ((unsigned)e < E) {
             atomicAdd(&cnt[e], 1);          // integer: order-free
@@ -183,7 +186,7 @@ __device__ __forceinline__ void plan_block(const int *idx, int n_slots, int n_ex
     }
     __syncthreads();
 
-    constexpr int PER = MOE_MAX_EXPERTS / kBlock;  // experts owned per thread
+    constexpr int PER = MOE_MAX_EXPERTS / NT;  // experts owned per thread
     int c[PER], nz = 0, sum = 0;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
@@ -193,8 +196,8 @@ __device__ __forceinline__ void plan_block(const int *idx, int n_slots, int n_ex
         nz += c[i] > 0;
     }
     int total_slots, total_unique;
-    int run = block_exclusive_scan(sum, lds4, &total_slots);
-    int urun = block_exclusive_scan(nz, lds4, &total_unique);
+    int run = block_exclusive_scan<NT>(sum, lds_scan, &total_slots);
+    int urun = block_exclusive_scan<NT>(nz, lds_scan, &total_unique);
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
         const int e = tid * PER + i;
@@ -211,7 +214,7 @@ __device__ __forceinline__ void plan_block(const int *idx, int n_slots, int n_ex
         }
         run += c[i];
     }
-    for (int u = total_unique + tid; u < n_experts; u += kBlock) {
+    for (int u = total_unique + tid; u < n_experts; u += NT) {
         p.unique_experts[u] = -1;
         p.work[u] = make_int4(-1, total_slots, 0, 0);
     }
