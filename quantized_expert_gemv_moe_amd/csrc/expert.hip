@@ -752,11 +752,12 @@ __global__ __launch_bounds__(NW * kWave) void down_cols_kernel(const uint4 *__re
                                                                const float *__restrict__ h,
                                                                float *__restrict__ y, PlanView plan,
                                                                int hidden, int dff, int n_experts,
-                                                               int n_slots) {
+                                                               int n_slots, int max_count) {
     constexpr int S = kDownColsStage;
     __shared__ float part[NW][S][kWave];
     Work wk;
     if (!plan_expert(plan, blockIdx.y, n_experts, n_slots, &wk)) return;
+    if (wk.count > max_count) return;  // the MFMA kernel's expert
     const int lane = threadIdx.x & (kWave - 1);
     // wave index as a scalar: addresses built from it stay wave-uniform
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -823,6 +824,155 @@ __global__ __launch_bounds__(NW * kWave) void down_cols_kernel(const uint4 *__re
 #pragma unroll
             for (int w = 1; w < NW; ++w) v += part[w][i][lane];
             y[(size_t)plan_slot(plan, wk, s0 + i, n_slots) * H + m] = v;
+        }
+        __syncthreads();
+    }
+}
+
+// ----------------------------------------------------- down, MFMA tiles
+
+// Experts with many tokens, column layout: v_mfma_f32_16x16x32_bf16 with h
+// carried exactly.  Each fp32 h is split into three bf16 parts by
+// truncation, h = hi + mid + lo with every bit of h in exactly one part
+// (the low 16 bits of each remainder are dropped into the next), so the
+// three MFMAs per 32 inputs sum (128 + q) * h with every product exact in
+// fp32, as the fp32 FMA kernels do; only the order of the fp32 additions
+// differs.  Per 64-group the result D gives
+//   y += s * D + (b - 128 s) * sum(h over the group),
+// the group sum taken from the fp32 h.  A workgroup of NW waves owns
+// 16 * RT rows of the expert; wave w takes GW of the 64-groups; lane
+// (r, kq) holds word kq of chunks 2g and 2g + 1 of row r of each 16-row
+// tile (256 contiguous bytes per chunk and tile across the wave) and the h
+// of token r in the same nibble pairing as gate+up's MFMA kernel.  Partial
+// sums meet in LDS and are added in wave order; tokens go in tiles of 16.
+__device__ __forceinline__ void split3_pairs(const float *v, uint32_t (*o)[4]) {
+    // v[0..7] -> o[part][p] = (bf16 part of v[p], bf16 part of v[p + 4])
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const float a = v[p], b = v[p + 4];
+        const uint32_t a1 = __float_as_uint(a) & 0xFFFF0000u, b1 = __float_as_uint(b) & 0xFFFF0000u;
+        const float ar = a - __uint_as_float(a1), br = b - __uint_as_float(b1);
+        const uint32_t a2 = __float_as_uint(ar) & 0xFFFF0000u, b2 = __float_as_uint(br) & 0xFFFF0000u;
+        const float ar2 = ar - __uint_as_float(a2), br2 = br - __uint_as_float(b2);
+        const uint32_t a3 = __float_as_uint(ar2) & 0xFFFF0000u, b3 = __float_as_uint(br2) & 0xFFFF0000u;
+        o[0][p] = (a1 >> 16) | b1;
+        o[1][p] = (a2 >> 16) | b2;
+        o[2][p] = (a3 >> 16) | b3;
+    }
+}
+
+template <int NW, int GW, int RT>
+__global__ __launch_bounds__(NW * kWave) void down_mfma_kernel(const uint32_t *__restrict__ q,
+                                                               const uint16_t *__restrict__ sc,
+                                                               const uint16_t *__restrict__ bi,
+                                                               const float *__restrict__ h,
+                                                               float *__restrict__ y, PlanView plan,
+                                                               int hidden, int n_experts, int n_slots,
+                                                               int min_count) {
+    constexpr int ROWS = 16 * RT;
+    constexpr int G = NW * GW, C = 2 * G, F = C * 32;
+    extern __shared__ float smem[];
+    Work wk;
+    if (!plan_expert(plan, blockIdx.y, n_experts, n_slots, &wk)) return;
+    if (wk.count < min_count) return;  // the VALU kernel's expert
+    const int H = hidden;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int r16 = lane & 15, kq = lane >> 4;
+    const int m0 = blockIdx.x * ROWS;
+    const int g0 = wave * GW;
+
+    // this wave's weights: word kq of chunks 2g, 2g + 1 of each row tile
+    uint32_t wa[GW][RT][2];
+#pragma unroll
+    for (int gi = 0; gi < GW; ++gi)
+#pragma unroll
+        for (int t = 0; t < RT; ++t)
+#pragma unroll
+            for (int c2 = 0; c2 < 2; ++c2) {
+                const int c = 2 * (g0 + gi) + c2;
+                wa[gi][t][c2] = __builtin_nontemporal_load(q + (((size_t)wk.e * C + c) * H + m0 + 16 * t + r16) * 4 + kq);
+            }
+    // scales [group][row] in fp32, biases already shifted by -128 * scale
+    float *ss = smem, *sb = smem + G * ROWS;
+    float *part = smem + 2 * G * ROWS;  // [wave][lane][4 * RT]
+    for (int i = threadIdx.x; i < ROWS * G; i += NW * kWave) {
+        const int g = i / ROWS, r = i - g * ROWS;
+        const size_t si = ((size_t)wk.e * G + g) * H + m0 + r;
+        const float s1 = f16_bits_to_f32(sc[si]);
+        ss[g * ROWS + r] = s1;
+        sb[g * ROWS + r] = fmaf(-128.f, s1, f16_bits_to_f32(bi[si]));
+    }
+    __syncthreads();
+
+    for (int t0 = 0; t0 < wk.count; t0 += kMfmaTokens) {
+        const int nt = wk.count - t0 < kMfmaTokens ? wk.count - t0 : kMfmaTokens;
+        const bool live = r16 < nt;  // this lane's token column
+        const int slot = live ? plan_slot(plan, wk, t0 + r16, n_slots) : 0;
+        const float *hr = h + (size_t)slot * F;
+        // h of the token: 8 values of chunk 2g and 8 of chunk 2g + 1 per group
+        float hv[GW][2][8];
+#pragma unroll
+        for (int gi = 0; gi < GW; ++gi)
+#pragma unroll
+            for (int c2 = 0; c2 < 2; ++c2) {
+                const float4 *p4 = (const float4 *)(hr + (2 * (g0 + gi) + c2) * 32 + 8 * kq);
+                const float4 lo = live ? p4[0] : make_float4(0.f, 0.f, 0.f, 0.f);
+                const float4 hi = live ? p4[1] : make_float4(0.f, 0.f, 0.f, 0.f);
+                hv[gi][c2][0] = lo.x; hv[gi][c2][1] = lo.y; hv[gi][c2][2] = lo.z; hv[gi][c2][3] = lo.w;
+                hv[gi][c2][4] = hi.x; hv[gi][c2][5] = hi.y; hv[gi][c2][6] = hi.z; hv[gi][c2][7] = hi.w;
+            }
+        f32x4_t acc[RT];
+#pragma unroll
+        for (int t = 0; t < RT; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int gi = 0; gi < GW; ++gi) {
+            const int g = g0 + gi;
+            uint32_t hb[2][3][4];
+            float hs = 0.f;
+#pragma unroll
+            for (int c2 = 0; c2 < 2; ++c2) {
+                split3_pairs(hv[gi][c2], hb[c2]);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) hs += hv[gi][c2][i];
+            }
+            hs = swap16_sum(hs, hs);  // add the four lanes of the token
+            hs = swap32_sum(hs, hs);
+#pragma unroll
+            for (int t = 0; t < RT; ++t) {
+                f32x4_t d = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int c2 = 0; c2 < 2; ++c2) {
+                    uint32_t a[4];
+                    q4_pairs(wa[gi][t][c2], a);
+                    d = mfma16x16x32(a, hb[c2][0], d);
+                    d = mfma16x16x32(a, hb[c2][1], d);
+                    d = mfma16x16x32(a, hb[c2][2], d);
+                }
+                const float4 s1 = *(const float4 *)(ss + g * ROWS + 16 * t + 4 * kq);
+                const float4 b1 = *(const float4 *)(sb + g * ROWS + 16 * t + 4 * kq);
+                acc[t][0] += fmaf(s1.x, d[0], b1.x * hs);
+                acc[t][1] += fmaf(s1.y, d[1], b1.y * hs);
+                acc[t][2] += fmaf(s1.z, d[2], b1.z * hs);
+                acc[t][3] += fmaf(s1.w, d[3], b1.w * hs);
+            }
+        }
+        float *mine = part + ((size_t)wave * kWave + lane) * (4 * RT);
+#pragma unroll
+        for (int t = 0; t < RT; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) mine[t * 4 + i] = acc[t][i];
+        __syncthreads();
+        if (wave == 0 && live) {  // add the partials in wave order
+#pragma unroll
+            for (int t = 0; t < RT; ++t)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    float v = 0.f;
+#pragma unroll
+                    for (int w = 0; w < NW; ++w) v += part[((size_t)w * kWave + lane) * (4 * RT) + t * 4 + i];
+                    y[(size_t)slot * H + m0 + 16 * t + 4 * kq + i] = v;
+                }
         }
         __syncthreads();
     }
@@ -1073,18 +1223,19 @@ static moe_status launch_down(DownArgs a, int groups_y, int max_count, hipStream
 
 template <int NW, int CPW>
 static void launch_down_cols_t(const moe_layer_t *L, const float *h, float *y, PlanView pv, int groups_y,
-                               int n_slots, hipStream_t s) {
+                               int n_slots, int max_count, hipStream_t s) {
     const dim3 grid(L->hidden / kWave, groups_y);
     hipLaunchKernelGGL((down_cols_kernel<NW, CPW>), grid, dim3(NW * kWave), 0, s, (const uint4 *)L->down_q,
-                       L->down_s, L->down_b, h, y, pv, L->hidden, L->dff, L->n_experts, n_slots);
+                       L->down_s, L->down_b, h, y, pv, L->hidden, L->dff, L->n_experts, n_slots, max_count);
 }
 
 static moe_status launch_down_cols(const moe_layer_t *L, const float *h, float *y, PlanView pv, int groups_y,
-                                   int n_slots, hipStream_t s) {
+                                   int n_slots, int max_count, hipStream_t s) {
     int nw, cpw;
     if (!pick_down_cols(L->dff, &nw, &cpw)) return MOE_ERR_UNSUPPORTED;
     switch (nw * 100 + cpw) {
-#define MOE_DC(NW, CPW) case NW * 100 + CPW: launch_down_cols_t<NW, CPW>(L, h, y, pv, groups_y, n_slots, s); break;
+#define MOE_DC(NW, CPW) \
+    case NW * 100 + CPW: launch_down_cols_t<NW, CPW>(L, h, y, pv, groups_y, n_slots, max_count, s); break;
         MOE_DC(4, 1) MOE_DC(4, 3) MOE_DC(4, 5) MOE_DC(4, 7)
         MOE_DC(8, 1) MOE_DC(8, 2) MOE_DC(8, 3)
         MOE_DC(16, 2) MOE_DC(16, 3) MOE_DC(16, 4)
@@ -1264,6 +1415,44 @@ static moe_status enqueue_gate_up(const moe_layer_t *layer, const void *x, int n
 // little, and the combine launch goes away.
 constexpr int kTokenMajorMaxTokens = 1;
 
+// The MFMA down kernel: waves (NW) and 64-groups per wave (GW) for a dff,
+// 16-row tiles per workgroup; false when it has no instance.
+constexpr int kMfmaDownRowTiles = 4;
+static bool mfma_down_shape(const moe_layer_t *layer, int *nw, int *gw) {
+    if (layer->down_layout != MOE_DOWN_COLS || layer->dff % kGroup) return false;
+    if (layer->hidden % (16 * kMfmaDownRowTiles)) return false;
+    const int G = layer->dff / kGroup;
+    for (int n = 8; n >= 2; n -= 2)
+        if (G % n == 0 && G / n <= 4) {
+            *nw = n;
+            *gw = G / n;
+            return true;
+        }
+    return false;
+}
+
+static moe_status launch_down_mfma(const moe_layer_t *L, const float *h, float *y, PlanView pv, int groups_y,
+                                   int n_slots, int nw, int gw, hipStream_t s) {
+    constexpr int RT = kMfmaDownRowTiles;
+    const int G = L->dff / kGroup;
+    const size_t lds = ((size_t)2 * G * 16 * RT + (size_t)nw * kWave * 4 * RT) * sizeof(float);
+    const dim3 grid(L->hidden / (16 * RT), groups_y);
+    switch (nw * 100 + gw) {
+#define MOE_DM(NW, GW)                                                                                        \
+    case NW * 100 + GW:                                                                                       \
+        hipLaunchKernelGGL((down_mfma_kernel<NW, GW, RT>), grid, dim3(NW * kWave), lds, s, L->down_q, L->down_s, \
+                           L->down_b, h, y, pv, L->hidden, L->n_experts, n_slots, kMfmaMinCount);             \
+        break;
+        MOE_DM(2, 1) MOE_DM(2, 2) MOE_DM(2, 3) MOE_DM(2, 4)
+        MOE_DM(4, 1) MOE_DM(4, 2) MOE_DM(4, 3) MOE_DM(4, 4)
+        MOE_DM(6, 1) MOE_DM(6, 2) MOE_DM(6, 3) MOE_DM(6, 4)
+        MOE_DM(8, 1) MOE_DM(8, 2) MOE_DM(8, 3) MOE_DM(8, 4)
+#undef MOE_DM
+        default: return MOE_ERR_UNSUPPORTED;
+    }
+    return MOE_OK;
+}
+
 static moe_status enqueue_down_combine(const moe_layer_t *layer, int n_tokens, const int32_t *topk_idx,
                                        const float *topk_w, const moe_plan_t *plan,
                                        const void *residual, void *out, void *workspace,
@@ -1277,8 +1466,11 @@ static moe_status enqueue_down_combine(const moe_layer_t *layer, int n_tokens, c
         if (st != MOE_ERR_UNSUPPORTED) return st;
     }
     if (layer->down_layout == MOE_DOWN_COLS) {
-        st = launch_down_cols(layer, h, y, plan_view(plan), groups_y_of(layer, n_tokens),
-                              n_tokens * layer->top_k, stream);
+        int nw = 0, gw = 0;
+        const bool mfma = n_tokens >= kMfmaMinCount && mfma_down_shape(layer, &nw, &gw);
+        const int gy = groups_y_of(layer, n_tokens), n_slots = n_tokens * layer->top_k;
+        st = launch_down_cols(layer, h, y, plan_view(plan), gy, n_slots, mfma ? kMfmaMinCount - 1 : INT_MAX, stream);
+        if (st == MOE_OK && mfma) st = launch_down_mfma(layer, h, y, plan_view(plan), gy, n_slots, nw, gw, stream);
     } else {
         Geometry gd;
         pick_geometry(layer->dff, &gd);

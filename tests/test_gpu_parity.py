@@ -218,6 +218,7 @@ def test_decode_step_column_layout_geometries(H, F, E, k):
     check_against_oracle(L, x, lg, run, f"cols {H}x{F}x{E}x{k}")
 
 
+@pytest.mark.parametrize("layout", ["rows", "cols"])
 @pytest.mark.parametrize("H,F,E,k,B", [
     (256, 128, 2, 1, 20),     # one group per wave
     (512, 192, 4, 2, 7),      # experts with 3..7 tokens
@@ -225,14 +226,40 @@ def test_decode_step_column_layout_geometries(H, F, E, k):
     (4096, 256, 2, 2, 5),     # the wide hidden size
     (1024, 64, 8, 8, 3),      # k = E: every expert holds all three tokens
 ])
-def test_gate_up_mfma_path(H, F, E, k, B):
-    """Experts with >= 3 tokens run the MFMA gate+up kernel."""
+def test_gate_up_mfma_path(H, F, E, k, B, layout):
+    """Experts with >= 3 tokens run the MFMA gate+up kernel (and, with
+    column-layout down weights, the MFMA down kernel where it has a shape)."""
     sh = Shape(f"m{H}x{F}", 36, H, F, E, k, "bf16")
     lg = make_logits(sh, B, seed=H + B)
     L = make_layer(sh, seed=H + B)
     x = make_x(sh, B, seed=H + B)
-    run = GpuRun(L, x, lg)
-    check_against_oracle(L, x, lg, run, f"mfma {H}x{F}x{E}x{k} B{B}")
+    if layout == "cols" and F in (192, 64):
+        pytest.skip(f"dff {F} has no column-layout down kernel")
+    run = GpuRun(L, x, lg, cols=layout == "cols")
+    check_against_oracle(L, x, lg, run, f"mfma {H}x{F}x{E}x{k} B{B} {layout}")
+    assert run.plan_np["counts"].max() >= 3
+
+
+@pytest.mark.parametrize("H,F,E,k,B,act", [
+    (256, 128, 4, 2, 9, "bf16"),     # 2 waves x 1 group
+    (128, 256, 3, 2, 8, "f32"),      # 4 x 1, fp32 activations
+    (192, 384, 4, 2, 9, "bf16"),     # 6 x 1
+    (64, 512, 2, 1, 7, "bf16"),      # 8 x 1
+    (2048, 768, 8, 4, 12, "bf16"),   # 6 x 2: the decode layer's dff
+    (128, 1024, 2, 2, 5, "bf16"),    # 8 x 2
+    (256, 1536, 3, 2, 6, "bf16"),    # 8 x 3
+    (4096, 2048, 4, 2, 20, "bf16"),  # 8 x 4: the wide layer; 20 tokens on some experts (two token tiles)
+])
+def test_down_mfma_path(H, F, E, k, B, act):
+    """Column-layout down projection of experts with >= 3 tokens on MFMA, h
+    split exactly into three bf16 parts; every (waves, groups) instance."""
+    sh = Shape(f"d{H}x{F}", 38, H, F, E, k, act)
+    lg = make_logits(sh, B, seed=F + B)
+    L = make_layer(sh, seed=F + B)
+    x = make_x(sh, B, seed=F + B)
+    log(f"[case] down mfma {H}x{F}x{E}x{k} B={B} {act}")
+    run = GpuRun(L, x, lg, cols=True)
+    check_against_oracle(L, x, lg, run, f"down mfma {H}x{F}x{E}x{k} B{B} {act}")
     assert run.plan_np["counts"].max() >= 3
 
 
@@ -290,7 +317,8 @@ def test_determinism_batch_invariance_permutation_and_duplicates(layout):
     assert np.array_equal(a.out, b.out), "run-to-run results differ"
     # A token's result is bitwise the same alone and in the batch when its
     # experts take the same kernel variant (experts holding >= 3 tokens of a
-    # batch run the MFMA gate+up; at B = 1 every expert runs the dot2 one);
+    # batch run the MFMA gate+up and, with column-layout down weights, the
+    # MFMA down; at B = 1 every expert runs the VALU kernels);
     # across the switch both stay within the fp32 pipeline's error.
     counts = a.plan_np["counts"]
     n_mfma = 0
