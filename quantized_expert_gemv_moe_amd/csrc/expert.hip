@@ -364,14 +364,15 @@ __device__ __forceinline__ void gate_up_token_rows(const GateUpArgs &a, const Ga
     }
 }
 
-// One wave per workgroup.  LPR lanes per row, NV chunks per lane, RI rows
-// per segment; TCH tokens' activations in registers at a time.
+// One wave: row block rb of distinct expert u.  LPR lanes per row, NV
+// chunks per lane, RI rows per segment; TCH tokens' activations in
+// registers at a time.
 template <int LPR, int NV, int RI, bool XBF16>
-__global__ __launch_bounds__(kWave) void gate_up_kernel(GateUpArgs a) {
+__device__ __forceinline__ void gate_up_valu_block(const GateUpArgs &a, int rb, int u) {
     constexpr int RPI = kWave / LPR;  // rows per wave-wide pass
     constexpr int ROWS_WG = RPI * RI;
     constexpr int TCH = (XBF16 && NV == 1) ? 2 : 1;
-    const int lane = threadIdx.x;
+    const int lane = threadIdx.x & (kWave - 1);
     const int sl = lane % LPR;
     // With one token in the batch its activations are known before the plan
     // record arrives: issue those loads now, so the record's round trip and
@@ -385,10 +386,10 @@ __global__ __launch_bounds__(kWave) void gate_up_kernel(GateUpArgs a) {
         }
     }
     Work wk;
-    if (!plan_expert(a.plan, blockIdx.y, a.n_experts, a.n_slots, &wk)) return;
+    if (!plan_expert(a.plan, u, a.n_experts, a.n_slots, &wk)) return;
     if (wk.count > a.max_count) return;  // the MFMA kernel's expert
     const int e = wk.e, count = wk.count;
-    const int row0 = blockIdx.x * ROWS_WG + lane / LPR;
+    const int row0 = rb * ROWS_WG + lane / LPR;
 
     GateUpRows<RI, NV> w;
     load_gate_up_rows<LPR, NV, RI, XBF16>(a, e, row0, sl, w);
@@ -411,6 +412,11 @@ __global__ __launch_bounds__(kWave) void gate_up_kernel(GateUpArgs a) {
             gate_up_token_rows<LPR, NV, RI, XBF16>(a, w, x[i], slot[i], row0, sc, lim);
         }
     }
+}
+
+template <int LPR, int NV, int RI, bool XBF16>
+__global__ __launch_bounds__(kWave) void gate_up_kernel(GateUpArgs a) {
+    gate_up_valu_block<LPR, NV, RI, XBF16>(a, blockIdx.x, blockIdx.y);
 }
 
 // A batch of one token, routed here, on a 1-D grid: block 0 routes in full
@@ -461,14 +467,14 @@ __global__ __launch_bounds__(kWave) void gate_up_route_kernel(GateUpArgs a, cons
 
 // ----------------------------------------------------- gate+up, MFMA tiles
 
-// Experts with many tokens: v_mfma_f32_16x16x32_bf16.  A workgroup of four
-// waves owns 16 * RT rows of the expert and all of hidden; wave w takes a
-// quarter of the 64-groups.  Per group and 16-row tile, each lane holds two
-// words of its row (16 nibbles) as bf16 pairs of value 128 + q, the same
-// nibble pairing as the dot2 path, and its token's activations in the same
-// pairing; two MFMAs then sum exactly one group, so the fp32 group scale
-// and the folded bias (b - 128 s) * sum(x) apply per group after the MFMA.
-// Output lane l holds token l % 16 and rows 4 * (l / 16) .. + 3.  The four
+// Experts with many tokens: v_mfma_f32_16x16x32_bf16.  A workgroup of NW
+// waves owns 16 * RT rows of the expert and all of hidden; wave w takes GW
+// of the 64-groups.  Per group and 16-row tile, each lane holds two words
+// of its row (16 nibbles) as bf16 pairs of value 1 + q / 16, in the nibble
+// pairing of the dot2 path, and its token's activations in the same
+// pairing; two MFMAs then sum exactly one group, so the group scale (times
+// 16) and the folded bias (b - 16 s) * sum(x) apply per group after the
+// MFMA.  Output lane l holds token l % 16 and rows 4 * (l / 16) .. + 3.  The
 // waves' partial sums meet in LDS and are added in wave order; tokens go in
 // tiles of 16.
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
@@ -489,6 +495,19 @@ __device__ __forceinline__ void q4_pairs(uint32_t w, uint32_t *o) {
     o[1] = ((w >> 4) & M) | B;
     o[2] = ((w >> 8) & M) | B;
     o[3] = ((w >> 12) & M) | B;
+}
+
+// The same nibble pairs as bf16 values 1 + q / 16 (q in mantissa bits 3..6
+// of 1.0).  For the MFMA kernels: the offset that the group bias has to take
+// back out is then 16 times the nibble unit instead of 128 times, so the
+// cancellation between the two terms of the epilogue loses about eight
+// times fewer bits of the fp32 accumulation.
+__device__ __forceinline__ void q4_pairs16(uint32_t w, uint32_t *o) {
+    const uint32_t M = 0x00780078u, B = 0x3F803F80u;
+    o[0] = ((w << 3) & M) | B;
+    o[1] = ((w >> 1) & M) | B;
+    o[2] = ((w >> 5) & M) | B;
+    o[3] = ((w >> 9) & M) | B;
 }
 
 // Eight bf16 activations (one 16-byte word) as the pairs (x_p, x_{p+4}),
@@ -514,20 +533,37 @@ __device__ __forceinline__ uint2 load_stream2(const uint2 *p) {
 // NW waves, GW 64-groups per wave (NW * GW = hidden / 64), RT 16-row tiles.
 // Every weight load of a wave is issued before its first MFMA, and every
 // activation load of a token tile before that tile's first MFMA.
+// Elements 64g + 16kq .. + 15 of a token's activations for each of the
+// wave's groups: the B operands of one token column.
+template <int GW>
+__device__ __forceinline__ void load_x_mfma(const GateUpArgs &a, int slot, bool live, int g0, int kq,
+                                            uint4 (*xw)[2]) {
+    const uint16_t *xr = (const uint16_t *)a.x + (size_t)(slot / a.top_k) * a.hidden;
+#pragma unroll
+    for (int gi = 0; gi < GW; ++gi) {
+        const uint4 *xp = (const uint4 *)(xr + (g0 + gi) * kGroup + 16 * kq);
+        xw[gi][0] = live ? xp[0] : make_uint4(0, 0, 0, 0);
+        xw[gi][1] = live ? xp[1] : make_uint4(0, 0, 0, 0);
+    }
+}
+
 template <int NW, int GW, int RT>
-__global__ __launch_bounds__(NW * kWave) void gate_up_mfma_kernel(GateUpArgs a, int min_count) {
+__device__ __forceinline__ void gate_up_mfma_block(const GateUpArgs &a, int rb, int u, float *smem, int min_count) {
     constexpr int ROWS = 16 * RT;
     constexpr int G = NW * GW;
-    extern __shared__ float smem[];
     Work wk;
-    if (!plan_expert(a.plan, blockIdx.y, a.n_experts, a.n_slots, &wk)) return;
+    if (!plan_expert(a.plan, u, a.n_experts, a.n_slots, &wk)) return;
     if (wk.count < min_count) return;  // the expert belongs to the VALU kernel
     const int H = a.hidden, F = a.dff;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int r16 = lane & 15, kq = lane >> 4;
-    const int row0 = blockIdx.x * ROWS;
+    const int row0 = rb * ROWS;
     const int g0 = wave * GW;
+    // the first token tile's slots and activations, in flight with the weights
+    int slot = r16 < wk.count ? plan_slot(a.plan, wk, r16, a.n_slots) : 0;
+    uint4 xw[GW][2];
+    load_x_mfma<GW>(a, slot, r16 < wk.count, g0, kq, xw);
 
     // this wave's weights: words 2kq and 2kq+1 of each group, per row tile
     uint2 wgq[GW][RT], wuq[GW][RT];
@@ -544,7 +580,8 @@ __global__ __launch_bounds__(NW * kWave) void gate_up_mfma_kernel(GateUpArgs a, 
             }
         }
     }
-    // scales [group][row] in fp32, biases already shifted by -128 * scale
+    // per [group][row]: 16 * scale, and bias - 16 * scale (the weights go
+    // into the MFMA as 1 + q / 16)
     float *sg = smem, *bg = smem + G * ROWS, *su = smem + 2 * G * ROWS, *bu = smem + 3 * G * ROWS;
     float *part = smem + 4 * G * ROWS;  // [wave][lane][8 * RT]
     for (int i = threadIdx.x; i < ROWS * G; i += NW * kWave) {
@@ -552,10 +589,10 @@ __global__ __launch_bounds__(NW * kWave) void gate_up_mfma_kernel(GateUpArgs a, 
         const int row = row0 + r < F ? row0 + r : F - 1;
         const size_t si = ((size_t)wk.e * F + row) * G + g;
         const float s1 = f16_bits_to_f32(a.gate_s[si]), s2 = f16_bits_to_f32(a.up_s[si]);
-        sg[g * ROWS + r] = s1;
-        bg[g * ROWS + r] = fmaf(-128.f, s1, f16_bits_to_f32(a.gate_b[si]));
-        su[g * ROWS + r] = s2;
-        bu[g * ROWS + r] = fmaf(-128.f, s2, f16_bits_to_f32(a.up_b[si]));
+        sg[g * ROWS + r] = 16.f * s1;
+        bg[g * ROWS + r] = fmaf(-16.f, s1, f16_bits_to_f32(a.gate_b[si]));
+        su[g * ROWS + r] = 16.f * s2;
+        bu[g * ROWS + r] = fmaf(-16.f, s2, f16_bits_to_f32(a.up_b[si]));
     }
     __syncthreads();
     const float sc = a.expert_scale ? a.expert_scale[wk.e] : 1.f;
@@ -564,15 +601,9 @@ __global__ __launch_bounds__(NW * kWave) void gate_up_mfma_kernel(GateUpArgs a, 
     for (int t0 = 0; t0 < wk.count; t0 += kMfmaTokens) {
         const int nt = wk.count - t0 < kMfmaTokens ? wk.count - t0 : kMfmaTokens;
         const bool live = r16 < nt;  // this lane's token column
-        const int slot = live ? plan_slot(a.plan, wk, t0 + r16, a.n_slots) : 0;
-        const uint16_t *xr = (const uint16_t *)a.x + (size_t)(slot / a.top_k) * H;
-        // elements 64g + 16kq .. + 15 of the token for each group: the B operands
-        uint4 xw[GW][2];
-#pragma unroll
-        for (int gi = 0; gi < GW; ++gi) {
-            const uint4 *xp = (const uint4 *)(xr + (g0 + gi) * kGroup + 16 * kq);
-            xw[gi][0] = live ? xp[0] : make_uint4(0, 0, 0, 0);
-            xw[gi][1] = live ? xp[1] : make_uint4(0, 0, 0, 0);
+        if (t0 > 0) {
+            slot = live ? plan_slot(a.plan, wk, t0 + r16, a.n_slots) : 0;
+            load_x_mfma<GW>(a, slot, live, g0, kq, xw);
         }
         f32x4_t accg[RT], accu[RT];
 #pragma unroll
@@ -592,10 +623,10 @@ __global__ __launch_bounds__(NW * kWave) void gate_up_mfma_kernel(GateUpArgs a, 
 #pragma unroll
             for (int t = 0; t < RT; ++t) {
                 uint32_t ag[2][4], au[2][4];
-                q4_pairs(wgq[gi][t].x, ag[0]);
-                q4_pairs(wgq[gi][t].y, ag[1]);
-                q4_pairs(wuq[gi][t].x, au[0]);
-                q4_pairs(wuq[gi][t].y, au[1]);
+                q4_pairs16(wgq[gi][t].x, ag[0]);
+                q4_pairs16(wgq[gi][t].y, ag[1]);
+                q4_pairs16(wuq[gi][t].x, au[0]);
+                q4_pairs16(wuq[gi][t].y, au[1]);
                 f32x4_t dg = mfma16x16x32(ag[0], xb[0], f32x4_t{0.f, 0.f, 0.f, 0.f});
                 dg = mfma16x16x32(ag[1], xb[1], dg);
                 f32x4_t du = mfma16x16x32(au[0], xb[0], f32x4_t{0.f, 0.f, 0.f, 0.f});
@@ -641,6 +672,31 @@ __global__ __launch_bounds__(NW * kWave) void gate_up_mfma_kernel(GateUpArgs a, 
         }
         __syncthreads();
     }
+}
+
+template <int NW, int GW, int RT>
+__global__ __launch_bounds__(NW * kWave) void gate_up_mfma_kernel(GateUpArgs a, int min_count) {
+    extern __shared__ float smem[];
+    gate_up_mfma_block<NW, GW, RT>(a, blockIdx.x, blockIdx.y, smem, min_count);
+}
+
+// Both gate+up variants in one launch: blocks [0, mfma_blocks) are MFMA
+// workgroups (row block, distinct expert) for the experts with min_count or
+// more tokens; every wave of the later blocks is one dot2 workgroup (row
+// block, distinct expert) for the others.  The two kinds run side by side
+// instead of one launch after the other.
+template <int LPR, int NV, int RI, int NW, int GW, int RT>
+__global__ __launch_bounds__(NW * kWave) void gate_up_mixed_kernel(GateUpArgs a, int mfma_blocks, int rb_mfma,
+                                                                   int rb_valu, int n_valu, int min_count) {
+    extern __shared__ float smem[];
+    const int b = blockIdx.x;
+    if (b < mfma_blocks) {
+        gate_up_mfma_block<NW, GW, RT>(a, b % rb_mfma, b / rb_mfma, smem, min_count);
+        return;
+    }
+    const int vb = (b - mfma_blocks) * NW + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    if (vb >= n_valu) return;
+    gate_up_valu_block<LPR, NV, RI, true>(a, vb % rb_valu, vb / rb_valu);
 }
 
 // ------------------------------------------------------------------- down
@@ -835,10 +891,10 @@ __global__ __launch_bounds__(NW * kWave) void down_cols_kernel(const uint4 *__re
 // carried exactly.  Each fp32 h is split into three bf16 parts by
 // truncation, h = hi + mid + lo with every bit of h in exactly one part
 // (the low 16 bits of each remainder are dropped into the next), so the
-// three MFMAs per 32 inputs sum (128 + q) * h with every product exact in
-// fp32, as the fp32 FMA kernels do; only the order of the fp32 additions
-// differs.  Per 64-group the result D gives
-//   y += s * D + (b - 128 s) * sum(h over the group),
+// three MFMAs per 32 inputs sum (1 + q / 16) * h with every product exact
+// in fp32, as the fp32 FMA kernels do; only the order of the fp32
+// additions differs.  Per 64-group the result D gives
+//   y += 16 s * D + (b - 16 s) * sum(h over the group),
 // the group sum taken from the fp32 h.  A workgroup of NW waves owns
 // 16 * RT rows of the expert; wave w takes GW of the 64-groups; lane
 // (r, kq) holds word kq of chunks 2g and 2g + 1 of row r of each 16-row
@@ -893,15 +949,16 @@ __global__ __launch_bounds__(NW * kWave) void down_mfma_kernel(const uint32_t *_
                 const int c = 2 * (g0 + gi) + c2;
                 wa[gi][t][c2] = __builtin_nontemporal_load(q + (((size_t)wk.e * C + c) * H + m0 + 16 * t + r16) * 4 + kq);
             }
-    // scales [group][row] in fp32, biases already shifted by -128 * scale
+    // per [group][row]: 16 * scale, and bias - 16 * scale (the weights go
+    // into the MFMA as 1 + q / 16)
     float *ss = smem, *sb = smem + G * ROWS;
     float *part = smem + 2 * G * ROWS;  // [wave][lane][4 * RT]
     for (int i = threadIdx.x; i < ROWS * G; i += NW * kWave) {
         const int g = i / ROWS, r = i - g * ROWS;
         const size_t si = ((size_t)wk.e * G + g) * H + m0 + r;
         const float s1 = f16_bits_to_f32(sc[si]);
-        ss[g * ROWS + r] = s1;
-        sb[g * ROWS + r] = fmaf(-128.f, s1, f16_bits_to_f32(bi[si]));
+        ss[g * ROWS + r] = 16.f * s1;
+        sb[g * ROWS + r] = fmaf(-16.f, s1, f16_bits_to_f32(bi[si]));
     }
     __syncthreads();
 
@@ -944,7 +1001,7 @@ __global__ __launch_bounds__(NW * kWave) void down_mfma_kernel(const uint32_t *_
 #pragma unroll
                 for (int c2 = 0; c2 < 2; ++c2) {
                     uint32_t a[4];
-                    q4_pairs(wa[gi][t][c2], a);
+                    q4_pairs16(wa[gi][t][c2], a);
                     d = mfma16x16x32(a, hb[c2][0], d);
                     d = mfma16x16x32(a, hb[c2][1], d);
                     d = mfma16x16x32(a, hb[c2][2], d);
@@ -1019,12 +1076,13 @@ __global__ __launch_bounds__(kBlock) void combine_kernel(const float *__restrict
     store_out<BF16>(acc, residual, out, (size_t)t * hidden + m);
 }
 
-// ------------------------------------------- down + combine, one token
+// ------------------------------------ down + combine, token by token
 
-// A token alone has nothing to deduplicate: one workgroup per block of RW
-// output rows takes all k of the token's experts, lane (j, r) = expert j,
-// row r (RW = 64 / KP, KP = top_k rounded up to a power of two), and
-// combines the k results in LDS, so no combine launch follows.  Waves split
+// For a token alone there is nothing to deduplicate, and for a handful
+// little: workgroup (block of RW output rows, token t) takes all k of the
+// token's experts, lane (j, r) = expert j, row r (RW = 64 / KP, KP = top_k
+// rounded up to a power of two), and combines the k results in LDS, so no
+// combine launch follows.  Waves split
 // dff exactly as down_cols_kernel<NW, CPW> does and every sum is formed in
 // the same order (chunk dot products, per-wave chunk sums, wave-ordered
 // totals, group sums from the same wave reduction, then the j-ordered
@@ -1285,9 +1343,9 @@ static moe_status launch_down_token_k(const moe_layer_t *L, int n_tokens, const 
     return MOE_OK;
 }
 
-// The one-token down + combine kernel, when the layer has column-layout
+// The token-major down + combine kernel, when the layer has column-layout
 // down weights and its LDS fits; MOE_ERR_UNSUPPORTED otherwise (the caller
-// then takes the batched kernels).
+// then takes the deduplicated kernels).
 static moe_status launch_down_token(const moe_layer_t *L, int n_tokens, const float *h, const int32_t *idx,
                                     const float *w, const void *residual, void *out, hipStream_t s) {
     int nw, cpw;
@@ -1356,6 +1414,12 @@ static int groups_y_of(const moe_layer_t *layer, int n_tokens) {
 // Experts with at least this many slots take the MFMA kernel (when the batch
 // can have such experts at all and the layer suits it).
 constexpr int kMfmaMinCount = 3;
+// The MFMA kernels are launched only for batches of this many tokens or
+// more.  Below, few experts reach kMfmaMinCount tokens, and the extra
+// workgroups (one per row block and distinct expert, most of them finding
+// no such expert) cost more than the dot2 kernels save: measured on the
+// decode layer shape, 16 tokens is where Zipf-skewed routing starts to gain.
+constexpr int kMfmaMinTokens = 16;
 // 16-row tiles per workgroup: two, or one where a wave's registers would not
 // hold two (more than eight waves, i.e. hidden above 2048).
 static int mfma_row_tiles(int nw) { return nw > 8 ? 1 : 2; }
@@ -1376,6 +1440,39 @@ static size_t mfma_gate_up_lds(const moe_layer_t *layer, int nw) {
     return ((size_t)4 * G * ROWS + (size_t)nw * kWave * 8 * rt) * sizeof(float);
 }
 
+template <int LPR, int NV, int NW, int GW>
+static moe_status launch_gate_up_mixed_t(const moe_layer_t *layer, const GateUpArgs &ga, int groups_y,
+                                         hipStream_t stream) {
+    constexpr int RT = NW <= 8 ? 2 : 1;
+    constexpr int RI = gate_up_ri<LPR, NV>();
+    const int rb_mfma = (layer->dff + 16 * RT - 1) / (16 * RT);
+    const int rows_valu = (kWave / LPR) * RI;
+    const int rb_valu = (layer->dff + rows_valu - 1) / rows_valu;
+    const int n_valu = rb_valu * groups_y;
+    const int mfma_blocks = rb_mfma * groups_y;
+    const dim3 grid(mfma_blocks + (n_valu + NW - 1) / NW);
+    hipLaunchKernelGGL((gate_up_mixed_kernel<LPR, NV, RI, NW, GW, RT>), grid, dim3(NW * kWave),
+                       mfma_gate_up_lds(layer, NW), stream, ga, mfma_blocks, rb_mfma, rb_valu, n_valu, kMfmaMinCount);
+    return MOE_OK;
+}
+
+// One launch for both gate+up variants, for the hidden sizes that have an
+// instance (the dot2 geometry and the MFMA shape both follow from hidden):
+// 256 to 2048.  Beyond, a 12- or 16-wave block cannot give the dot2 waves
+// their registers, and the two variants go in two launches.
+static moe_status launch_gate_up_mixed(const moe_layer_t *layer, const GateUpArgs &ga, const Geometry &gu, int nw,
+                                       int gw, int groups_y, hipStream_t stream) {
+    if (gw != 4) return MOE_ERR_UNSUPPORTED;
+    const int key = (gu.lpr * 8 + gu.nv) * 100 + nw;
+    switch (key) {
+#define MOE_GMX(LPR, NV, NW) \
+    case (LPR * 8 + NV) * 100 + NW: return launch_gate_up_mixed_t<LPR, NV, NW, 4>(layer, ga, groups_y, stream);
+        MOE_GMX(2, 4, 1) MOE_GMX(4, 4, 2) MOE_GMX(8, 4, 4) MOE_GMX(16, 3, 6) MOE_GMX(64, 1, 8)
+#undef MOE_GMX
+        default: return MOE_ERR_UNSUPPORTED;
+    }
+}
+
 static moe_status enqueue_gate_up(const moe_layer_t *layer, const void *x, int n_tokens,
                                   const moe_plan_t *plan, void *workspace, hipStream_t stream) {
     Geometry gu;
@@ -1383,7 +1480,7 @@ static moe_status enqueue_gate_up(const moe_layer_t *layer, const void *x, int n
     const Workspace ws = workspace_layout(layer, n_tokens);
     float *h = (float *)((char *)workspace + ws.h_off);
     int nw = 0, gw = 0;
-    const bool use_mfma = n_tokens >= kMfmaMinCount && mfma_gate_up_shape(layer, &nw, &gw);
+    const bool use_mfma = n_tokens >= kMfmaMinTokens && mfma_gate_up_shape(layer, &nw, &gw);
     GateUpArgs ga{(const uint4 *)layer->gate_q, (const uint4 *)layer->up_q, layer->gate_s,
                   layer->gate_b, layer->up_s, layer->up_b, layer->expert_scale,
                   layer->clamp_limit, x, plan_view(plan), h, layer->hidden, layer->dff,
@@ -1392,6 +1489,10 @@ static moe_status enqueue_gate_up(const moe_layer_t *layer, const void *x, int n
     const bool bf16 = layer->act_dtype == MOE_DTYPE_BF16;
     const int groups_y = groups_y_of(layer, n_tokens);
     moe_status st;
+    if (use_mfma) {  // both variants in one launch where an instance exists
+        st = launch_gate_up_mixed(layer, ga, gu, nw, gw, groups_y, stream);
+        if (st != MOE_ERR_UNSUPPORTED) return st;
+    }
     MOE_GEOMETRY_SWITCH(gu, st, launch_gate_up, ga, bf16, groups_y, stream)
     if (st != MOE_OK || !use_mfma) return st;
     const int rows = 16 * mfma_row_tiles(nw);
@@ -1410,10 +1511,12 @@ static moe_status enqueue_gate_up(const moe_layer_t *layer, const void *x, int n
     return MOE_OK;
 }
 
-// Batches up to this many tokens take the one-token down + combine kernel
-// (one workgroup row per token): with so few slots deduplication saves
-// little, and the combine launch goes away.
-constexpr int kTokenMajorMaxTokens = 1;
+// Batches up to this many tokens take the token-major down + combine kernel
+// (one row of workgroups per token): with so few slots deduplication saves
+// little of the down projection's bytes, and the combine launch goes away
+// (measured faster than the deduplicated kernels plus combine at 2, 4 and
+// 8 tokens).
+constexpr int kTokenMajorMaxTokens = 8;
 
 // The MFMA down kernel: waves (NW) and 64-groups per wave (GW) for a dff,
 // 16-row tiles per workgroup; false when it has no instance.
@@ -1467,7 +1570,7 @@ static moe_status enqueue_down_combine(const moe_layer_t *layer, int n_tokens, c
     }
     if (layer->down_layout == MOE_DOWN_COLS) {
         int nw = 0, gw = 0;
-        const bool mfma = n_tokens >= kMfmaMinCount && mfma_down_shape(layer, &nw, &gw);
+        const bool mfma = n_tokens >= kMfmaMinTokens && mfma_down_shape(layer, &nw, &gw);
         const int gy = groups_y_of(layer, n_tokens), n_slots = n_tokens * layer->top_k;
         st = launch_down_cols(layer, h, y, plan_view(plan), gy, n_slots, mfma ? kMfmaMinCount - 1 : INT_MAX, stream);
         if (st == MOE_OK && mfma) st = launch_down_mfma(layer, h, y, plan_view(plan), gy, n_slots, nw, gw, stream);

@@ -221,14 +221,16 @@ def test_decode_step_column_layout_geometries(H, F, E, k):
 @pytest.mark.parametrize("layout", ["rows", "cols"])
 @pytest.mark.parametrize("H,F,E,k,B", [
     (256, 128, 2, 1, 20),     # one group per wave
-    (512, 192, 4, 2, 7),      # experts with 3..7 tokens
+    (512, 192, 12, 2, 16),    # experts with 0..7 tokens: both variants in one launch
     (2048, 768, 1, 1, 40),    # 40 tokens on one expert: three token tiles of 16
-    (4096, 256, 2, 2, 5),     # the wide hidden size
-    (1024, 64, 8, 8, 3),      # k = E: every expert holds all three tokens
+    (4096, 256, 2, 2, 16),    # the wide hidden size: the two variants in two launches
+    (1024, 64, 8, 8, 16),     # k = E: every expert holds all 16 tokens
+    (1536, 128, 8, 1, 17),    # one to five tokens per expert
 ])
 def test_gate_up_mfma_path(H, F, E, k, B, layout):
-    """Experts with >= 3 tokens run the MFMA gate+up kernel (and, with
-    column-layout down weights, the MFMA down kernel where it has a shape)."""
+    """In batches of 16 or more tokens, experts with >= 3 tokens run the
+    MFMA gate+up kernel (and, with column-layout down weights, the MFMA down
+    kernel where it has a shape)."""
     sh = Shape(f"m{H}x{F}", 36, H, F, E, k, "bf16")
     lg = make_logits(sh, B, seed=H + B)
     L = make_layer(sh, seed=H + B)
@@ -241,13 +243,13 @@ def test_gate_up_mfma_path(H, F, E, k, B, layout):
 
 
 @pytest.mark.parametrize("H,F,E,k,B,act", [
-    (256, 128, 4, 2, 9, "bf16"),     # 2 waves x 1 group
-    (128, 256, 3, 2, 8, "f32"),      # 4 x 1, fp32 activations
-    (192, 384, 4, 2, 9, "bf16"),     # 6 x 1
-    (64, 512, 2, 1, 7, "bf16"),      # 8 x 1
-    (2048, 768, 8, 4, 12, "bf16"),   # 6 x 2: the decode layer's dff
-    (128, 1024, 2, 2, 5, "bf16"),    # 8 x 2
-    (256, 1536, 3, 2, 6, "bf16"),    # 8 x 3
+    (256, 128, 4, 2, 16, "bf16"),    # 2 waves x 1 group
+    (128, 256, 3, 2, 16, "f32"),     # 4 x 1, fp32 activations
+    (192, 384, 4, 2, 17, "bf16"),    # 6 x 1
+    (64, 512, 2, 1, 16, "bf16"),     # 8 x 1
+    (2048, 768, 24, 4, 18, "bf16"),  # 6 x 2: the decode layer's dff; 0..8 tokens per expert
+    (128, 1024, 2, 2, 16, "bf16"),   # 8 x 2
+    (256, 1536, 3, 2, 16, "bf16"),   # 8 x 3
     (4096, 2048, 4, 2, 20, "bf16"),  # 8 x 4: the wide layer; 20 tokens on some experts (two token tiles)
 ])
 def test_down_mfma_path(H, F, E, k, B, act):
@@ -316,10 +318,37 @@ def test_determinism_batch_invariance_permutation_and_duplicates(layout):
     b = GpuRun(L, x, lg, dl=dl)
     assert np.array_equal(a.out, b.out), "run-to-run results differ"
     # A token's result is bitwise the same alone and in the batch when its
-    # experts take the same kernel variant (experts holding >= 3 tokens of a
-    # batch run the MFMA gate+up and, with column-layout down weights, the
-    # MFMA down; at B = 1 every expert runs the VALU kernels);
-    # across the switch both stay within the fp32 pipeline's error.
+    # experts take the same kernel variant.  Batches under 16 tokens run the
+    # VALU kernels only, so here every token must match bitwise (the shared
+    # experts hold three tokens: in a batch of 16 they would go to MFMA).
+    assert a.plan_np["counts"].max() >= 3
+    for t in range(B):
+        one = GpuRun(L, x[t:t + 1], lg[t:t + 1], dl=dl)
+        assert np.array_equal(one.out[0], a.out[t]), f"token {t} alone differs from the batch"
+    perm = np.array([5, 2, 7, 0, 1, 6, 3, 4])
+    p = GpuRun(L, x[perm], lg[perm], dl=dl)
+    assert np.array_equal(p.out, a.out[perm])
+    d = GpuRun(L, np.repeat(x[2:3], 4, axis=0), dup_lg, dl=dl)
+    assert d.plan_np["n_unique"] == sh.top_k
+    assert np.all(d.out == d.out[0:1])
+    assert np.array_equal(d.out[0], a.out[2])
+
+
+@pytest.mark.parametrize("layout", ["rows", "cols"])
+def test_batch_invariance_across_the_mfma_switch(layout):
+    """In a batch of 16, tokens whose experts all hold < 3 tokens stay
+    bitwise equal to the token alone; the others (MFMA kernels) stay within
+    the fp32 pipeline's error of it."""
+    sh = SHAPES["cohort"]
+    B = 16
+    lg = make_logits(sh, B, regime="sharing", seed=21)
+    x = make_x(sh, B, seed=21)
+    L = layer_for(sh, lg, seed=21)
+    dl = moe.DeviceLayer.from_host(L)
+    if layout == "cols":
+        dl = dl.pack_down()
+    a = GpuRun(L, x, lg, dl=dl)
+    check_against_oracle(L, x, lg, a, f"cohort B16 sharing {layout}")
     counts = a.plan_np["counts"]
     n_mfma = 0
     for t in range(B):
@@ -329,14 +358,7 @@ def test_determinism_batch_invariance_permutation_and_duplicates(layout):
         else:
             n_mfma += 1
             assert rel_l2(oracle.bf16_to_f64(one.out[0]), oracle.bf16_to_f64(a.out[t])) <= 5e-4
-    assert n_mfma > 0  # the shared experts hold three tokens
-    perm = np.array([5, 2, 7, 0, 1, 6, 3, 4])
-    p = GpuRun(L, x[perm], lg[perm], dl=dl)
-    assert np.array_equal(p.out, a.out[perm])
-    d = GpuRun(L, np.repeat(x[2:3], 4, axis=0), dup_lg, dl=dl)
-    assert d.plan_np["n_unique"] == sh.top_k
-    assert np.all(d.out == d.out[0:1])
-    assert rel_l2(oracle.bf16_to_f64(d.out[0]), oracle.bf16_to_f64(a.out[2])) <= 5e-4
+    assert 0 < n_mfma < B
 
 
 def test_batch_size_changes_between_calls_with_the_same_buffers():
