@@ -266,6 +266,27 @@ def cpu_baseline(rot, budget_s):
 
 
 # ------------------------------------------------------------------ main
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "decode_b1_traffic.json")
+
+
+def counted_traffic(workload: str, kernel: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    record (FETCH_SIZE and WRITE_SIZE, scaled by a plain copy's counts), or
+    None when there is none for this workload or the kernel sources changed
+    since the counters were taken."""
+    import hashlib
+
+    if workload != "decode" or not os.path.exists(TRAFFIC_RECORD):
+        return None
+    rec = json.load(open(TRAFFIC_RECORD))
+    h = hashlib.sha256()
+    for f in rec["sources"]:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    if h.hexdigest() != rec["sources_sha256"] or kernel not in rec["kernels"]:
+        return None
+    return rec["kernels"][kernel]["traffic_bytes"]
+
+
 def copy_calibration():
     import torch
 
@@ -323,7 +344,9 @@ def main():
     kernels["down_combine"]["gbps"] = dn_bytes / kt["down_combine"] / 1e9
     log(f"[bench] kernels: " + ", ".join(f"{k} {v['us']:.2f} us" for k, v in kernels.items()))
     ach = gu_bytes / kt["route_gate_up"] / 1e9
-    gu_kernel = "gate_up_route_kernel" if B == 1 else "route_plan_kernel + gate_up kernels"
+    gu_kernel = ("gate_up_route_kernel<64, 1, 4, true, 2>" if B == 1 and sh.hidden == 2048 and sh.n_experts == 128
+                 else "gate_up_route_kernel" if B == 1 else "route_plan_kernel + gate_up kernels")
+    traffic = counted_traffic(args.workload, gu_kernel)
 
     ladder = []
     if not args.no_ladder and sh.name in ("decode", "cohort", "stack"):
@@ -368,7 +391,7 @@ def main():
         "hbm_frac": gbps / HBM_PEAK_GBPS,
         "unique_experts_per_step": avg_unique,
         "roofline": {"bound": "hbm", "kernel": gu_kernel, "achieved": ach, "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": ach / HBM_PEAK_GBPS, "traffic": None,
+                     "unit": "GB/s", "frac": ach / HBM_PEAK_GBPS, "traffic": traffic,
                      "bytes_per_launch": gu_bytes, "us_per_launch": kt["route_gate_up"] * 1e6},
         "kernels": kernels,
         "ladder": ladder,
