@@ -1115,26 +1115,39 @@ __global__ __launch_bounds__(NW * kWave) void down_token_kernel(const uint4 *__r
     float *hl = smem;                        // [k][HS]   h of the token's slots
     float *gs = smem + top_k * HS;           // [k][G]    sums of h over each 64-group
     float *part = gs + top_k * G;            // [NW][64]  per-wave sums
+    float *sl = part + NW * kWave;           // [2][k][G][RW] scales, then biases
     const int t = blockIdx.y;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int j = lane / RW, r = lane % RW;
     const bool live = j < top_k;
-    const int m = xcd_block(blockIdx.x, gridDim.x) * RW + r;
+    const int mb = xcd_block(blockIdx.x, gridDim.x) * RW;
+    const int m = mb + r;
     const int e_raw = live ? topk_idx[t * top_k + j] : 0;
     const float wj = live ? topk_w[t * top_k + j] : 0.f;  // read now, used by the combine
     const int e = (unsigned)e_raw < (unsigned)n_experts ? e_raw : 0;  // invalid: NaN below
     const int c0 = wave * CPW;
 
     uint4 wq[CPW];
-    float ws[CPW], wb[CPW];
 #pragma unroll
-    for (int jj = 0; jj < CPW; ++jj) {
-        const int c = c0 + jj;
-        wq[jj] = load_stream(q + ((size_t)e * C + c) * H + m);
-        const size_t gi = ((size_t)e * G + c / 2) * H + m;
-        ws[jj] = f16_bits_to_f32(sc[gi]);
-        wb[jj] = (c & 1) ? 0.f : f16_bits_to_f32(bi[gi]);
+    for (int jj = 0; jj < CPW; ++jj) wq[jj] = load_stream(q + ((size_t)e * C + (c0 + jj)) * H + m);
+    // Scales and biases of the block's RW rows, 4 rows (8 bytes) per load:
+    // unit u = ((sb * k + expert) * G + group) * RW/4 + quarter.  Loading them
+    // per lane would touch one cache line per 16 bytes used.
+    constexpr int QPR = RW / 4;  // RW >= 4 as top_k <= 16
+    const int n_units = 2 * top_k * G * QPR;
+    uint2 su[(2 * KP * G * QPR + NW * kWave - 1) / (NW * kWave)];
+#pragma unroll
+    for (int i = 0; i < (int)(sizeof(su) / sizeof(su[0])); ++i) {
+        const int u = threadIdx.x + i * NW * kWave;
+        su[i] = make_uint2(0, 0);
+        if (u < n_units) {
+            const int qq = u % QPR, g = (u / QPR) % G, jx = (u / (QPR * G)) % top_k, sb = u / (QPR * G * top_k);
+            const int ex_raw = topk_idx[t * top_k + jx];
+            const int ex = (unsigned)ex_raw < (unsigned)n_experts ? ex_raw : 0;
+            const uint16_t *src = sb ? bi : sc;
+            su[i] = *(const uint2 *)(src + ((size_t)ex * G + g) * H + mb + 4 * qq);
+        }
     }
     // stage h and its group sums: wave w takes the (slot, group) pairs
     // w, w + NW, ... (at most MAXP of them), all loads in flight at once
@@ -1158,7 +1171,26 @@ __global__ __launch_bounds__(NW * kWave) void down_token_kernel(const uint4 *__r
             if (lane == 0) gs[jp * G + g] = sum;
         }
     }
+#pragma unroll
+    for (int i = 0; i < (int)(sizeof(su) / sizeof(su[0])); ++i) {
+        const int u = threadIdx.x + i * NW * kWave;
+        if (u < n_units) {
+            float *d = sl + (size_t)u * 4;  // unit u covers rows 4 * (u % QPR) .. + 3
+            const uint32_t w0 = su[i].x, w1 = su[i].y;
+            d[0] = f16_bits_to_f32((uint16_t)w0);
+            d[1] = f16_bits_to_f32((uint16_t)(w0 >> 16));
+            d[2] = f16_bits_to_f32((uint16_t)w1);
+            d[3] = f16_bits_to_f32((uint16_t)(w1 >> 16));
+        }
+    }
     __syncthreads();
+    float ws[CPW], wb[CPW];
+#pragma unroll
+    for (int jj = 0; jj < CPW; ++jj) {
+        const int c = c0 + jj, g = c / 2;
+        ws[jj] = sl[((size_t)j * G + g) * RW + r];
+        wb[jj] = (c & 1) ? 0.f : sl[(((size_t)top_k + j) * G + g) * RW + r];
+    }
 
     float acc = 0.f;
     if (live) {
@@ -1311,8 +1343,9 @@ static int pow2_at_least(int k) {
 }
 
 static size_t down_token_lds(const moe_layer_t *L, int nw) {
-    const int F = L->dff;
-    return ((size_t)L->top_k * (F + kHPad) + (size_t)L->top_k * (F / kGroup) + (size_t)nw * kWave) * sizeof(float);
+    const int F = L->dff, G = F / kGroup, k = L->top_k;
+    const int rw = kWave / pow2_at_least(k);
+    return ((size_t)k * (F + kHPad) + (size_t)k * G + (size_t)nw * kWave + (size_t)2 * k * G * rw) * sizeof(float);
 }
 
 template <int NW, int CPW, int KP>

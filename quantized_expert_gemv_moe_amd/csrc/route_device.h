@@ -113,7 +113,10 @@ __device__ __forceinline__ bool route_token(const float *__restrict__ row, int n
     return lane < top_k;
 }
 
-// The expert of rank `rank` (0 = largest logit) alone: rank + 1 rounds.
+// The expert of rank `rank` (0 = largest logit) alone: rank + 1 selection
+// rounds.  (An MSB-first radix select over the 32 key bits, whose time does
+// not grow with the rank, measured slower at top-8 of 128: 32 dependent
+// ballot steps against 4.5 rounds on average.)
 template <int PER_LANE>
 __device__ __forceinline__ int route_rank(const float *__restrict__ row, int n_experts, int rank) {
     uint32_t key[PER_LANE];

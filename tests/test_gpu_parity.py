@@ -274,13 +274,20 @@ def test_down_mfma_path(H, F, E, k, B, act):
     (256, 256, 4, 4, "bf16"),       # k = E
     (128, 384, 512, 16, "bf16"),    # 512 experts: routed by the router launch instead
 ])
-def test_decode_layer_one_token_is_bitwise_the_two_call_path(H, F, E, k, act, layout):
-    """moe_decode_layer at B = 1 (gate+up routes for itself) against
-    moe_route_plan + moe_decode_step: outputs, routing and plan identical."""
+@pytest.mark.parametrize("ties", ["none", "ties"])
+def test_decode_layer_one_token_is_bitwise_the_two_call_path(H, F, E, k, act, layout, ties):
+    """moe_decode_layer at B = 1 (gate+up routes for itself, each workgroup
+    selecting only its own rank) against moe_route_plan + moe_decode_step:
+    outputs, routing and plan identical, also with tied logits (ties go to
+    the lower id; -0 equals +0)."""
     wide = (H, E) == (4096, 256)
     sh = Shape(f"l{H}x{F}x{E}", 37, H, F, E, k, act, sidecar=wide, clamp=10.0 if wide else 0.0)
-    log(f"[case] decode_layer B=1 {H}x{F}x{E}x{k} {act} down={layout}")
+    log(f"[case] decode_layer B=1 {H}x{F}x{E}x{k} {act} down={layout} {ties}")
     lg = make_logits(sh, 1, seed=E + k)
+    if ties == "ties":
+        lg[0, ::3] = 1.5                 # a third of the experts tie at the top
+        lg[0, 1::7] = 0.0
+        lg[0, 2::14] = -0.0
     L = layer_for(sh, lg, seed=E + k)
     x = make_x(sh, 1, seed=E + k)
     res = make_x(sh, 1, seed=E + k + 1)
