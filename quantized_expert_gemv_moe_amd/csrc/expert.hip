@@ -100,7 +100,13 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
 // (128 + q[p], 128 + q[p + 4]) by masking into the mantissa of 128.0; the
 // products are exact in fp32.
 __device__ __forceinline__ float dot8_q4_bf16(uint32_t w, const uint32_t *xp, float acc) {
-    const uint32_t M = 0x000F000Fu, B = 0x43004300u;
+    // The mask in an SGPR and the 128.0 pair in a VGPR, opaque to constant
+    // folding: then (w & M) | B is one v_and_or_b32 (gfx9's three-operand
+    // encoding takes no literal, so with both as literals the compiler
+    // emits a separate and + or per nibble pair).
+    uint32_t M, B;
+    asm("s_mov_b32 %0, 0xf000f" : "=s"(M));
+    asm("v_mov_b32 %0, 0x43004300" : "=v"(B));
     acc = dot2_bf16((w & M) | B, xp[0], acc);
     acc = dot2_bf16(((w >> 4) & M) | B, xp[1], acc);
     acc = dot2_bf16(((w >> 8) & M) | B, xp[2], acc);
@@ -503,7 +509,9 @@ __device__ __forceinline__ void q4_pairs(uint32_t w, uint32_t *o) {
 // cancellation between the two terms of the epilogue loses about eight
 // times fewer bits of the fp32 accumulation.
 __device__ __forceinline__ void q4_pairs16(uint32_t w, uint32_t *o) {
-    const uint32_t M = 0x00780078u, B = 0x3F803F80u;
+    uint32_t M, B;  // opaque, for v_and_or_b32 (see dot8_q4_bf16)
+    asm("s_mov_b32 %0, 0x780078" : "=s"(M));
+    asm("v_mov_b32 %0, 0x3f803f80" : "=v"(B));
     o[0] = ((w << 3) & M) | B;
     o[1] = ((w >> 1) & M) | B;
     o[2] = ((w >> 5) & M) | B;
