@@ -425,50 +425,61 @@ __global__ __launch_bounds__(kWave) void gate_up_kernel(GateUpArgs a) {
     gate_up_valu_block<LPR, NV, RI, XBF16>(a, blockIdx.x, blockIdx.y);
 }
 
-// A batch of one token, routed here, on a 1-D grid: block 0 routes in full
-// and writes topk_idx, topk_w and the plan, exactly as moe_route_plan would;
-// every other block (row block, j) finds the token's expert of rank j itself
-// from the logits (j + 1 selection rounds) instead of waiting for a router
-// launch and a plan.  The arithmetic per row is gate_up_kernel's, so h is
-// bitwise the same as on the batched path.
+// A small batch (up to kRouteBlockWaves tokens), routed here, on a 1-D grid
+// of 4-wave blocks.  Block 0 routes every token in full, one wave per
+// token, and writes topk_idx, topk_w and the plan, exactly as
+// moe_route_plan would.  Every wave of the other blocks is one item (token
+// t, rank j, row block): it finds the token's expert of rank j itself from
+// the logits (j + 1 selection rounds) instead of waiting for a router launch
+// and a plan, and computes that expert's rows for that token alone (no
+// deduplication: with so few tokens it would save little and cost a
+// launch).  The arithmetic per row is gate_up_kernel's, so h is bitwise the
+// same as on the batched path.
+constexpr int kRouteBlockWaves = 4;
+
 template <int LPR, int NV, int RI, bool XBF16, int PL>
-__global__ __launch_bounds__(kWave) void gate_up_route_kernel(GateUpArgs a, const float *__restrict__ logits,
-                                                              int *__restrict__ topk_idx,
-                                                              float *__restrict__ topk_w, PlanOut p,
-                                                              int row_blocks) {
+__global__ __launch_bounds__(kRouteBlockWaves * kWave) void gate_up_route_kernel(
+    GateUpArgs a, const float *__restrict__ logits, int *__restrict__ topk_idx, float *__restrict__ topk_w,
+    PlanOut p, int row_blocks, int n_tokens) {
     constexpr int RPI = kWave / LPR;
     constexpr int ROWS_WG = RPI * RI;
-    const int lane = threadIdx.x;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int sl = lane % LPR;
+    const int E = a.n_experts, k = a.top_k;
     if (blockIdx.x == 0) {
-        __shared__ int idx_lds[kWave];
+        __shared__ int idx_lds[kRouteBlockWaves * MOE_MAX_TOP_K];
         __shared__ int cnt[MOE_MAX_EXPERTS], off[MOE_MAX_EXPERTS], uix[MOE_MAX_EXPERTS];
-        int id;
-        float wt;
-        if (route_token<PL>(logits, a.n_experts, a.top_k, &id, &wt)) {
-            topk_idx[lane] = id;
-            topk_w[lane] = wt;
-            idx_lds[lane] = id;
+        if (wave < n_tokens) {
+            int id;
+            float wt;
+            if (route_token<PL>(logits + (size_t)wave * E, E, k, &id, &wt)) {
+                topk_idx[wave * k + lane] = id;
+                topk_w[wave * k + lane] = wt;
+                idx_lds[wave * k + lane] = id;
+            }
         }
-        __builtin_amdgcn_wave_barrier();
-        plan_wave_small<PL>(idx_lds, a.top_k, a.n_experts, p, cnt, off, uix);
+        __syncthreads();
+        if (wave == 0) plan_wave_small<PL>(idx_lds, n_tokens * k, E, p, cnt, off, uix);
         return;
     }
-    const int bb = blockIdx.x - 1;
-    const int rb = bb % row_blocks, j = bb / row_blocks;
+    const int item = (blockIdx.x - 1) * kRouteBlockWaves + wave;
+    if (item >= n_tokens * k * row_blocks) return;
+    const int rb = item % row_blocks, j = (item / row_blocks) % k, t = item / (row_blocks * k);
     const int row0 = rb * ROWS_WG + lane / LPR;
     uint4 xraw0[XBF16 ? NV : 1][4];
     if constexpr (XBF16) {
 #pragma unroll
-        for (int v = 0; v < NV; ++v) load_x32_bf16((const uint16_t *)a.x, 0, (v * LPR + sl) * 32, xraw0[v]);
+        for (int v = 0; v < NV; ++v)
+            load_x32_bf16((const uint16_t *)a.x, (size_t)t * a.hidden, (v * LPR + sl) * 32, xraw0[v]);
     }
-    const int e = route_rank<PL>(logits, a.n_experts, j);
+    const int e = route_rank<PL>(logits + (size_t)t * E, E, j);
     GateUpRows<RI, NV> w;
     load_gate_up_rows<LPR, NV, RI, XBF16>(a, e, row0, sl, w);
     const float sc = a.expert_scale ? a.expert_scale[e] : 1.f;
     GateUpX<LPR, NV, XBF16> x;
-    load_gate_up_x<LPR, NV, XBF16>(a, 0, sl, x, XBF16 ? xraw0 : nullptr);
-    gate_up_token_rows<LPR, NV, RI, XBF16>(a, w, x, j, row0, sc, a.clamp_limit);
+    load_gate_up_x<LPR, NV, XBF16>(a, t, sl, x, XBF16 ? xraw0 : nullptr);
+    gate_up_token_rows<LPR, NV, RI, XBF16>(a, w, x, t * k + j, row0, sc, a.clamp_limit);
 }
 
 // ----------------------------------------------------- gate+up, MFMA tiles
@@ -1241,14 +1252,18 @@ __global__ __launch_bounds__(NW * kWave) void down_token_kernel(const uint4 *__r
     const bool bad = __builtin_amdgcn_ballot_w64(live && (unsigned)e_raw >= (unsigned)n_experts) != 0;
     part[wave * kWave + lane] = acc;
     __syncthreads();
-    if (wave == 0) {  // lane r < RW: row r's k results, then the combine in j order
+    if (wave == 0) {
+        // lane (j, r): expert j's result for row r, the waves' sums in wave order
+        float y = part[lane];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) y += part[w * kWave + lane];
+        part[lane] = y;  // LDS operations of one wave complete in order
+        __builtin_amdgcn_wave_barrier();
+        // lane r < RW: the combine of row r in j order
         float o = 0.f;
         for (int jk = 0; jk < top_k; ++jk) {
-            float y = part[jk * RW + r];
-#pragma unroll
-            for (int w = 1; w < NW; ++w) y += part[w * kWave + jk * RW + r];
             const float wk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wj), jk * RW));
-            o = fmaf(wk, y, o);
+            o = fmaf(wk, part[jk * RW + r], o);
         }
         if (bad) o = __builtin_nanf("");
         if (lane < RW) store_out<BF16>(o, residual, out, (size_t)t * H + m);
@@ -1281,18 +1296,19 @@ static moe_status launch_gate_up(const GateUpArgs &a, bool bf16, int groups_y, h
 // row blocks x top_k.
 template <int LPR, int NV>
 static moe_status launch_gate_up_route(const GateUpArgs &a, bool bf16, int pl, const float *logits,
-                                       int32_t *idx, float *w, const PlanOut &p, hipStream_t s) {
+                                       int32_t *idx, float *w, const PlanOut &p, int n_tokens, hipStream_t s) {
     constexpr int RI = gate_up_ri<LPR, NV>();
     constexpr int rows = (kWave / LPR) * RI;
     const int row_blocks = (a.dff + rows - 1) / rows;
-    const dim3 grid(1 + row_blocks * a.top_k);
+    const int items = n_tokens * a.top_k * row_blocks;
+    const dim3 grid(1 + (items + kRouteBlockWaves - 1) / kRouteBlockWaves), block(kRouteBlockWaves * kWave);
 #define MOE_GUR(PL)                                                                                        \
     if (bf16)                                                                                              \
-        hipLaunchKernelGGL((gate_up_route_kernel<LPR, NV, RI, true, PL>), grid, dim3(kWave), 0, s, a, logits, \
-                           idx, w, p, row_blocks);                                                         \
+        hipLaunchKernelGGL((gate_up_route_kernel<LPR, NV, RI, true, PL>), grid, block, 0, s, a, logits,    \
+                           idx, w, p, row_blocks, n_tokens);                                               \
     else                                                                                                   \
-        hipLaunchKernelGGL((gate_up_route_kernel<LPR, NV, RI, false, PL>), grid, dim3(kWave), 0, s, a, logits, \
-                           idx, w, p, row_blocks);
+        hipLaunchKernelGGL((gate_up_route_kernel<LPR, NV, RI, false, PL>), grid, block, 0, s, a, logits,   \
+                           idx, w, p, row_blocks, n_tokens);
     switch (pl) {
         case 1: MOE_GUR(1) break;
         case 2: MOE_GUR(2) break;
@@ -1703,11 +1719,12 @@ extern "C" moe_status moe_route_gate_up(const moe_layer_t *layer, const float *l
     if ((st = check_x(x)) != MOE_OK) return st;
     hipStream_t stream = (hipStream_t)hip_stream;
     const int pl = per_lane_bucket(layer->n_experts);
-    if (n_tokens > 1 || pl > 4) {  // router + planner launch, then gate+up
+    if (n_tokens > kRouteBlockWaves || pl > 4 || n_tokens * layer->top_k > kWave) {
+        // router + planner launch, then the deduplicated gate+up
         st = moe_route_plan(logits, n_tokens, layer->n_experts, layer->top_k, topk_idx, topk_w, plan, hip_stream);
         if (st != MOE_OK) return st;
         st = enqueue_gate_up(layer, x, n_tokens, plan, workspace, stream);
-    } else {  // one token: a single launch that routes for itself
+    } else {  // a few tokens: one launch that routes for itself
         Geometry gu;
         pick_geometry_gate_up(layer->hidden, &gu);
         const Workspace ws = workspace_layout(layer, n_tokens);
@@ -1715,11 +1732,11 @@ extern "C" moe_status moe_route_gate_up(const moe_layer_t *layer, const float *l
         const GateUpArgs ga{(const uint4 *)layer->gate_q, (const uint4 *)layer->up_q, layer->gate_s,
                             layer->gate_b, layer->up_s, layer->up_b, layer->expert_scale,
                             layer->clamp_limit, x, plan_view(plan), h, layer->hidden, layer->dff,
-                            layer->n_experts, layer->top_k, layer->top_k, INT_MAX};
+                            layer->n_experts, layer->top_k, n_tokens * layer->top_k, INT_MAX};
         const PlanOut po{plan->counts, plan->offsets, plan->sorted_slots, plan->unique_experts, plan->n_unique,
                          (int4 *)plan->work};
         MOE_GEOMETRY_SWITCH(gu, st, launch_gate_up_route, ga, layer->act_dtype == MOE_DTYPE_BF16, pl, logits,
-                            topk_idx, topk_w, po, stream)
+                            topk_idx, topk_w, po, n_tokens, stream)
     }
     if (st != MOE_OK) return st;
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_DEVICE;

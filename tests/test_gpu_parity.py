@@ -274,23 +274,23 @@ def test_down_mfma_path(H, F, E, k, B, act):
     (256, 256, 4, 4, "bf16"),       # k = E
     (128, 384, 512, 16, "bf16"),    # 512 experts: routed by the router launch instead
 ])
-@pytest.mark.parametrize("ties", ["none", "ties"])
-def test_decode_layer_one_token_is_bitwise_the_two_call_path(H, F, E, k, act, layout, ties):
-    """moe_decode_layer at B = 1 (gate+up routes for itself, each workgroup
+@pytest.mark.parametrize("ties,B", [("none", 1), ("ties", 1), ("none", 2), ("ties", 4)])
+def test_decode_layer_few_tokens_is_bitwise_the_two_call_path(H, F, E, k, act, layout, ties, B):
+    """moe_decode_layer at B = 1, 2, 4 (gate+up routes for itself, each wave
     selecting only its own rank) against moe_route_plan + moe_decode_step:
     outputs, routing and plan identical, also with tied logits (ties go to
     the lower id; -0 equals +0)."""
     wide = (H, E) == (4096, 256)
     sh = Shape(f"l{H}x{F}x{E}", 37, H, F, E, k, act, sidecar=wide, clamp=10.0 if wide else 0.0)
-    log(f"[case] decode_layer B=1 {H}x{F}x{E}x{k} {act} down={layout} {ties}")
-    lg = make_logits(sh, 1, seed=E + k)
+    log(f"[case] decode_layer B={B} {H}x{F}x{E}x{k} {act} down={layout} {ties}")
+    lg = make_logits(sh, B, seed=E + k)
     if ties == "ties":
-        lg[0, ::3] = 1.5                 # a third of the experts tie at the top
-        lg[0, 1::7] = 0.0
-        lg[0, 2::14] = -0.0
+        lg[:, ::3] = 1.5                 # a third of the experts tie at the top
+        lg[:, 1::7] = 0.0
+        lg[:, 2::14] = -0.0
     L = layer_for(sh, lg, seed=E + k)
-    x = make_x(sh, 1, seed=E + k)
-    res = make_x(sh, 1, seed=E + k + 1)
+    x = make_x(sh, B, seed=E + k)
+    res = make_x(sh, B, seed=E + k + 1)
     dl = moe.DeviceLayer.from_host(L)
     if layout == "cols":
         dl = dl.pack_down()
@@ -303,7 +303,7 @@ def test_decode_layer_one_token_is_bitwise_the_two_call_path(H, F, E, k, act, la
     assert torch.equal(idx1, idx2) and torch.equal(w1, w2)
     for f in ("counts", "offsets", "unique_experts", "n_unique", "work"):
         assert torch.equal(getattr(plan1, f), getattr(plan2, f)), f
-    assert torch.equal(plan1.sorted_slots[:k], plan2.sorted_slots[:k])
+    assert torch.equal(plan1.sorted_slots[:B * k], plan2.sorted_slots[:B * k])
     assert np.array_equal(host_bits(out1), host_bits(out2))
     ridx, _ = oracle.route_topk(lg, k)
     assert np.array_equal(idx1.cpu().numpy(), ridx)
