@@ -203,7 +203,7 @@ moe_status moe_decode_step(const moe_layer_t *layer, const void *x, int32_t n_to
  * The pages split a decoded token's MoE time into router, expert GEMV and
  * combine (page "perf(moe): attribute the MoE decode gap at the M = 1
  * expert gather", Proposed Solution); at a few tokens each of those is a
- * short, latency-bound kernel.  So a batch of up to 4 tokens (with at most
+ * short, latency-bound kernel.  So a batch of up to 8 tokens (with at most
  * 256 experts and n_tokens * top_k <= 64) takes two launches
  * instead of three or more: every gate+up wave selects its own expert from
  * the logits (one block also writes topk_idx, topk_w and the plan), and one
@@ -217,7 +217,7 @@ moe_status moe_decode_layer(const moe_layer_t *layer, const float *logits, const
 
 /*
  * The first half of moe_decode_layer: routes, plans and writes h into the
- * workspace (one launch for up to 4 tokens, else moe_route_plan and the
+ * workspace (one launch for up to 8 tokens, else moe_route_plan and the
  * gate+up kernels); moe_expert_down_combine with the same workspace, plan,
  * topk_idx and topk_w is the second half.  Same checks as moe_decode_layer
  * (out and residual aside).

@@ -425,9 +425,9 @@ __global__ __launch_bounds__(kWave) void gate_up_kernel(GateUpArgs a) {
     gate_up_valu_block<LPR, NV, RI, XBF16>(a, blockIdx.x, blockIdx.y);
 }
 
-// A small batch (up to kRouteBlockWaves tokens), routed here, on a 1-D grid
-// of 4-wave blocks.  Block 0 routes every token in full, one wave per
-// token, and writes topk_idx, topk_w and the plan, exactly as
+// A small batch (up to BW tokens), routed here, on a 1-D grid of BW-wave
+// blocks.  Block 0 routes every token in full, one wave per token, and
+// writes topk_idx, topk_w and the plan, exactly as
 // moe_route_plan would.  Every wave of the other blocks is one item (token
 // t, rank j, row block): it finds the token's expert of rank j itself from
 // the logits (j + 1 selection rounds) instead of waiting for a router launch
@@ -435,10 +435,10 @@ __global__ __launch_bounds__(kWave) void gate_up_kernel(GateUpArgs a) {
 // deduplication: with so few tokens it would save little and cost a
 // launch).  The arithmetic per row is gate_up_kernel's, so h is bitwise the
 // same as on the batched path.
-constexpr int kRouteBlockWaves = 4;
+constexpr int kRouteMaxTokens = 8;
 
-template <int LPR, int NV, int RI, bool XBF16, int PL>
-__global__ __launch_bounds__(kRouteBlockWaves * kWave) void gate_up_route_kernel(
+template <int LPR, int NV, int RI, bool XBF16, int PL, int BW>
+__global__ __launch_bounds__(BW * kWave) void gate_up_route_kernel(
     GateUpArgs a, const float *__restrict__ logits, int *__restrict__ topk_idx, float *__restrict__ topk_w,
     PlanOut p, int row_blocks, int n_tokens) {
     constexpr int RPI = kWave / LPR;
@@ -448,7 +448,7 @@ __global__ __launch_bounds__(kRouteBlockWaves * kWave) void gate_up_route_kernel
     const int sl = lane % LPR;
     const int E = a.n_experts, k = a.top_k;
     if (blockIdx.x == 0) {
-        __shared__ int idx_lds[kRouteBlockWaves * MOE_MAX_TOP_K];
+        __shared__ int idx_lds[kWave];  // n_tokens * top_k <= 64
         __shared__ int cnt[MOE_MAX_EXPERTS], off[MOE_MAX_EXPERTS], uix[MOE_MAX_EXPERTS];
         if (wave < n_tokens) {
             int id;
@@ -463,7 +463,7 @@ __global__ __launch_bounds__(kRouteBlockWaves * kWave) void gate_up_route_kernel
         if (wave == 0) plan_wave_small<PL>(idx_lds, n_tokens * k, E, p, cnt, off, uix);
         return;
     }
-    const int item = (blockIdx.x - 1) * kRouteBlockWaves + wave;
+    const int item = (blockIdx.x - 1) * BW + wave;
     if (item >= n_tokens * k * row_blocks) return;
     const int rb = item % row_blocks, j = (item / row_blocks) % k, t = item / (row_blocks * k);
     const int row0 = rb * ROWS_WG + lane / LPR;
@@ -1301,18 +1301,24 @@ static moe_status launch_gate_up_route(const GateUpArgs &a, bool bf16, int pl, c
     constexpr int rows = (kWave / LPR) * RI;
     const int row_blocks = (a.dff + rows - 1) / rows;
     const int items = n_tokens * a.top_k * row_blocks;
-    const dim3 grid(1 + (items + kRouteBlockWaves - 1) / kRouteBlockWaves), block(kRouteBlockWaves * kWave);
-#define MOE_GUR(PL)                                                                                        \
+    // 4-wave blocks up to 4 tokens, 8-wave blocks beyond (measured best at
+    // either end)
+    const int bw = n_tokens <= 4 ? 4 : 8;
+    const dim3 grid(1 + (items + bw - 1) / bw), block(bw * kWave);
+#define MOE_GUR(PL, BW)                                                                                    \
     if (bf16)                                                                                              \
-        hipLaunchKernelGGL((gate_up_route_kernel<LPR, NV, RI, true, PL>), grid, block, 0, s, a, logits,    \
+        hipLaunchKernelGGL((gate_up_route_kernel<LPR, NV, RI, true, PL, BW>), grid, block, 0, s, a, logits, \
                            idx, w, p, row_blocks, n_tokens);                                               \
     else                                                                                                   \
-        hipLaunchKernelGGL((gate_up_route_kernel<LPR, NV, RI, false, PL>), grid, block, 0, s, a, logits,   \
+        hipLaunchKernelGGL((gate_up_route_kernel<LPR, NV, RI, false, PL, BW>), grid, block, 0, s, a, logits, \
                            idx, w, p, row_blocks, n_tokens);
-    switch (pl) {
-        case 1: MOE_GUR(1) break;
-        case 2: MOE_GUR(2) break;
-        case 4: MOE_GUR(4) break;
+    switch (pl * 10 + bw / 4) {
+        case 11: MOE_GUR(1, 4) break;
+        case 21: MOE_GUR(2, 4) break;
+        case 41: MOE_GUR(4, 4) break;
+        case 12: MOE_GUR(1, 8) break;
+        case 22: MOE_GUR(2, 8) break;
+        case 42: MOE_GUR(4, 8) break;
         default: return MOE_ERR_UNSUPPORTED;
     }
 #undef MOE_GUR
@@ -1719,7 +1725,7 @@ extern "C" moe_status moe_route_gate_up(const moe_layer_t *layer, const float *l
     if ((st = check_x(x)) != MOE_OK) return st;
     hipStream_t stream = (hipStream_t)hip_stream;
     const int pl = per_lane_bucket(layer->n_experts);
-    if (n_tokens > kRouteBlockWaves || pl > 4 || n_tokens * layer->top_k > kWave) {
+    if (n_tokens > kRouteMaxTokens || pl > 4 || n_tokens * layer->top_k > kWave) {
         // router + planner launch, then the deduplicated gate+up
         st = moe_route_plan(logits, n_tokens, layer->n_experts, layer->top_k, topk_idx, topk_w, plan, hip_stream);
         if (st != MOE_OK) return st;

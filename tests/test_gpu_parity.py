@@ -274,9 +274,9 @@ def test_down_mfma_path(H, F, E, k, B, act):
     (256, 256, 4, 4, "bf16"),       # k = E
     (128, 384, 512, 16, "bf16"),    # 512 experts: routed by the router launch instead
 ])
-@pytest.mark.parametrize("ties,B", [("none", 1), ("ties", 1), ("none", 2), ("ties", 4)])
+@pytest.mark.parametrize("ties,B", [("none", 1), ("ties", 1), ("none", 2), ("ties", 4), ("none", 8)])
 def test_decode_layer_few_tokens_is_bitwise_the_two_call_path(H, F, E, k, act, layout, ties, B):
-    """moe_decode_layer at B = 1, 2, 4 (gate+up routes for itself, each wave
+    """moe_decode_layer at B = 1, 2, 4, 8 (gate+up routes for itself, each wave
     selecting only its own rank) against moe_route_plan + moe_decode_step:
     outputs, routing and plan identical, also with tied logits (ties go to
     the lower id; -0 equals +0)."""
