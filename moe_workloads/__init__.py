@@ -28,6 +28,7 @@ from .gen import (  # noqa: F401
     make_layer,
     make_x,
     make_logits,
+    make_router,
     make_layer_device,
     rng_for,
 )

@@ -3,8 +3,8 @@
 Seeding: every array is drawn from
 ``numpy.random.default_rng(SeedSequence([seed, cfg, layer, stream, index]))``
 with the streams 0 activations, 1 logits, 2 gate, 3 up, 4 down, 5 sidecar,
-6 Zipf rank permutation, 7 sharing set.  The same arguments always give the
-same bytes.
+6 Zipf rank permutation, 7 sharing set, 8 router projection.  The same
+arguments always give the same bytes.
 
 Weight storage (the layout both sides read):
   * ``*_q``  uint32 ``[E][rows][cols/8]``; nibble i of word w holds element
@@ -29,7 +29,7 @@ GROUP = 64
 POISON_F16 = np.uint16(0x7E00)  # fp16 quiet NaN
 
 # streams of the seed sequence
-S_X, S_LOGITS, S_GATE, S_UP, S_DOWN, S_SIDECAR, S_RANK, S_SHARE = range(8)
+S_X, S_LOGITS, S_GATE, S_UP, S_DOWN, S_SIDECAR, S_RANK, S_SHARE, S_ROUTER = range(9)
 
 
 @dataclass(frozen=True)
@@ -178,6 +178,14 @@ def make_x(shape: Shape, n_tokens: int, layer: int = 0, seed: int = 0, scale: fl
     if shape.act == "f32":
         return x
     return bf16_bits_from_f32(x)
+
+
+def make_router(shape: Shape, layer: int = 0, seed: int = 0) -> np.ndarray:
+    """Router projection weights, bf16 bit patterns [E][hidden] drawn from
+    N(0, 1/hidden), so that N(0,1) activations give logits of unit scale."""
+    w = rng_for(seed, shape.cfg, layer, S_ROUTER).standard_normal((shape.n_experts, shape.hidden), np.float32)
+    w *= np.float32(1.0 / np.sqrt(shape.hidden))
+    return bf16_bits_from_f32(w)
 
 
 # ------------------------------------------------------------------- logits

@@ -294,3 +294,28 @@ void orc_residual_bf16(const uint16_t *x, const double *out, size_t n, uint16_t 
         x_next[i] = orc_f64_to_bf16((double)sum);
     }
 }
+
+/* Router projection, the step in front of the router: logits[t][e] =
+ * sum_h x[t][h] * Wr[e][h], with Wr a dense bf16 matrix [n_experts][hidden]
+ * (one row per expert) and x bf16 or fp32 as in the expert block.  Products
+ * and the sum in fp64 (exact products; the sum in h order).  The pages
+ * name the router as one of the per-token decode costs (page "perf(moe):
+ * attribute the MoE decode gap at the M = 1 expert gather", Proposed
+ * Solution step 2) without its form; a dense linear map of the token's
+ * hidden state to one logit per expert is the plain reading. */
+int orc_router_logits(const void *x, int x_is_bf16, int n_tokens, int hidden, int n_experts,
+                      const uint16_t *w_router, double *logits) {
+    if (n_tokens < 0 || hidden <= 0 || n_experts <= 0) return 1;
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int t = 0; t < n_tokens; ++t)
+        for (int e = 0; e < n_experts; ++e) {
+            double acc = 0.0;
+            for (int c = 0; c < hidden; ++c) {
+                const double xv = x_is_bf16 ? orc_bf16_to_f64(((const uint16_t *)x)[(size_t)t * hidden + c])
+                                            : (double)((const float *)x)[(size_t)t * hidden + c];
+                acc += xv * orc_bf16_to_f64(w_router[(size_t)e * hidden + c]);
+            }
+            logits[(size_t)t * n_experts + e] = acc;
+        }
+    return 0;
+}

@@ -67,7 +67,8 @@ def lib():
         L.orc_f16_to_f64.restype = C.c_double
         L.orc_f64_to_bf16.argtypes = [C.c_double]
         L.orc_f64_to_bf16.restype = C.c_uint16
-        for f in ("orc_route_topk", "orc_plan", "orc_decode_step"):
+        L.orc_router_logits.argtypes = [vp, i32, i32, i32, i32, vp, vp]
+        for f in ("orc_route_topk", "orc_plan", "orc_decode_step", "orc_router_logits"):
             getattr(L, f).restype = C.c_int
         _lib = L
     return _lib
@@ -156,6 +157,22 @@ def decode_step(layer, x: np.ndarray, idx: np.ndarray, w: np.ndarray,
     if want_y:
         res.append(y)
     return res[0] if len(res) == 1 else tuple(res)
+
+
+def router_logits(x: np.ndarray, w_router: np.ndarray) -> np.ndarray:
+    """Router projection in fp64: x fp32 [B,H] or bf16 bits [B,H], w_router
+    bf16 bits [E,H] -> logits [B,E] = x . Wr^T."""
+    x_is_bf16 = x.dtype == np.uint16
+    xc = _c(x, np.uint16 if x_is_bf16 else np.float32)
+    wc = _c(w_router, np.uint16)
+    B, H = xc.shape
+    E, H2 = wc.shape
+    if H != H2:
+        raise ValueError("oracle router_logits: hidden sizes differ")
+    out = np.zeros((B, E), np.float64)
+    if lib().orc_router_logits(_p(xc), 1 if x_is_bf16 else 0, B, H, E, _p(wc), _p(out)):
+        raise ValueError("oracle router_logits: bad sizes")
+    return out
 
 
 def dequant(q: np.ndarray, s: np.ndarray, b: np.ndarray) -> np.ndarray:

@@ -18,7 +18,7 @@ import pytest
 from scipy.special import softmax
 
 import bruteforce as bf
-from moe_workloads import SHAPES, Shape, make_layer, make_logits, make_x, quantize_affine4
+from moe_workloads import SHAPES, Shape, make_layer, make_logits, make_router, make_x, quantize_affine4
 from moe_workloads.gen import bf16_bits_from_f32, f32_from_bf16_bits
 from oracle import oracle
 
@@ -417,3 +417,50 @@ def test_residual_step_mirrors_two_roundings():
     o16 = f32_from_bf16_bits(oracle.round_bf16(out))
     ref = bf16_bits_from_f32((f32_from_bf16_bits(x) + o16).astype(np.float32))
     assert np.array_equal(nxt, ref)
+
+
+# ------------------------------------------------------ router projection
+# Pins of oracle.router_logits (the step in front of the router): an
+# independent numpy product, one-hot and single-entry closed forms, and the
+# fp32 / bf16 activation paths agreeing on bf16-representable values.
+
+def test_router_logits_match_an_independent_float64_product():
+    sh = Shape("rp", 120, 384, 64, 40, 4, "bf16")
+    x = make_x(sh, 5, seed=30)
+    wr = make_router(sh, seed=30)
+    got = oracle.router_logits(x, wr)
+    ref = f32_from_bf16_bits(x).astype(np.float64) @ f32_from_bf16_bits(wr).astype(np.float64).T
+    assert got.shape == (5, 40)
+    assert np.allclose(got, ref, rtol=1e-12, atol=1e-12)
+    assert 0.5 < got.std() < 2.0  # unit-scale logits by construction
+
+
+def test_router_logits_one_hot_activation_reads_a_weight_column():
+    sh = Shape("rp1", 121, 128, 64, 12, 2, "bf16")
+    wr = make_router(sh, seed=31)
+    x = np.zeros((3, 128), np.uint16)
+    for t, c in enumerate((0, 77, 127)):
+        x[t, c] = 0x3F80  # bf16 1.0
+    got = oracle.router_logits(x, wr)
+    for t, c in enumerate((0, 77, 127)):
+        assert np.array_equal(got[t], f32_from_bf16_bits(wr[:, c]).astype(np.float64))
+
+
+def test_router_logits_single_entry_rows_scale_one_activation():
+    rng = np.random.default_rng(32)
+    x = rng.standard_normal((4, 96)).astype(np.float32)
+    wr = np.zeros((6, 96), np.uint16)
+    cols = [3, 3, 50, 95, 0, 17]
+    pows = [0, 1, -2, 3, -1, 2]
+    for e, (c, p) in enumerate(zip(cols, pows)):
+        wr[e, c] = bf16_bits_from_f32(np.array([2.0 ** p], np.float32))[0]
+    got = oracle.router_logits(x, wr)
+    for e, (c, p) in enumerate(zip(cols, pows)):
+        assert np.array_equal(got[:, e], x[:, c].astype(np.float64) * 2.0 ** p)
+
+
+def test_router_logits_fp32_and_bf16_activations_agree():
+    sh = Shape("rp2", 122, 256, 64, 16, 2, "bf16")
+    xb = make_x(sh, 3, seed=33)
+    wr = make_router(sh, seed=33)
+    assert np.array_equal(oracle.router_logits(xb, wr), oracle.router_logits(f32_from_bf16_bits(xb), wr))
