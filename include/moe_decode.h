@@ -162,6 +162,22 @@ moe_status moe_route_plan(const float *logits, int32_t n_tokens, int32_t n_exper
                           int32_t *topk_idx, float *topk_w, const moe_plan_t *plan,
                           void *hip_stream);
 
+/*
+ * Router projection, the step in front of the router: logits[t][e] =
+ * sum_h x[t][h] * w_router[e][h] (the pages name the router as one of the
+ * per-token decode costs: page "perf(moe): attribute the MoE decode gap at
+ * the M = 1 expert gather", Proposed Solution step 2).
+ *   x         [n_tokens][hidden], act_dtype (bf16 or fp32), 16-byte aligned
+ *   w_router  bf16 bits [n_experts][hidden], 16-byte aligned
+ *   logits    fp32 [n_tokens][n_experts], the router's input
+ * Products exact, fp32 accumulation in a fixed order.  MOE_ERR_UNSUPPORTED
+ * when hidden has no lane geometry (hidden/8 must be a power of two up to 64
+ * times 1..8) or n_experts > MOE_MAX_EXPERTS; n_tokens == 0 launches
+ * nothing.  Asynchronous on hip_stream.
+ */
+moe_status moe_router_logits(const void *x, int32_t n_tokens, int32_t hidden, moe_dtype act_dtype,
+                             const uint16_t *w_router, int32_t n_experts, float *logits, void *hip_stream);
+
 /* Bytes of device workspace moe_decode_step needs for up to max_tokens
  * tokens of this layer's shape (0 if the layer is invalid). */
 size_t moe_workspace_size(const moe_layer_t *layer, int32_t max_tokens);

@@ -32,6 +32,7 @@ from ._lib import (  # noqa: F401
     library_path,
     route_plan,
     route_topk,
+    router_logits,
     status_str,
     workspace_size,
 )

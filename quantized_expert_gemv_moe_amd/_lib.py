@@ -49,7 +49,8 @@ class PlanStruct(C.Structure):
 
 _lib = None
 
-EXPORTS = ("moe_route_topk", "moe_expert_plan", "moe_route_plan", "moe_workspace_size", "moe_decode_step",
+EXPORTS = ("moe_router_logits", "moe_route_topk", "moe_expert_plan", "moe_route_plan", "moe_workspace_size",
+           "moe_decode_step",
            "moe_decode_layer", "moe_route_gate_up", "moe_expert_gate_up", "moe_expert_down_combine", "moe_pack_down",
            "moe_layer_check", "moe_status_str", "moe_abi_version")
 
@@ -69,6 +70,8 @@ def lib() -> C.CDLL:
                 "or python -m quantized_expert_gemv_moe_amd.build")
         L = C.CDLL(path)
         vp, i32 = C.c_void_p, C.c_int32
+        L.moe_router_logits.argtypes = [vp, i32, i32, C.c_int, vp, i32, vp, vp]
+        L.moe_router_logits.restype = C.c_int
         L.moe_route_topk.argtypes = [vp, i32, i32, i32, vp, vp, vp]
         L.moe_route_topk.restype = C.c_int
         L.moe_expert_plan.argtypes = [vp, i32, i32, i32, C.POINTER(PlanStruct), vp]
@@ -218,6 +221,25 @@ class Plan:
 
 
 # ------------------------------------------------------------- entry points
+def router_logits(x: torch.Tensor, w_router: torch.Tensor, logits: Optional[torch.Tensor] = None,
+                  stream=None) -> torch.Tensor:
+    """moe_router_logits: x [B,H] (bf16 or fp32), w_router bf16 [E,H] -> fp32 logits [B,E]."""
+    if x.dim() != 2 or not x.is_contiguous() or x.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("x must be a contiguous bf16 or fp32 [B, H] tensor")
+    if w_router.dim() != 2 or not w_router.is_contiguous() or w_router.dtype != torch.bfloat16:
+        raise ValueError("w_router must be a contiguous bf16 [E, H] tensor")
+    B, H = x.shape
+    E = w_router.shape[0]
+    if w_router.shape[1] != H:
+        raise ValueError("x and w_router disagree on hidden")
+    if logits is None:
+        logits = torch.empty((B, E), dtype=torch.float32, device=x.device)
+    act = MOE_DTYPE_BF16 if x.dtype == torch.bfloat16 else MOE_DTYPE_F32
+    _check(lib().moe_router_logits(_ptr(x), B, H, act, _ptr(w_router), E, _ptr(logits), _stream(stream)),
+           "moe_router_logits")
+    return logits
+
+
 def route_topk(logits: torch.Tensor, top_k: int, idx: Optional[torch.Tensor] = None,
                w: Optional[torch.Tensor] = None, stream=None):
     """moe_route_topk: fp32 logits [B,E] -> (int32 idx [B,k], fp32 w [B,k])."""

@@ -210,6 +210,23 @@ def test_pack_down_validation_before_any_launch():
     assert f(C.byref(src), D, D + 16, D + 0x20000000, None) == moe.MOE_ERR_INVALID_ARG
 
 
+def test_router_logits_validation_before_any_launch():
+    f = moe.lib().moe_router_logits
+    X, W, O = FAKE + 0x1000000, FAKE + 0x2000000, FAKE + 0x3000000
+    BF, F32 = moe.MOE_DTYPE_BF16, moe.MOE_DTYPE_F32
+    assert f(X, 0, 2048, BF, W, 128, O, None) == moe.MOE_OK       # empty batch
+    assert f(X, -1, 2048, BF, W, 128, O, None) == moe.MOE_ERR_INVALID_ARG
+    assert f(X, 1, 2048, 5, W, 128, O, None) == moe.MOE_ERR_INVALID_ARG
+    assert f(None, 1, 2048, BF, W, 128, O, None) == moe.MOE_ERR_INVALID_ARG
+    assert f(X, 1, 2048, BF, None, 128, O, None) == moe.MOE_ERR_INVALID_ARG
+    assert f(X, 1, 2048, BF, W, 128, None, None) == moe.MOE_ERR_INVALID_ARG
+    assert f(X + 8, 1, 2048, BF, W, 128, O, None) == moe.MOE_ERR_INVALID_ARG
+    assert f(X, 1, 2048, F32, W + 4, 128, O, None) == moe.MOE_ERR_INVALID_ARG
+    assert f(X, 1, 2044, BF, W, 128, O, None) == moe.MOE_ERR_UNSUPPORTED  # hidden % 8
+    assert f(X, 1, 8 * 9 * 64, BF, W, 128, O, None) == moe.MOE_ERR_UNSUPPORTED  # 576 chunks: no geometry
+    assert f(X, 1, 2048, BF, W, 2048, O, None) == moe.MOE_ERR_UNSUPPORTED  # > MOE_MAX_EXPERTS
+
+
 def test_binding_raises_on_error_status():
     with pytest.raises(moe.MoeError) as ei:
         _lib._check(moe.MOE_ERR_UNSUPPORTED, "probe")

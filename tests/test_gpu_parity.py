@@ -12,7 +12,7 @@ import torch
 
 import quantized_expert_gemv_moe_amd as moe
 from gpu_helpers import GpuRun, check_against_oracle, dev_x, host_bits, layer_for, log, rel_l2
-from moe_workloads import SHAPES, Shape, make_layer, make_logits, make_x
+from moe_workloads import SHAPES, Shape, make_layer, make_logits, make_router, make_x
 from oracle import oracle
 
 pytestmark = pytest.mark.gpu
@@ -449,3 +449,51 @@ def test_empty_batch_decode_step_is_a_no_op():
     moe.decode_step(dl, torch.zeros((0, sh.hidden), device="cuda"), torch.zeros((0, 2), dtype=torch.int32, device="cuda"),
                     torch.zeros((0, 2), device="cuda"), plan, out=out, workspace=torch.empty(256, dtype=torch.uint8, device="cuda"))
     torch.cuda.synchronize()
+
+
+# -------------------------------------------------------- router projection
+@pytest.mark.parametrize("H,E,B,act", [
+    (2048, 128, 1, "bf16"),    # the decode layer: 64 lanes x 4 chunks per row
+    (2048, 128, 32, "bf16"),
+    (4096, 256, 4, "bf16"),    # 64 x 8
+    (256, 8, 3, "f32"),        # the toy layer: 32 lanes x 1 chunk, fp32 activations
+    (384, 37, 5, "bf16"),      # 16 x 3; E not a multiple of the rows per wave
+    (8, 5, 2, "f32"),          # one chunk per row
+    (3072, 64, 2, "f32"),      # 64 x 6
+])
+def test_router_logits_match_oracle(H, E, B, act):
+    sh = Shape(f"rp{H}x{E}", 39, H, 64, E, 1, act)
+    x = make_x(sh, B, seed=H + E)
+    wr = make_router(sh, seed=H + E)
+    xt = dev_x(x)
+    wt = torch.from_numpy(wr.view(np.int16)).cuda().view(torch.bfloat16)
+    got = moe.router_logits(xt, wt)
+    torch.cuda.synchronize()
+    ref = oracle.router_logits(x, wr)
+    xf = oracle.bf16_to_f64(x) if x.dtype == np.uint16 else x.astype(np.float64)
+    mag = np.abs(xf) @ np.abs(oracle.bf16_to_f64(wr)).T
+    err = np.abs(got.cpu().numpy().astype(np.float64) - ref)
+    log(f"[parity] router logits {H}x{E} B{B} {act}: max err/|x||w| = {(err / mag).max():.3g}")
+    # exact products, fp32 sums of H terms: far below 1e-5 of sum |x w|; one
+    # dropped or doubled term is ~1/H of it
+    assert np.all(err <= 1e-5 * mag + 1e-30)
+    again = moe.router_logits(xt, wt)
+    one = moe.router_logits(xt[B - 1:B].contiguous(), wt)
+    torch.cuda.synchronize()
+    assert torch.equal(got, again)
+    assert torch.equal(one[0], got[B - 1])  # a token's logits do not depend on the batch
+
+
+@pytest.mark.parametrize("name,B", [("decode", 1), ("cohort", 8), ("stack", 32)])
+def test_layer_routed_from_the_projection(name, B):
+    """x -> moe_router_logits -> moe_decode_layer, against the oracle routing
+    the same fp32 logits."""
+    sh = SHAPES[name]
+    x = make_x(sh, B, seed=40)
+    wr = make_router(sh, seed=40)
+    lg = moe.router_logits(dev_x(x), torch.from_numpy(wr.view(np.int16)).cuda().view(torch.bfloat16))
+    torch.cuda.synchronize()
+    lg_np = lg.cpu().numpy()
+    L = layer_for(sh, lg_np, seed=40)
+    run = GpuRun(L, x, lg_np, cols=True)
+    check_against_oracle(L, x, lg_np, run, f"projected {name} B{B}")
