@@ -203,6 +203,25 @@ def run_kernel_pass(rot, reps=4):
     return res
 
 
+def run_router_projection(rot, reps=4):
+    """The router projection in front of the router (moe_router_logits),
+    timed alone on R distinct bf16 weight matrices; not part of the step,
+    whose router starts from logits."""
+    import torch
+
+    sh, R = rot.shape, rot.R
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(1234)
+    wr = [(torch.randn((sh.n_experts, sh.hidden), device="cuda", generator=gen) / math.sqrt(sh.hidden))
+          .to(torch.bfloat16) for _ in range(R)]
+    lg = [torch.empty((rot.B, sh.n_experts), dtype=torch.float32, device="cuda") for _ in range(R)]
+    g = capture(lambda: [rot.moe.router_logits(rot.x[i], wr[i], lg[i]) for i in range(R)])
+    g.replay()
+    t = time_graph(g, reps) / (reps * R)
+    nbytes = sh.n_experts * sh.hidden * 2
+    return {"us": t * 1e6, "gbps": nbytes / t / 1e9, "bytes_per_launch": nbytes}
+
+
 def unique_bytes(shape, n_unique):
     return n_unique * 3 * shape.hidden * shape.dff * BYTES_PER_WEIGHT
 
@@ -348,6 +367,9 @@ def main():
                  else "gate_up_route_kernel" if B == 1 else "route_plan_kernel + gate_up kernels")
     traffic = counted_traffic(args.workload, gu_kernel)
 
+    rp = run_router_projection(rot)
+    log(f"[bench] router projection (next row): {rp['us']:.2f} us per launch, {rp['gbps']:.0f} GB/s")
+
     ladder = []
     if not args.no_ladder and sh.name in ("decode", "cohort", "stack"):
         for wl in ("cohort4", "cohort8", "stack32"):
@@ -395,6 +417,7 @@ def main():
                      "bytes_per_launch": gu_bytes, "us_per_launch": kt["route_gate_up"] * 1e6},
         "kernels": kernels,
         "ladder": ladder,
+        "next_rows": {"router_projection": rp},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
