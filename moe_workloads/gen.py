@@ -3,8 +3,8 @@
 Seeding: every array is drawn from
 ``numpy.random.default_rng(SeedSequence([seed, cfg, layer, stream, index]))``
 with the streams 0 activations, 1 logits, 2 gate, 3 up, 4 down, 5 sidecar,
-6 Zipf rank permutation, 7 sharing set, 8 router projection.  The same
-arguments always give the same bytes.
+6 Zipf rank permutation, 7 sharing set, 8 router projection, 9 down
+sidecar.  The same arguments always give the same bytes.
 
 Weight storage (the layout both sides read):
   * ``*_q``  uint32 ``[E][rows][cols/8]``; nibble i of word w holds element
@@ -29,7 +29,7 @@ GROUP = 64
 POISON_F16 = np.uint16(0x7E00)  # fp16 quiet NaN
 
 # streams of the seed sequence
-S_X, S_LOGITS, S_GATE, S_UP, S_DOWN, S_SIDECAR, S_RANK, S_SHARE, S_ROUTER = range(9)
+S_X, S_LOGITS, S_GATE, S_UP, S_DOWN, S_SIDECAR, S_RANK, S_SHARE, S_ROUTER, S_DOWN_SIDECAR = range(10)
 
 
 @dataclass(frozen=True)
@@ -45,6 +45,8 @@ class Shape:
     act: str  # "f32" or "bf16"
     sidecar: bool = False
     clamp: float = 0.0
+    activation: str = "swiglu"   # or "geglu"
+    down_sidecar: bool = False   # a per-expert fp32 scale of the down output
 
 
 SHAPES: Dict[str, Shape] = {
@@ -123,6 +125,8 @@ class Layer:
     sidecar: Optional[np.ndarray]  # fp32 [E] or None
     clamp: float
     materialised: np.ndarray = field(default=None)  # bool [E]
+    activation: str = "swiglu"
+    down_sidecar: Optional[np.ndarray] = None  # fp32 [E] or None
 
 
 def _empty_layer(shape: Shape) -> Layer:
@@ -141,6 +145,7 @@ def _empty_layer(shape: Shape) -> Layer:
         sidecar=None,
         clamp=shape.clamp,
         materialised=np.zeros(E, bool),
+        activation=shape.activation,
     )
 
 
@@ -167,6 +172,8 @@ def make_layer(shape: Shape, layer: int = 0, experts: Optional[Iterable[int]] = 
         L.materialised[e] = True
     if shape.sidecar:
         L.sidecar = rng_for(seed, shape.cfg, layer, S_SIDECAR).uniform(0.5, 1.5, E).astype(np.float32)
+    if shape.down_sidecar:
+        L.down_sidecar = rng_for(seed, shape.cfg, layer, S_DOWN_SIDECAR).uniform(0.5, 1.5, E).astype(np.float32)
     return L
 
 

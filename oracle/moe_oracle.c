@@ -182,6 +182,8 @@ typedef struct {
     const uint32_t *gate_q, *up_q, *down_q;
     const uint16_t *gate_s, *gate_b, *up_s, *up_b, *down_s, *down_b;
     const float *sidecar;       /* [E] or NULL */
+    int32_t activation;         /* 0: SwiGLU, 1: GeGLU (tanh-form GELU) */
+    const float *down_sidecar;  /* [E] or NULL: y *= down_sidecar[e] */
 } orc_layer;
 
 static double orc_x(const orc_layer *L, const void *x, int t, int c) {
@@ -196,8 +198,18 @@ static double orc_clip(double v, double lim) {
     return v;
 }
 
-/* Intermediate h (length dff) of expert e for token t: SiLU(g) * u after the
- * optional sidecar (first) and clamp (second). */
+/* GELU in the tanh form, 0.5 g (1 + tanh(sqrt(2/pi) (g + 0.044715 g^3))):
+ * the GeGLU variant the pages list as a next family (page "perf(moe):
+ * batched decode scales 1.55x against 3.25x on dense", Implementation
+ * Notes) gives no formula; this is the form of the gemma checkpoints it
+ * names. */
+static double orc_gelu(double g) {
+    const double c = sqrt(2.0 / 3.14159265358979323846);
+    return 0.5 * g * (1.0 + tanh(c * (g + 0.044715 * g * g * g)));
+}
+
+/* Intermediate h (length dff) of expert e for token t: SiLU(g) * u (or
+ * GELU(g) * u) after the optional sidecar (first) and clamp (second). */
 static void orc_expert_h(const orc_layer *L, const void *x, int t, int e, double *h) {
     const int H = L->hidden, F = L->dff;
     const size_t gq = (size_t)e * F * (H / 8), gs = (size_t)e * F * (H / ORC_GROUP);
@@ -217,7 +229,7 @@ static void orc_expert_h(const orc_layer *L, const void *x, int t, int e, double
             g = orc_clip(g, L->clamp_limit);
             u = orc_clip(u, L->clamp_limit);
         }
-        h[n] = g / (1.0 + exp(-g)) * u;
+        h[n] = (L->activation == 1 ? orc_gelu(g) : g / (1.0 + exp(-g))) * u;
     }
 }
 
@@ -229,7 +241,7 @@ static void orc_expert_down(const orc_layer *L, int e, const double *h, double *
         double acc = 0.0;
         for (int n = 0; n < F; ++n)
             acc += orc_weight(L->down_q + dq, L->down_s + ds, L->down_b + ds, F, m, n) * h[n];
-        y[m] = acc;
+        y[m] = L->down_sidecar ? acc * (double)L->down_sidecar[e] : acc;
     }
 }
 

@@ -46,6 +46,7 @@ class _Layer(C.Structure):
         ("gate_s", C.c_void_p), ("gate_b", C.c_void_p), ("up_s", C.c_void_p), ("up_b", C.c_void_p),
         ("down_s", C.c_void_p), ("down_b", C.c_void_p),
         ("sidecar", C.c_void_p),
+        ("activation", C.c_int32), ("down_sidecar", C.c_void_p),
     ]
 
 
@@ -118,12 +119,18 @@ def _layer_struct(layer, x_is_bf16: bool, keep: list) -> _Layer:
     for name in ("gate_s", "gate_b", "up_s", "up_b", "down_s", "down_b"):
         arrs[name] = _c(getattr(layer, name), np.uint16)
     sc = None if layer.sidecar is None else _c(layer.sidecar, np.float32)
+    dsc = getattr(layer, "down_sidecar", None)
+    dsc = None if dsc is None else _c(dsc, np.float32)
     keep.extend(arrs.values())
-    if sc is not None:
-        keep.append(sc)
+    keep.extend(a for a in (sc, dsc) if a is not None)
+    act = getattr(layer, "activation", "swiglu")
+    if act not in ("swiglu", "geglu"):
+        raise ValueError(f"oracle: unknown activation {act}")
     st = _Layer(hidden=sh.hidden, dff=sh.dff, n_experts=sh.n_experts, top_k=sh.top_k,
                 x_is_bf16=1 if x_is_bf16 else 0, clamp_limit=float(layer.clamp or 0.0),
-                sidecar=None if sc is None else sc.ctypes.data)
+                sidecar=None if sc is None else sc.ctypes.data,
+                activation=1 if act == "geglu" else 0,
+                down_sidecar=None if dsc is None else dsc.ctypes.data)
     for name, a in arrs.items():
         setattr(st, name, a.ctypes.data)
     return st

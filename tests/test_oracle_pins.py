@@ -464,3 +464,62 @@ def test_router_logits_fp32_and_bf16_activations_agree():
     xb = make_x(sh, 3, seed=33)
     wr = make_router(sh, seed=33)
     assert np.array_equal(oracle.router_logits(xb, wr), oracle.router_logits(f32_from_bf16_bits(xb), wr))
+
+
+# ---------------------------------------------- GeGLU and the down sidecar
+# GeGLU reads GELU in the tanh form.  It is pinned without retyping it: it
+# stays within 5e-4 of the exact x * Phi(x) (scipy's normal CDF), it is
+# 0 at 0, and with the same weights its h differs from SwiGLU's exactly as
+# GELU(g) / SiLU(g) does, per element.
+
+def _geglu_layer(down_sidecar=False, activation="geglu", cfg=140):
+    sh = Shape("gg", cfg, 128, 64, 3, 1, "f32", activation=activation, down_sidecar=down_sidecar)
+    return sh, make_layer(sh, seed=41)
+
+
+def test_geglu_h_is_the_normal_cdf_gelu_within_the_tanh_form_error():
+    from scipy.special import ndtr
+    sh, L = _geglu_layer()
+    x = make_x(sh, 1, seed=41) * np.float32(40.0)  # spread g over about +-6
+    idx = np.array([[1]], np.int32)
+    _, h = oracle.decode_step(L, x, idx, np.ones((1, 1)), want_h=True)
+    q = bf.dequant_dense(L.gate_q[1], L.gate_s[1], L.gate_b[1])
+    uq = bf.dequant_dense(L.up_q[1], L.up_s[1], L.up_b[1])
+    g = q @ x[0].astype(np.float64)
+    u = uq @ x[0].astype(np.float64)
+    assert np.abs(g).max() > 3.0
+    exact = g * ndtr(g) * u
+    assert np.all(np.abs(h[0] - exact) <= 5e-4 * np.abs(u) + 1e-15)
+    assert np.abs(h[0] - exact).max() > 0  # the tanh form, not the exact one
+
+
+def test_geglu_and_swiglu_differ_only_in_the_gate_function():
+    sh_g, Lg = _geglu_layer()
+    _, Ls = _geglu_layer(activation="swiglu")
+    x = make_x(sh_g, 2, seed=42)
+    idx = np.array([[0], [2]], np.int32)
+    _, hg = oracle.decode_step(Lg, x, idx, np.ones((2, 1)), want_h=True)
+    _, hs = oracle.decode_step(Ls, x, idx, np.ones((2, 1)), want_h=True)
+    for t, e in enumerate((0, 2)):
+        g = bf.dequant_dense(Lg.gate_q[e], Lg.gate_s[e], Lg.gate_b[e]) @ x[t].astype(np.float64)
+        silu = g / (1.0 + np.exp(-g))
+        nz = np.abs(silu) > 1e-30
+        # h_geglu / h_swiglu = gelu(g) / silu(g); both sides from the same u
+        ratio = hg[t][nz] / hs[t][nz]
+        from scipy.special import ndtr
+        assert np.allclose(ratio, g[nz] * ndtr(g[nz]) / silu[nz], rtol=2e-2, atol=1e-3)
+
+
+def test_down_sidecar_scales_each_expert_output():
+    sh, L = _geglu_layer(down_sidecar=True, activation="swiglu")
+    x = make_x(sh, 2, seed=43)
+    idx = np.array([[0], [2]], np.int32)
+    w = np.array([[1.0], [1.0]])
+    L.down_sidecar = np.array([2.0, 0.5, 0.25], np.float32)
+    out, y = oracle.decode_step(L, x, idx, w, want_y=True)
+    dsc = L.down_sidecar
+    L.down_sidecar = None
+    out0, y0 = oracle.decode_step(L, x, idx, w, want_y=True)
+    assert np.array_equal(y[0], 2.0 * y0[0]) and np.array_equal(y[1], 0.25 * y0[1])
+    assert np.array_equal(out, np.stack([2.0 * out0[0], 0.25 * out0[1]]))
+    assert dsc is not None
