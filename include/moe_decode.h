@@ -61,6 +61,9 @@ typedef enum { MOE_DTYPE_F32 = 0, MOE_DTYPE_BF16 = 1 } moe_dtype;
 /* Storage of the down projection (see moe_layer_t and moe_pack_down). */
 typedef enum { MOE_DOWN_ROWS = 0, MOE_DOWN_COLS = 1 } moe_down_layout;
 
+/* Gated activation of the expert MLP (see moe_layer_t). */
+typedef enum { MOE_ACT_SWIGLU = 0, MOE_ACT_GEGLU = 1 } moe_activation;
+
 /* Limits enforced by validation. */
 #define MOE_MAX_EXPERTS 1024
 #define MOE_MAX_TOP_K 16
@@ -95,6 +98,18 @@ typedef enum { MOE_DOWN_ROWS = 0, MOE_DOWN_COLS = 1 } moe_down_layout;
  * page "perf(moe): attribute ...", Problem / Background).  `clamp_limit`
  * (0 = none) clips gate and up pre-activations to [-L, L] after the sidecar
  * and before SiLU*up (the clamp stage named on the same page).
+ *
+ * `activation` is MOE_ACT_SWIGLU (h = silu(g) * u) or MOE_ACT_GEGLU
+ * (h = gelu(g) * u with the tanh form 0.5 g (1 + tanh(sqrt(2/pi)
+ * (g + 0.044715 g^3)))), the GeGLU variant of the fused kernel that page
+ * "perf(moe): batched decode scales 1.55x against 3.25x on dense" lists
+ * among its kernels (Implementation Notes); the pages give no GELU formula,
+ * the tanh form is the one of the gemma checkpoints that kernel serves.
+ * `down_scale` (optional, NULL = none) is one fp32 factor per expert that
+ * multiplies that expert's down-projection output y before the weighted
+ * combine: the second of the "both sidecars" that page "perf(moe):
+ * attribute ..." names (Problem / Background), which it does not define
+ * further.  Both are appended after the v4 fields.
  */
 typedef struct {
     int32_t hidden;      /* H, multiple of 64 */
@@ -109,6 +124,8 @@ typedef struct {
     const uint32_t *gate_q, *up_q, *down_q;
     const uint16_t *gate_s, *gate_b, *up_s, *up_b, *down_s, *down_b;
     const float *expert_scale; /* [E] or NULL */
+    const float *down_scale;   /* [E] or NULL */
+    int32_t activation;        /* moe_activation */
 } moe_layer_t;
 
 /*
@@ -195,8 +212,10 @@ size_t moe_workspace_size(const moe_layer_t *layer, int32_t max_tokens);
  *   g = Wg[e] x_t, u = Wu[e] x_t   (fp32 accumulation)
  *   g, u *= expert_scale[e]        (if given)
  *   g, u = clip(g, u, -L, L)       (if clamp_limit > 0)
- *   h = silu(g) * u                (fp32, never rounded)
+ *   h = silu(g) * u                (gelu(g) * u for MOE_ACT_GEGLU;
+ *                                   fp32, never rounded)
  *   y = Wd[e] h                    (fp32)
+ *   y *= down_scale[e]             (if given)
  *   o_t = sum_{j<k} topk_w[t][j] * y_{t,j}, in j order, rounded once to
  *         act_dtype (round to nearest even)
  *   out_t = o_t, or with a residual: act(residual_t + o_t) in fp32

@@ -7,6 +7,8 @@ library; the first call does, and raises if it has not been built.
 
 from ._lib import (  # noqa: F401
     EXPORTS,
+    MOE_ACT_GEGLU,
+    MOE_ACT_SWIGLU,
     MOE_DOWN_COLS,
     MOE_DOWN_ROWS,
     MOE_DTYPE_BF16,

@@ -20,6 +20,8 @@ from . import build as _build
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_DEVICE = range(5)
 MOE_DTYPE_F32, MOE_DTYPE_BF16 = 0, 1
 MOE_DOWN_ROWS, MOE_DOWN_COLS = 0, 1
+MOE_ACT_SWIGLU, MOE_ACT_GEGLU = 0, 1
+_ACTIVATIONS = {"swiglu": MOE_ACT_SWIGLU, "geglu": MOE_ACT_GEGLU}
 MOE_MAX_EXPERTS = 1024
 MOE_MAX_TOP_K = 16
 
@@ -38,7 +40,7 @@ class LayerStruct(C.Structure):
         ("gate_q", C.c_void_p), ("up_q", C.c_void_p), ("down_q", C.c_void_p),
         ("gate_s", C.c_void_p), ("gate_b", C.c_void_p), ("up_s", C.c_void_p), ("up_b", C.c_void_p),
         ("down_s", C.c_void_p), ("down_b", C.c_void_p),
-        ("expert_scale", C.c_void_p),
+        ("expert_scale", C.c_void_p), ("down_scale", C.c_void_p), ("activation", C.c_int32),
     ]
 
 
@@ -140,28 +142,37 @@ class DeviceLayer:
     tensors: dict
     struct: LayerStruct
     down_layout: int = MOE_DOWN_ROWS
+    activation: str = "swiglu"
 
     @staticmethod
     def from_tensors(hidden, dff, n_experts, top_k, act: str, clamp_limit: float, tensors: dict,
-                     down_layout: int = MOE_DOWN_ROWS):
+                     down_layout: int = MOE_DOWN_ROWS, activation: str = "swiglu"):
         """``tensors``: gate_q/up_q/down_q (int32 or uint32 words), *_s/*_b (fp16 bits as
-        int16/uint16), optional 'sidecar' (fp32 [E]); all on the same device."""
+        int16/uint16), optional 'sidecar' (fp32 [E], on gate and up) and 'down_sidecar'
+        (fp32 [E], on the down output); all on the same device.  ``activation`` is
+        "swiglu" or "geglu"."""
+        if activation not in _ACTIVATIONS:
+            raise ValueError(f"activation must be one of {sorted(_ACTIVATIONS)}")
         t = {k: v for k, v in tensors.items() if v is not None}
         for k, v in t.items():
             if not v.is_contiguous():
                 raise ValueError(f"{k} must be contiguous")
         st = LayerStruct(hidden=hidden, dff=dff, n_experts=n_experts, top_k=top_k, bits=4,
                          group_size=64, act_dtype=MOE_DTYPE_BF16 if act == "bf16" else MOE_DTYPE_F32,
-                         clamp_limit=float(clamp_limit), down_layout=down_layout)
+                         clamp_limit=float(clamp_limit), down_layout=down_layout,
+                         activation=_ACTIVATIONS[activation])
         for name in ("gate_q", "up_q", "down_q", "gate_s", "gate_b", "up_s", "up_b", "down_s", "down_b"):
             setattr(st, name, t[name].data_ptr())
         sc = t.get("sidecar")
         st.expert_scale = None if sc is None else sc.data_ptr()
-        return DeviceLayer(hidden, dff, n_experts, top_k, st.act_dtype, float(clamp_limit), t, st, down_layout)
+        ds = t.get("down_sidecar")
+        st.down_scale = None if ds is None else ds.data_ptr()
+        return DeviceLayer(hidden, dff, n_experts, top_k, st.act_dtype, float(clamp_limit), t, st, down_layout,
+                           activation)
 
     def pack_down(self, stream=None, free_rows: bool = False) -> "DeviceLayer":
         """A copy of this layer whose down projection is regrouped to MOE_DOWN_COLS
-        (moe_pack_down); gate/up and the sidecar are shared."""
+        (moe_pack_down); gate/up and the sidecars are shared."""
         if self.down_layout != MOE_DOWN_ROWS:
             raise ValueError("the down projection is already packed")
         t = dict(self.tensors)
@@ -175,7 +186,7 @@ class DeviceLayer:
         t["down_q"], t["down_s"], t["down_b"] = q, s, b
         act = "bf16" if self.act_dtype == MOE_DTYPE_BF16 else "f32"
         return DeviceLayer.from_tensors(self.hidden, self.dff, self.n_experts, self.top_k, act, self.clamp_limit,
-                                        t, down_layout=MOE_DOWN_COLS)
+                                        t, down_layout=MOE_DOWN_COLS, activation=self.activation)
 
     @staticmethod
     def from_host(layer, device="cuda"):
@@ -192,8 +203,10 @@ class DeviceLayer:
         for n in ("gate_s", "gate_b", "up_s", "up_b", "down_s", "down_b"):
             t[n] = dev(getattr(layer, n), np.int16)
         t["sidecar"] = None if layer.sidecar is None else dev(layer.sidecar.astype(np.float32), np.float32)
+        t["down_sidecar"] = (None if layer.down_sidecar is None
+                             else dev(layer.down_sidecar.astype(np.float32), np.float32))
         return DeviceLayer.from_tensors(sh.hidden, sh.dff, sh.n_experts, sh.top_k, sh.act,
-                                        layer.clamp or 0.0, t)
+                                        layer.clamp or 0.0, t, activation=layer.activation)
 
     def check(self) -> int:
         return lib().moe_layer_check(C.byref(self.struct))

@@ -72,6 +72,8 @@ moe_status check_layer(const moe_layer_t *L) {
     for (const void *p : sb)
         if (!p || !aligned(p, 4)) return MOE_ERR_INVALID_ARG;
     if (L->expert_scale && !aligned(L->expert_scale, 4)) return MOE_ERR_INVALID_ARG;
+    if (L->down_scale && !aligned(L->down_scale, 4)) return MOE_ERR_INVALID_ARG;
+    if (L->activation != MOE_ACT_SWIGLU && L->activation != MOE_ACT_GEGLU) return MOE_ERR_INVALID_ARG;
     Geometry g;
     if (!pick_geometry_gate_up(L->hidden, &g)) return MOE_ERR_UNSUPPORTED;
     if (L->down_layout == MOE_DOWN_ROWS) {
@@ -137,6 +139,6 @@ const char *moe_status_str(moe_status s) {
     return "unknown status";
 }
 
-int32_t moe_abi_version(void) { return 4; }
+int32_t moe_abi_version(void) { return 5; }
 
 }  // extern "C"

@@ -52,6 +52,7 @@ struct GateUpArgs {
     float *h;
     int hidden, dff, n_experts, top_k, n_slots;
     int max_count;  // the VALU kernel leaves experts with more slots to the MFMA kernel
+    int activation;  // moe_activation
 };
 
 struct DownArgs {
@@ -244,13 +245,17 @@ __device__ __forceinline__ float wave_sum_all(float v) {
 
 // ---------------------------------------------------------------- gate+up
 
-__device__ __forceinline__ float silu_mul(float g, float u, float sc, float lim) {
+// h from the gate and up pre-activations: expert-scale sidecar, clamp, then
+// SiLU(g) * u, or GELU(g) * u (tanh form) for the GeGLU variant.
+__device__ __forceinline__ float act_mul(float g, float u, float sc, float lim, int activation) {
     g *= sc;
     u *= sc;
     if (lim > 0.f) {
         g = fminf(fmaxf(g, -lim), lim);
         u = fminf(fmaxf(u, -lim), lim);
     }
+    if (activation == MOE_ACT_GEGLU)
+        return 0.5f * g * (1.f + tanhf(0.7978845608028654f * (g + 0.044715f * g * g * g))) * u;
     return g / (1.f + expf(-g)) * u;
 }
 
@@ -358,14 +363,14 @@ __device__ __forceinline__ void gate_up_token_rows(const GateUpArgs &a, const Ga
         const float other = dpp<kDppMirror>(tot);  // lane 16r reads lane 16r+15 (the u)
         const int r = lane >> 4;
         const int row = row0 + r * RPI;
-        if ((lane & 15) == 0 && row < F) a.h[(size_t)slot * F + row] = silu_mul(tot, other, sc, lim);
+        if ((lane & 15) == 0 && row < F) a.h[(size_t)slot * F + row] = act_mul(tot, other, sc, lim, a.activation);
     } else {
 #pragma unroll
         for (int r = 0; r < RI; ++r) {
             const float g = seg_sum<LPR>(part[2 * r]);
             const float u = seg_sum<LPR>(part[2 * r + 1]);
             const int row = row0 + r * RPI;
-            if (sl == 0 && row < F) a.h[(size_t)slot * F + row] = silu_mul(g, u, sc, lim);
+            if (sl == 0 && row < F) a.h[(size_t)slot * F + row] = act_mul(g, u, sc, lim, a.activation);
         }
     }
 }
@@ -686,7 +691,7 @@ __device__ __forceinline__ void gate_up_mfma_block(const GateUpArgs &a, int rb, 
                         u += pw[t * 8 + 4 + i];
                     }
                     const int row = row0 + 16 * t + 4 * kq + i;
-                    if (row < F) a.h[(size_t)slot * F + row] = silu_mul(g, u, sc, lim);
+                    if (row < F) a.h[(size_t)slot * F + row] = act_mul(g, u, sc, lim, a.activation);
                 }
         }
         __syncthreads();
@@ -1073,12 +1078,14 @@ __device__ __forceinline__ void store_out(float o, const void *residual, void *o
     }
 }
 
-// out[t][m] = sum_j w[t][j] * y[t * k + j][m]: fp32 FMAs in j order; a
-// token with an invalid expert id gets NaN.
+// out[t][m] = sum_j w[t][j] * (y[t * k + j][m] * dscale[e]): fp32 FMAs in j
+// order, the down-projection sidecar (if any) applied to y as it enters
+// the sum; a token with an invalid expert id gets NaN.
 template <bool BF16>
 __global__ __launch_bounds__(kBlock) void combine_kernel(const float *__restrict__ y,
                                                          const int *__restrict__ topk_idx,
                                                          const float *__restrict__ topk_w,
+                                                         const float *__restrict__ dscale,
                                                          const void *residual, void *out,
                                                          int hidden, int top_k, int n_experts) {
     const int t = blockIdx.y;
@@ -1088,8 +1095,12 @@ __global__ __launch_bounds__(kBlock) void combine_kernel(const float *__restrict
     bool bad = false;
     for (int j = 0; j < top_k; ++j) {
         const int s = t * top_k + j;
-        bad |= (unsigned)topk_idx[s] >= (unsigned)n_experts;
-        acc = fmaf(topk_w[s], y[(size_t)s * hidden + m], acc);
+        const int e = topk_idx[s];
+        const bool invalid = (unsigned)e >= (unsigned)n_experts;
+        bad |= invalid;
+        float v = y[(size_t)s * hidden + m];
+        if (dscale && !invalid) v *= dscale[e];
+        acc = fmaf(topk_w[s], v, acc);
     }
     if (bad) acc = __builtin_nanf("");
     store_out<BF16>(acc, residual, out, (size_t)t * hidden + m);
@@ -1124,6 +1135,7 @@ __global__ __launch_bounds__(NW * kWave) void down_token_kernel(const uint4 *__r
                                                                 const float *__restrict__ h,
                                                                 const int *__restrict__ topk_idx,
                                                                 const float *__restrict__ topk_w,
+                                                                const float *__restrict__ dscale,
                                                                 const void *residual, void *out,
                                                                 int hidden, int dff, int n_experts, int top_k) {
     constexpr int RW = kWave / KP;
@@ -1145,6 +1157,7 @@ __global__ __launch_bounds__(NW * kWave) void down_token_kernel(const uint4 *__r
     const int e_raw = live ? topk_idx[t * top_k + j] : 0;
     const float wj = live ? topk_w[t * top_k + j] : 0.f;  // read now, used by the combine
     const int e = (unsigned)e_raw < (unsigned)n_experts ? e_raw : 0;  // invalid: NaN below
+    const float dsj = (dscale && live) ? dscale[e] : 1.f;  // down-projection sidecar
     const int c0 = wave * CPW;
 
     uint4 wq[CPW];
@@ -1257,7 +1270,7 @@ __global__ __launch_bounds__(NW * kWave) void down_token_kernel(const uint4 *__r
         float y = part[lane];
 #pragma unroll
         for (int w = 1; w < NW; ++w) y += part[w * kWave + lane];
-        part[lane] = y;  // LDS operations of one wave complete in order
+        part[lane] = y * dsj;  // LDS operations of one wave complete in order
         __builtin_amdgcn_wave_barrier();
         // lane r < RW: the combine of row r in j order
         float o = 0.f;
@@ -1385,10 +1398,12 @@ static void launch_down_token_t(const moe_layer_t *L, int n_tokens, const float 
     const uint4 *q = (const uint4 *)L->down_q;
     if (L->act_dtype == MOE_DTYPE_BF16)
         hipLaunchKernelGGL((down_token_kernel<NW, CPW, KP, true>), grid, dim3(NW * kWave), lds, s, q, L->down_s,
-                           L->down_b, h, idx, w, residual, out, L->hidden, L->dff, L->n_experts, L->top_k);
+                           L->down_b, h, idx, w, L->down_scale, residual, out, L->hidden, L->dff, L->n_experts,
+                           L->top_k);
     else
         hipLaunchKernelGGL((down_token_kernel<NW, CPW, KP, false>), grid, dim3(NW * kWave), lds, s, q, L->down_s,
-                           L->down_b, h, idx, w, residual, out, L->hidden, L->dff, L->n_experts, L->top_k);
+                           L->down_b, h, idx, w, L->down_scale, residual, out, L->hidden, L->dff, L->n_experts,
+                           L->top_k);
 }
 
 template <int NW, int CPW>
@@ -1548,7 +1563,7 @@ static moe_status enqueue_gate_up(const moe_layer_t *layer, const void *x, int n
                   layer->gate_b, layer->up_s, layer->up_b, layer->expert_scale,
                   layer->clamp_limit, x, plan_view(plan), h, layer->hidden, layer->dff,
                   layer->n_experts, layer->top_k, n_tokens * layer->top_k,
-                  use_mfma ? kMfmaMinCount - 1 : INT_MAX};
+                  use_mfma ? kMfmaMinCount - 1 : INT_MAX, layer->activation};
     const bool bf16 = layer->act_dtype == MOE_DTYPE_BF16;
     const int groups_y = groups_y_of(layer, n_tokens);
     moe_status st;
@@ -1648,10 +1663,10 @@ static moe_status enqueue_down_combine(const moe_layer_t *layer, int n_tokens, c
     const dim3 cgrid((layer->hidden + kBlock - 1) / kBlock, n_tokens);
     if (layer->act_dtype == MOE_DTYPE_BF16)
         hipLaunchKernelGGL(combine_kernel<true>, cgrid, dim3(kBlock), 0, stream, y, topk_idx, topk_w,
-                           residual, out, layer->hidden, layer->top_k, layer->n_experts);
+                           layer->down_scale, residual, out, layer->hidden, layer->top_k, layer->n_experts);
     else
         hipLaunchKernelGGL(combine_kernel<false>, cgrid, dim3(kBlock), 0, stream, y, topk_idx, topk_w,
-                           residual, out, layer->hidden, layer->top_k, layer->n_experts);
+                           layer->down_scale, residual, out, layer->hidden, layer->top_k, layer->n_experts);
     return MOE_OK;
 }
 
@@ -1738,7 +1753,7 @@ extern "C" moe_status moe_route_gate_up(const moe_layer_t *layer, const float *l
         const GateUpArgs ga{(const uint4 *)layer->gate_q, (const uint4 *)layer->up_q, layer->gate_s,
                             layer->gate_b, layer->up_s, layer->up_b, layer->expert_scale,
                             layer->clamp_limit, x, plan_view(plan), h, layer->hidden, layer->dff,
-                            layer->n_experts, layer->top_k, n_tokens * layer->top_k, INT_MAX};
+                            layer->n_experts, layer->top_k, n_tokens * layer->top_k, INT_MAX, layer->activation};
         const PlanOut po{plan->counts, plan->offsets, plan->sorted_slots, plan->unique_experts, plan->n_unique,
                          (int4 *)plan->work};
         MOE_GEOMETRY_SWITCH(gu, st, launch_gate_up_route, ga, layer->act_dtype == MOE_DTYPE_BF16, pl, logits,

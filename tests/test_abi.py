@@ -32,7 +32,7 @@ def test_library_exports_every_declared_function():
     assert set(declared) == set(_lib.EXPORTS)
     for name in declared:
         assert hasattr(L, name), name
-    assert L.moe_abi_version() == 4
+    assert L.moe_abi_version() == 5
 
 
 def test_status_strings():
@@ -64,6 +64,7 @@ def test_layer_check_accepts_the_workload_shapes():
     assert check(hidden=256, dff=128, n_experts=8, top_k=2, act_dtype=moe.MOE_DTYPE_F32) == moe.MOE_OK
     assert check(hidden=4096, dff=2048, n_experts=256, top_k=6, clamp_limit=10.0,
                  expert_scale=FAKE + 0x9000000) == moe.MOE_OK
+    assert check(activation=moe.MOE_ACT_GEGLU, down_scale=FAKE + 0xA000000) == moe.MOE_OK
 
 
 @pytest.mark.parametrize("kw,want", [
@@ -83,6 +84,9 @@ def test_layer_check_accepts_the_workload_shapes():
     (dict(down_q=FAKE + 8), moe.MOE_ERR_INVALID_ARG),  # not 16-byte aligned
     (dict(up_s=FAKE + 2), moe.MOE_ERR_INVALID_ARG),
     (dict(down_layout=5), moe.MOE_ERR_INVALID_ARG),
+    (dict(activation=2), moe.MOE_ERR_INVALID_ARG),
+    (dict(activation=-1), moe.MOE_ERR_INVALID_ARG),
+    (dict(down_scale=FAKE + 2), moe.MOE_ERR_INVALID_ARG),   # not 4-byte aligned
     (dict(dff=1152, down_layout=moe.MOE_DOWN_COLS), moe.MOE_ERR_UNSUPPORTED),  # 36 chunks: no column kernel
     (dict(dff=192, down_layout=moe.MOE_DOWN_COLS), moe.MOE_ERR_UNSUPPORTED),   # dff % 128 != 0
 ])

@@ -273,6 +273,7 @@ def test_down_mfma_path(H, F, E, k, B, act):
     (512, 256, 16, 1, "bf16"),      # k = 1
     (256, 256, 4, 4, "bf16"),       # k = E
     (128, 384, 512, 16, "bf16"),    # 512 experts: routed by the router launch instead
+    (1024, 512, 64, 4, "f32"),      # GeGLU with a down-projection sidecar
 ])
 @pytest.mark.parametrize("ties,B", [("none", 1), ("ties", 1), ("none", 2), ("ties", 4), ("none", 8)])
 def test_decode_layer_few_tokens_is_bitwise_the_two_call_path(H, F, E, k, act, layout, ties, B):
@@ -281,7 +282,9 @@ def test_decode_layer_few_tokens_is_bitwise_the_two_call_path(H, F, E, k, act, l
     outputs, routing and plan identical, also with tied logits (ties go to
     the lower id; -0 equals +0)."""
     wide = (H, E) == (4096, 256)
-    sh = Shape(f"l{H}x{F}x{E}", 37, H, F, E, k, act, sidecar=wide, clamp=10.0 if wide else 0.0)
+    geglu = H == 1024
+    sh = Shape(f"l{H}x{F}x{E}", 37, H, F, E, k, act, sidecar=wide, clamp=10.0 if wide else 0.0,
+               activation="geglu" if geglu else "swiglu", down_sidecar=geglu)
     log(f"[case] decode_layer B={B} {H}x{F}x{E}x{k} {act} down={layout} {ties}")
     lg = make_logits(sh, B, seed=E + k)
     if ties == "ties":
@@ -307,6 +310,57 @@ def test_decode_layer_few_tokens_is_bitwise_the_two_call_path(H, F, E, k, act, l
     assert np.array_equal(host_bits(out1), host_bits(out2))
     ridx, _ = oracle.route_topk(lg, k)
     assert np.array_equal(idx1.cpu().numpy(), ridx)
+
+
+# ------------------------------------------- GeGLU and the down-projection sidecar
+GEGLU_CASES = [
+    # (shape, B, regime): B <= 8 routes inside gate+up and combines in the down
+    # kernel; 12 runs the VALU kernels and the combine launch; 16 and 32 the
+    # MFMA kernels where an expert holds >= 3 tokens
+    ("decode", 1, "normal"),
+    ("cohort", 4, "sharing"),
+    ("cohort", 12, "sharing"),
+    ("wide", 2, "normal"),
+    ("wide", 16, "same"),
+    ("stack", 32, "zipf"),
+]
+
+
+@pytest.mark.parametrize("layout", ["rows", "cols"])
+@pytest.mark.parametrize("name,B,regime", GEGLU_CASES)
+def test_geglu_with_down_sidecar_matches_oracle(name, B, regime, layout):
+    """GeGLU (tanh-form GELU) and a per-expert scale of the down output, on
+    every kernel path, against the oracle's fp64 GELU and scaling."""
+    import dataclasses
+    sh = dataclasses.replace(SHAPES[name], activation="geglu", down_sidecar=True)
+    log(f"[case] geglu+down sidecar {name} B={B} {regime} down={layout}")
+    lg = make_logits(sh, B, regime=regime, seed=11)
+    L = layer_for(sh, lg, seed=11)
+    assert L.activation == "geglu" and L.down_sidecar is not None
+    x = make_x(sh, B, seed=11)
+    run = GpuRun(L, x, lg, cols=layout == "cols")
+    check_against_oracle(L, x, lg, run, f"geglu {name}/B{B}/{regime}/{layout}")
+
+
+@pytest.mark.parametrize("B", [1, 4, 12, 32])
+def test_power_of_two_down_sidecar_scales_the_output_exactly(B):
+    """A down sidecar of 2 (4 for every other expert) multiplies each y by a
+    power of two: with fp32 activations and no residual, every output is
+    then exactly the weighted sum of those scaled y, so a uniform 2 doubles
+    the output bit for bit; the GeGLU h is untouched by it."""
+    import dataclasses
+    sh = dataclasses.replace(SHAPES["cohort"], act="f32", activation="geglu")
+    lg = make_logits(sh, B, regime="sharing", seed=B)
+    L = layer_for(sh, lg, seed=B)
+    x = make_x(sh, B, seed=B)
+    base = GpuRun(L, x, lg, cols=True)
+    L.down_sidecar = np.full(sh.n_experts, 2.0, np.float32)
+    two = GpuRun(L, x, lg, cols=True)
+    assert np.array_equal(two.out, base.out * 2)
+    assert np.array_equal(two.h, base.h)
+    check_against_oracle(L, x, lg, two, f"down sidecar x2 B{B}")
+    L.down_sidecar = np.where(np.arange(sh.n_experts) % 2, 4.0, 2.0).astype(np.float32)
+    check_against_oracle(L, x, lg, GpuRun(L, x, lg, cols=True), f"down sidecar 2/4 B{B}")
 
 
 # --------------------------------------------------------------- invariants
