@@ -20,8 +20,11 @@ capturing stream):
   2. kernels : R launches of each half of the step alone (moe_route_gate_up,
      moe_expert_down_combine) -> the average duration of the dominant
      kernel (gate+up: two thirds of the bytes) for the roofline entry
-  3. ladder  : B = 4 / 8 (30 % sharing) and B = 32 (Zipf 1.1) on the same
-     layers -> sublinearity of the step time in B
+  3. ladder  : B = 4 / 8 (30 % sharing), B = 32 (Zipf 1.1) and prefill
+     chunks of B = 256 / 1024 on the same layers -> sublinearity of the
+     step time in B, and the expert GEMM rate of the large batches
+  4. next rows: the router projection (moe_router_logits) alone, and the
+     step with the GeGLU activation and a down-projection sidecar
 The oracle (plain fp64 C, OpenMP) is timed on a bounded sample of the same
 workload on the host cores (rank 0, N = 1 only).
 
@@ -53,6 +56,8 @@ WORKLOADS = {
     "cohort4": ("cohort", 4, "sharing", "batched cohort, same layer, B=4, 30% of tokens share a top-8"),
     "cohort8": ("cohort", 8, "sharing", "batched cohort, same layer, B=8, 30% of tokens share a top-8"),
     "stack32": ("stack", 32, "zipf", "one layer of the 48-layer stack, B=32, Zipf(1.1) expert popularity"),
+    "prefill256": ("cohort", 256, "normal", "prefill chunk on the same layer, B=256, independent tokens"),
+    "prefill1024": ("cohort", 1024, "normal", "prefill chunk on the same layer, B=1024, independent tokens"),
     "wide1": ("wide", 1, "normal",
               "wide clamped layer: hidden 4096, dff 2048, 256 experts, top_k 6, sidecar, clamp 10, B=1"),
     "wide4": ("wide", 4, "normal",
@@ -222,6 +227,28 @@ def run_router_projection(rot, reps=4):
     return {"us": t * 1e6, "gbps": nbytes / t / 1e9, "bytes_per_launch": nbytes}
 
 
+def run_geglu_down_sidecar(rot, regime, seed):
+    """The same step on the same weights with the GeGLU activation and a
+    per-expert down-projection sidecar (uniform in [0.5, 1.5)), timed like
+    the headline steps over 2R steps."""
+    import torch
+
+    sh, R = rot.shape, rot.R
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(4321)
+    layers = []
+    for l in rot.layers:
+        t = dict(l.tensors)
+        t["down_sidecar"] = 0.5 + torch.rand(sh.n_experts, device="cuda", generator=gen)
+        act = "bf16" if l.act_dtype == rot.moe.MOE_DTYPE_BF16 else "f32"
+        layers.append(rot.moe.DeviceLayer.from_tensors(l.hidden, l.dff, l.n_experts, l.top_k, act,
+                                                       l.clamp_limit, t, down_layout=l.down_layout,
+                                                       activation="geglu"))
+    lr = Rotation(rot.moe, sh, rot.B, regime, R, seed, layers=layers)
+    t, _ = run_steps(lr, 2 * R, R)
+    return {"us_per_step": t / (2 * R) * 1e6, "steps_per_s": 2 * R / t}
+
+
 def unique_bytes(shape, n_unique):
     return n_unique * 3 * shape.hidden * shape.dff * BYTES_PER_WEIGHT
 
@@ -370,20 +397,30 @@ def main():
     rp = run_router_projection(rot)
     log(f"[bench] router projection (next row): {rp['us']:.2f} us per launch, {rp['gbps']:.0f} GB/s")
 
+    gg = run_geglu_down_sidecar(rot, regime, args.seed)
+    gg["step_time_vs_swiglu"] = gg["us_per_step"] / (ms * 1e3)
+    log(f"[bench] GeGLU + down sidecar (next row): {gg['us_per_step']:.2f} us/step "
+        f"({gg['step_time_vs_swiglu']:.3f}x the SwiGLU step)")
+
     ladder = []
     if not args.no_ladder and sh.name in ("decode", "cohort", "stack"):
-        for wl in ("cohort4", "cohort8", "stack32"):
+        for wl in ("cohort4", "cohort8", "stack32", "prefill256", "prefill1024"):
             s2, b2, r2, _ = WORKLOADS[wl]
             lr = Rotation(moe, SHAPES[s2], b2, r2, R, args.seed, layers=rot.layers)
             k2 = 2 * R
             t2, _ = run_steps(lr, k2, R)
             nu2 = float(np.mean(lr.n_unique()))
             st = t2 / k2
+            s2h = SHAPES[s2]
+            # multiply-adds actually required: 3 matrices of H x F per (token, k) slot
+            tflops = 2.0 * b2 * s2h.top_k * 3 * s2h.hidden * s2h.dff / st / 1e12
             ladder.append({"workload": wl, "B": b2, "steps_per_s": 1.0 / st, "us_per_step": st * 1e6,
-                           "unique_experts": nu2, "unique_gbps": unique_bytes(SHAPES[s2], nu2) / st / 1e9,
+                           "tokens_per_s": b2 / st,
+                           "unique_experts": nu2, "unique_gbps": unique_bytes(s2h, nu2) / st / 1e9,
+                           "expert_tflops": tflops,
                            "step_time_vs_B1": st / (secs / args.steps)})
             log(f"[bench] ladder {wl}: {st * 1e6:.2f} us/step, n_unique {nu2:.1f}, "
-                f"t/t1 {st / (secs / args.steps):.2f}")
+                f"t/t1 {st / (secs / args.steps):.2f}, {tflops:.2f} TFLOP/s")
             del lr
 
     cpu = None
@@ -417,7 +454,7 @@ def main():
                      "bytes_per_launch": gu_bytes, "us_per_launch": kt["route_gate_up"] * 1e6},
         "kernels": kernels,
         "ladder": ladder,
-        "next_rows": {"router_projection": rp},
+        "next_rows": {"router_projection": rp, "geglu_down_sidecar": gg},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -67,6 +67,9 @@ typedef enum { MOE_ACT_SWIGLU = 0, MOE_ACT_GEGLU = 1 } moe_activation;
 /* Limits enforced by validation. */
 #define MOE_MAX_EXPERTS 1024
 #define MOE_MAX_TOP_K 16
+/* Tokens per call of the expert entry points (one row of combine
+ * workgroups per token). */
+#define MOE_MAX_TOKENS 65535
 
 /*
  * One MoE layer: stacked expert weights, affine 4-bit, groups of 64 along

@@ -24,6 +24,7 @@ MOE_ACT_SWIGLU, MOE_ACT_GEGLU = 0, 1
 _ACTIVATIONS = {"swiglu": MOE_ACT_SWIGLU, "geglu": MOE_ACT_GEGLU}
 MOE_MAX_EXPERTS = 1024
 MOE_MAX_TOP_K = 16
+MOE_MAX_TOKENS = 65535
 
 
 class MoeError(RuntimeError):

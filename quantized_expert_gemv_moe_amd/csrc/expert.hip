@@ -1471,7 +1471,7 @@ static moe_status check_step(const moe_layer_t *layer, int32_t n_tokens, const m
     moe_status st = check_layer(layer);
     if (st != MOE_OK) return st;
     if (n_tokens < 0) return MOE_ERR_INVALID_ARG;
-    if ((int64_t)n_tokens * layer->top_k > INT32_MAX / 2) return MOE_ERR_UNSUPPORTED;
+    if (n_tokens > MOE_MAX_TOKENS) return MOE_ERR_UNSUPPORTED;
     if (n_tokens == 0) return MOE_OK;
     if (!plan || !plan->work || !plan->sorted_slots || (uintptr_t)plan->work % 16)
         return MOE_ERR_INVALID_ARG;

@@ -153,6 +153,7 @@ def test_decode_step_validation_before_any_launch():
     assert call(n=0) == moe.MOE_OK  # empty batch: nothing launched
     assert call(lay=layer(bits=2)) == moe.MOE_ERR_UNSUPPORTED
     assert call(n=-1) == moe.MOE_ERR_INVALID_ARG
+    assert call(n=65536) == moe.MOE_ERR_UNSUPPORTED        # beyond MOE_MAX_TOKENS
     assert call(x=None) == moe.MOE_ERR_INVALID_ARG
     assert call(out=X) == moe.MOE_ERR_INVALID_ARG          # out aliases x
     assert call(res=O) == moe.MOE_ERR_INVALID_ARG          # out aliases residual

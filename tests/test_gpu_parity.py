@@ -363,6 +363,39 @@ def test_power_of_two_down_sidecar_scales_the_output_exactly(B):
     check_against_oracle(L, x, lg, GpuRun(L, x, lg, cols=True), f"down sidecar 2/4 B{B}")
 
 
+# ------------------------------------------------------- large batches
+@pytest.mark.parametrize("B,layout", [(256, "rows"), (256, "cols"), (1024, "cols")])
+def test_prefill_sized_batch_on_sampled_tokens(B, layout):
+    """Prefill-sized batches (every expert holds tokens, 16 or 64 on
+    average, in several MFMA token tiles): routing and plan checked whole,
+    h and outputs of sampled tokens against the oracle run on those tokens
+    alone (a token's result depends on that token only)."""
+    sh = SHAPES["cohort"]
+    log(f"[case] prefill B={B} down={layout}")
+    lg = make_logits(sh, B, regime="normal", seed=B + 5)
+    L = layer_for(sh, lg, seed=B + 5)
+    x = make_x(sh, B, seed=B + 5)
+    run = GpuRun(L, x, lg, cols=layout == "cols")
+    idx, w = oracle.route_topk(lg, sh.top_k)
+    assert np.array_equal(run.idx, idx)
+    assert float(np.abs(run.w - w).max()) <= 1e-6
+    p = oracle.plan(idx, sh.n_experts)
+    for k in ("counts", "offsets", "sorted_slots", "unique_experts"):
+        assert np.array_equal(run.plan_np[k], p[k]), k
+    assert p["counts"].min() >= 3, "every expert should take the MFMA kernels"
+    rng = np.random.default_rng(B)
+    toks = np.unique(np.concatenate([[0, B - 1], rng.choice(B, 14, replace=False)]))
+    out64, h64 = oracle.decode_step(L, x[toks], idx[toks], w[toks], want_h=True)
+    slots = (toks[:, None] * sh.top_k + np.arange(sh.top_k)[None, :]).ravel()
+    eh = rel_l2(run.h[slots], h64)
+    got = oracle.bf16_to_f64(run.out[toks])
+    eo = rel_l2(got, out64)
+    dg = rel_l2(got, oracle.bf16_to_f64(oracle.round_bf16(out64)))
+    log(f"[parity] prefill B={B} {layout}: {len(toks)} tokens h_rel={eh:.3g} out_rel={eo:.3g} diag={dg:.3g}")
+    assert eh <= 1e-5 and eo <= 2e-3 and dg <= 5e-4
+    assert np.isfinite(oracle.bf16_to_f64(run.out)).all()
+
+
 # --------------------------------------------------------------- invariants
 @pytest.mark.parametrize("layout", ["rows", "cols"])
 def test_determinism_batch_invariance_permutation_and_duplicates(layout):
