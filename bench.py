@@ -390,7 +390,7 @@ def main():
     kernels["down_combine"]["gbps"] = dn_bytes / kt["down_combine"] / 1e9
     log(f"[bench] kernels: " + ", ".join(f"{k} {v['us']:.2f} us" for k, v in kernels.items()))
     ach = gu_bytes / kt["route_gate_up"] / 1e9
-    gu_kernel = ("gate_up_route_kernel<64, 1, 4, true, 2>" if B == 1 and sh.hidden == 2048 and sh.n_experts == 128
+    gu_kernel = ("gate_up_route_kernel<64, 1, 4, true, 2, 4>" if B == 1 and sh.hidden == 2048 and sh.n_experts == 128
                  else "gate_up_route_kernel" if B == 1 else "route_plan_kernel + gate_up kernels")
     traffic = counted_traffic(args.workload, gu_kernel)
 
