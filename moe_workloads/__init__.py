@@ -24,6 +24,8 @@ from .gen import (  # noqa: F401
     POISON_F16,
     bf16_bits_from_f32,
     f32_from_bf16_bits,
+    pack_bits,
+    quantize_affine,
     quantize_affine4,
     make_layer,
     make_x,

@@ -7,12 +7,15 @@ with the streams 0 activations, 1 logits, 2 gate, 3 up, 4 down, 5 sidecar,
 sidecar.  The same arguments always give the same bytes.
 
 Weight storage (the layout both sides read):
-  * ``*_q``  uint32 ``[E][rows][cols/8]``; nibble i of word w holds element
-    ``8*w + i`` of the row, lowest nibble first.  Rows are output features
-    (gate/up: Dff rows of ``hidden`` inputs; down: ``hidden`` rows of Dff
-    inputs), so the product is ``x @ W.T`` per expert.
-  * ``*_s``, ``*_b`` uint16 ``[E][rows][cols/64]``: fp16 bit patterns of the
-    per-group scale and bias of 64 consecutive inputs.
+  * ``*_q``  uint32 ``[E][rows][cols*bits/32]``: a row is a little-endian
+    bit stream, element c in stream bits ``c*bits .. c*bits+bits-1`` (so at
+    4 bits nibble i of word w holds element ``8*w + i``, lowest nibble
+    first).  Rows are output features (gate/up: Dff rows of ``hidden``
+    inputs; down: ``hidden`` rows of Dff inputs), so the product is
+    ``x @ W.T`` per expert.  Gate and up use ``shape.bits``, down
+    ``shape.down_bits``.
+  * ``*_s``, ``*_b`` uint16 ``[E][rows][cols/group]``: fp16 bit patterns of
+    the per-group scale and bias of ``shape.group_size`` consecutive inputs.
 Unmaterialised experts carry NaN scales and biases ("poison"): any read of
 them turns the result into NaN.
 """
@@ -47,6 +50,9 @@ class Shape:
     clamp: float = 0.0
     activation: str = "swiglu"   # or "geglu"
     down_sidecar: bool = False   # a per-expert fp32 scale of the down output
+    bits: int = 4                # width of the gate and up elements
+    down_bits: int = 4           # width of the down elements
+    group_size: int = 64         # inputs per scale/bias group
 
 
 SHAPES: Dict[str, Shape] = {
@@ -80,33 +86,47 @@ def f32_from_bf16_bits(b: np.ndarray) -> np.ndarray:
 
 
 # ------------------------------------------------------------- quantisation
-def quantize_affine4(w: np.ndarray):
-    """Quantise fp32 ``w[rows, cols]`` to affine 4-bit, groups of 64 along cols.
+def pack_bits(q: np.ndarray, bits: int) -> np.ndarray:
+    """Unsigned ``q[rows, cols]`` (< 2^bits) -> uint32 words [rows, cols*bits/32],
+    each row a little-endian bit stream with element c at bits c*bits.."""
+    rows, cols = q.shape
+    assert (cols * bits) % 32 == 0
+    b = ((q.astype(np.uint32)[:, :, None] >> np.arange(bits, dtype=np.uint32)) & 1).astype(np.uint8)
+    packed = np.packbits(b.reshape(rows, cols * bits), axis=1, bitorder="little")
+    return np.ascontiguousarray(packed).view("<u4").astype(np.uint32)
 
-    Per group: scale = fp16((max - min) / 15), bias = fp16(min),
-    q = clip(rint((w - bias) / scale), 0, 15).  Returns (q_words uint32
-    [rows, cols/8], scale bits uint16 [rows, cols/64], bias bits uint16).
-    Any deterministic quantiser gives valid inputs; both sides read the
-    stored bytes only.
+
+def quantize_affine(w: np.ndarray, bits: int = 4, group: int = GROUP):
+    """Quantise fp32 ``w[rows, cols]`` to affine ``bits``-bit, groups of
+    ``group`` along cols.
+
+    Per group, with n = 2^bits - 1: scale = fp16((max - min) / n), bias =
+    fp16(min), q = clip(rint((w - bias) / scale), 0, n).  Returns (q_words
+    uint32 [rows, cols*bits/32], scale bits uint16 [rows, cols/group], bias
+    bits uint16).  Any deterministic quantiser gives valid inputs; both sides
+    read the stored bytes only.
     """
     rows, cols = w.shape
-    assert cols % GROUP == 0
-    g = w.reshape(rows, cols // GROUP, GROUP).astype(np.float32, copy=False)
+    assert cols % group == 0
+    n = float(2 ** bits - 1)
+    g = w.reshape(rows, cols // group, group).astype(np.float32, copy=False)
     mn = g.min(axis=2)
     mx = g.max(axis=2)
-    s16 = ((mx - mn) / np.float32(15.0)).astype(np.float16)
+    s16 = ((mx - mn) / np.float32(n)).astype(np.float16)
     b16 = mn.astype(np.float16)
     s = s16.astype(np.float32)[:, :, None]
     b = b16.astype(np.float32)[:, :, None]
     safe = np.where(s == 0, np.float32(1.0), s)
     q = np.rint((g - b) / safe)
     q *= (s != 0)
-    np.clip(q, 0, 15, out=q)
-    q = q.astype(np.uint8).reshape(rows, cols)
-    # two nibbles per byte, lowest first; four little-endian bytes per word
-    packed = (q[:, 0::2] | (q[:, 1::2] << 4)).astype(np.uint8)
-    words = np.ascontiguousarray(packed).view("<u4").astype(np.uint32)
-    return words, s16.view(np.uint16), b16.view(np.uint16)
+    np.clip(q, 0, n, out=q)
+    q = q.astype(np.uint32).reshape(rows, cols)
+    return pack_bits(q, bits), s16.view(np.uint16), b16.view(np.uint16)
+
+
+def quantize_affine4(w: np.ndarray):
+    """:func:`quantize_affine` at 4 bits, groups of 64."""
+    return quantize_affine(w, 4, GROUP)
 
 
 # -------------------------------------------------------------------- layer
@@ -131,17 +151,19 @@ class Layer:
 
 def _empty_layer(shape: Shape) -> Layer:
     E, H, F = shape.n_experts, shape.hidden, shape.dff
+    G, nb, nd = shape.group_size, shape.bits, shape.down_bits
+    assert H % G == 0 and F % G == 0 and (H * nb) % 32 == 0 and (F * nd) % 32 == 0
     return Layer(
         shape=shape,
-        gate_q=np.zeros((E, F, H // 8), np.uint32),
-        gate_s=np.full((E, F, H // GROUP), POISON_F16, np.uint16),
-        gate_b=np.full((E, F, H // GROUP), POISON_F16, np.uint16),
-        up_q=np.zeros((E, F, H // 8), np.uint32),
-        up_s=np.full((E, F, H // GROUP), POISON_F16, np.uint16),
-        up_b=np.full((E, F, H // GROUP), POISON_F16, np.uint16),
-        down_q=np.zeros((E, H, F // 8), np.uint32),
-        down_s=np.full((E, H, F // GROUP), POISON_F16, np.uint16),
-        down_b=np.full((E, H, F // GROUP), POISON_F16, np.uint16),
+        gate_q=np.zeros((E, F, H * nb // 32), np.uint32),
+        gate_s=np.full((E, F, H // G), POISON_F16, np.uint16),
+        gate_b=np.full((E, F, H // G), POISON_F16, np.uint16),
+        up_q=np.zeros((E, F, H * nb // 32), np.uint32),
+        up_s=np.full((E, F, H // G), POISON_F16, np.uint16),
+        up_b=np.full((E, F, H // G), POISON_F16, np.uint16),
+        down_q=np.zeros((E, H, F * nd // 32), np.uint32),
+        down_s=np.full((E, H, F // G), POISON_F16, np.uint16),
+        down_b=np.full((E, H, F // G), POISON_F16, np.uint16),
         sidecar=None,
         clamp=shape.clamp,
         materialised=np.zeros(E, bool),
@@ -160,14 +182,14 @@ def make_layer(shape: Shape, layer: int = 0, experts: Optional[Iterable[int]] = 
     L = _empty_layer(shape)
     ids = range(E) if experts is None else sorted(set(int(e) for e in experts))
     for e in ids:
-        for stream, (qa, sa, ba, rows, cols) in (
-            (S_GATE, (L.gate_q, L.gate_s, L.gate_b, F, H)),
-            (S_UP, (L.up_q, L.up_s, L.up_b, F, H)),
-            (S_DOWN, (L.down_q, L.down_s, L.down_b, H, F)),
+        for stream, (qa, sa, ba, rows, cols, nb) in (
+            (S_GATE, (L.gate_q, L.gate_s, L.gate_b, F, H, shape.bits)),
+            (S_UP, (L.up_q, L.up_s, L.up_b, F, H, shape.bits)),
+            (S_DOWN, (L.down_q, L.down_s, L.down_b, H, F, shape.down_bits)),
         ):
             w = rng_for(seed, shape.cfg, layer, stream, e).standard_normal((rows, cols), np.float32)
             w *= np.float32(std)
-            q, s, b = quantize_affine4(w)
+            q, s, b = quantize_affine(w, nb, shape.group_size)
             qa[e], sa[e], ba[e] = q, s, b
         L.materialised[e] = True
     if shape.sidecar:
@@ -242,33 +264,43 @@ def make_logits(shape: Shape, n_tokens: int, layer: int = 0, regime: str = "norm
 
 
 # ------------------------------------------------- device-side bulk weights
-def quantize_affine4_torch(w):
-    """:func:`quantize_affine4` on a torch tensor ``w[n, rows, cols]`` (any
+def quantize_affine_torch(w, bits: int = 4, group: int = GROUP):
+    """:func:`quantize_affine` on a torch tensor ``w[n, rows, cols]`` (any
     device), bit-identical to the numpy version on the same fp32 values.
-    Returns int32 words [n, rows, cols/8] and int16 fp16-bit scale/bias."""
+    Returns int32 words [n, rows, cols*bits/32] and int16 fp16-bit scale/bias."""
     import torch
 
     n, rows, cols = w.shape
-    grp = w.reshape(n, rows, cols // GROUP, GROUP)
+    lv = float(2 ** bits - 1)
+    grp = w.reshape(n, rows, cols // group, group)
     mn = grp.amin(dim=3)
     mx = grp.amax(dim=3)
-    s16 = ((mx - mn) / 15.0).half()
+    s16 = ((mx - mn) / lv).half()
     b16 = mn.half()
     s = s16.float().unsqueeze(3)
     b = b16.float().unsqueeze(3)
     safe = torch.where(s == 0, torch.ones_like(s), s)
     q = torch.round((grp - b) / safe) * (s != 0)
-    q = q.clamp_(0, 15).to(torch.int64).view(n, rows, cols // 8, 8)
-    shifts = torch.arange(8, device=w.device, dtype=torch.int64) * 4
-    words = (q << shifts).sum(dim=3)  # < 2^32, in int64
+    q = q.clamp_(0, lv).to(torch.int64).view(n, rows, cols)
+    # the row's bit stream, 32 bits per word, lowest first
+    bit = torch.arange(bits, device=w.device, dtype=torch.int64)
+    stream = ((q.unsqueeze(3) >> bit) & 1).view(n, rows, cols * bits // 32, 32)
+    shifts = torch.arange(32, device=w.device, dtype=torch.int64)
+    words = (stream << shifts).sum(dim=3)  # < 2^32, in int64
     words = torch.where(words >= 2 ** 31, words - 2 ** 32, words).to(torch.int32)
     return words, s16.view(torch.int16), b16.view(torch.int16)
 
 
+def quantize_affine4_torch(w):
+    """:func:`quantize_affine_torch` at 4 bits, groups of 64."""
+    return quantize_affine_torch(w, 4, GROUP)
+
+
 def make_layer_device(shape: Shape, layer: int, device, seed: int = 0, std: float = 0.02,
                       chunk_experts: int = 8):
-    """Same recipe as :func:`make_layer` (N(0,std), affine 4-bit g64) drawn with
-    torch's generator on ``device``, for benchmark volumes (GBs of weights).
+    """Same recipe as :func:`make_layer` (N(0,std), affine quantisation at the
+    shape's widths and group size) drawn with torch's generator on
+    ``device``, for benchmark volumes (GBs of weights).
 
     The bytes differ from :func:`make_layer` (another random stream); the
     distribution and storage layout are the same.  Returns a dict of device
@@ -280,15 +312,14 @@ def make_layer_device(shape: Shape, layer: int, device, seed: int = 0, std: floa
     g = torch.Generator(device=device)
     g.manual_seed(int(np.random.SeedSequence([seed, shape.cfg, layer, 9]).generate_state(1)[0]))
     out = {}
-    quant = quantize_affine4_torch
-
-    for name, rows, cols in (("gate", F, H), ("up", F, H), ("down", H, F)):
+    for name, rows, cols, nb in (("gate", F, H, shape.bits), ("up", F, H, shape.bits),
+                                 ("down", H, F, shape.down_bits)):
         qs, ss, bs = [], [], []
         for e0 in range(0, E, chunk_experts):
             n = min(chunk_experts, E - e0)
             w = torch.randn((n, rows, cols), generator=g, device=device, dtype=torch.float32)
             w.mul_(std)
-            q, s, b = quant(w)
+            q, s, b = quantize_affine_torch(w, nb, shape.group_size)
             qs.append(q)
             ss.append(s)
             bs.append(b)

@@ -19,7 +19,7 @@
  *              of distinct experts -- the cross-cohort dedup that page
  *              "perf(moe): batched decode scales ..." proposes (Proposed
  *              Solution, second bullet).
- *   expert   : SwitchGLU expert: g = Wg x, u = Wu x (affine 4-bit weights,
+ *   expert   : SwitchGLU expert: g = Wg x, u = Wu x (affine 4-, 6- or 8-bit weights,
  *              groups of 64, dequantised exactly in fp64), optional
  *              per-expert scale sidecar on g and u, optional clamp of g and
  *              u to [-L, L], h = silu(g) * u, y = Wd h.  The gather of one
@@ -39,8 +39,6 @@
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
-
-#define ORC_GROUP 64
 
 /* ------------------------------------------------------------ conversions */
 
@@ -91,23 +89,35 @@ uint16_t orc_f64_to_bf16(double v) {
 
 /* ------------------------------------------------------------ dequantise */
 
-/* One weight of an affine 4-bit matrix stored as rows of cols/8 words,
- * element c of a row in nibble (c % 8) of word (c / 8), lowest nibble first;
- * scale and bias per group of 64 consecutive elements of a row. */
+/* One weight of an affine `bits`-bit matrix, w = scale * q + bias with q
+ * unsigned.  A row of `cols` elements is a little-endian bit stream of
+ * cols * bits / 32 words (bit j of the stream is bit j % 32 of word j / 32);
+ * element c occupies stream bits c*bits .. c*bits + bits - 1, lowest first,
+ * so 4-bit elements sit in nibble c % 8 of word c / 8 and a 6-bit element
+ * may straddle two words.  Scale and bias (fp16) per `group` consecutive
+ * elements of a row.  The pages template the fused kernel on bits and group
+ * size and name 4-bit gate/up with 6-bit down, which needs Dff divisible by
+ * 16 (page "perf(moe): batched decode scales 1.55x against 3.25x on
+ * dense", Implementation Notes); they give no packing, and this bit stream
+ * is the plainest one that makes 16 six-bit elements fill whole words. */
 static double orc_weight(const uint32_t *q, const uint16_t *s, const uint16_t *b,
-                         int cols, int r, int c) {
-    uint32_t word = q[(size_t)r * (cols / 8) + c / 8];
-    int nib = (int)((word >> (4 * (c % 8))) & 0xFu);
-    size_t g = (size_t)r * (cols / ORC_GROUP) + c / ORC_GROUP;
-    return orc_f16_to_f64(s[g]) * (double)nib + orc_f16_to_f64(b[g]);
+                         int cols, int bits, int group, int r, int c) {
+    const uint32_t *row = q + (size_t)r * ((size_t)cols * bits / 32);
+    uint32_t v = 0;
+    for (int i = 0; i < bits; ++i) {
+        size_t p = (size_t)c * bits + i;
+        v |= ((row[p / 32] >> (p % 32)) & 1u) << i;
+    }
+    size_t g = (size_t)r * (cols / group) + c / group;
+    return orc_f16_to_f64(s[g]) * (double)v + orc_f16_to_f64(b[g]);
 }
 
 /* Dense fp64 copy of one [rows][cols] quantised matrix (used by tests). */
 void orc_dequant(const uint32_t *q, const uint16_t *s, const uint16_t *b,
-                 int rows, int cols, double *w) {
+                 int rows, int cols, int bits, int group, double *w) {
     for (int r = 0; r < rows; ++r)
         for (int c = 0; c < cols; ++c)
-            w[(size_t)r * cols + c] = orc_weight(q, s, b, cols, r, c);
+            w[(size_t)r * cols + c] = orc_weight(q, s, b, cols, bits, group, r, c);
 }
 
 /* ----------------------------------------------------------------- route */
@@ -184,6 +194,9 @@ typedef struct {
     const float *sidecar;       /* [E] or NULL */
     int32_t activation;         /* 0: SwiGLU, 1: GeGLU (tanh-form GELU) */
     const float *down_sidecar;  /* [E] or NULL: y *= down_sidecar[e] */
+    int32_t bits;               /* width of gate and up elements */
+    int32_t down_bits;          /* width of down elements */
+    int32_t group_size;         /* elements per scale/bias group, all three */
 } orc_layer;
 
 static double orc_x(const orc_layer *L, const void *x, int t, int c) {
@@ -211,14 +224,14 @@ static double orc_gelu(double g) {
 /* Intermediate h (length dff) of expert e for token t: SiLU(g) * u (or
  * GELU(g) * u) after the optional sidecar (first) and clamp (second). */
 static void orc_expert_h(const orc_layer *L, const void *x, int t, int e, double *h) {
-    const int H = L->hidden, F = L->dff;
-    const size_t gq = (size_t)e * F * (H / 8), gs = (size_t)e * F * (H / ORC_GROUP);
+    const int H = L->hidden, F = L->dff, nb = L->bits, G = L->group_size;
+    const size_t gq = (size_t)e * F * ((size_t)H * nb / 32), gs = (size_t)e * F * (H / G);
     for (int n = 0; n < F; ++n) {
         double g = 0.0, u = 0.0;
         for (int c = 0; c < H; ++c) {
             double xv = orc_x(L, x, t, c);
-            g += orc_weight(L->gate_q + gq, L->gate_s + gs, L->gate_b + gs, H, n, c) * xv;
-            u += orc_weight(L->up_q + gq, L->up_s + gs, L->up_b + gs, H, n, c) * xv;
+            g += orc_weight(L->gate_q + gq, L->gate_s + gs, L->gate_b + gs, H, nb, G, n, c) * xv;
+            u += orc_weight(L->up_q + gq, L->up_s + gs, L->up_b + gs, H, nb, G, n, c) * xv;
         }
         if (L->sidecar) {
             double sc = (double)L->sidecar[e];
@@ -235,12 +248,12 @@ static void orc_expert_h(const orc_layer *L, const void *x, int t, int e, double
 
 /* y (length hidden) = Wd[e] h. */
 static void orc_expert_down(const orc_layer *L, int e, const double *h, double *y) {
-    const int H = L->hidden, F = L->dff;
-    const size_t dq = (size_t)e * H * (F / 8), ds = (size_t)e * H * (F / ORC_GROUP);
+    const int H = L->hidden, F = L->dff, nb = L->down_bits, G = L->group_size;
+    const size_t dq = (size_t)e * H * ((size_t)F * nb / 32), ds = (size_t)e * H * (F / G);
     for (int m = 0; m < H; ++m) {
         double acc = 0.0;
         for (int n = 0; n < F; ++n)
-            acc += orc_weight(L->down_q + dq, L->down_s + ds, L->down_b + ds, F, m, n) * h[n];
+            acc += orc_weight(L->down_q + dq, L->down_s + ds, L->down_b + ds, F, nb, G, m, n) * h[n];
         y[m] = L->down_sidecar ? acc * (double)L->down_sidecar[e] : acc;
     }
 }
@@ -256,7 +269,10 @@ int orc_decode_step(const orc_layer *L, const void *x, int n_tokens,
                     const int32_t *idx, const double *w, double *out,
                     double *h_out, double *y_out) {
     const int H = L->hidden, F = L->dff, k = L->top_k;
-    if (n_tokens < 0 || H % ORC_GROUP || F % ORC_GROUP || k < 1) return -1;
+    const int G = L->group_size;
+    if (n_tokens < 0 || k < 1 || G < 1 || H % G || F % G) return -1;
+    if (L->bits < 1 || L->bits > 16 || L->down_bits < 1 || L->down_bits > 16) return -1;
+    if ((H * L->bits) % 32 || (F * L->down_bits) % 32) return -1;
     const int n_slots = n_tokens * k;
     for (int s = 0; s < n_slots; ++s)
         if (idx[s] < 0 || idx[s] >= L->n_experts) return -1;

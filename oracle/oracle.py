@@ -47,6 +47,7 @@ class _Layer(C.Structure):
         ("down_s", C.c_void_p), ("down_b", C.c_void_p),
         ("sidecar", C.c_void_p),
         ("activation", C.c_int32), ("down_sidecar", C.c_void_p),
+        ("bits", C.c_int32), ("down_bits", C.c_int32), ("group_size", C.c_int32),
     ]
 
 
@@ -60,7 +61,7 @@ def lib():
         L.orc_route_topk.argtypes = [vp, i32, i32, i32, vp, vp]
         L.orc_plan.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp, vp]
         L.orc_decode_step.argtypes = [C.POINTER(_Layer), vp, i32, vp, vp, vp, vp, vp]
-        L.orc_dequant.argtypes = [vp, vp, vp, i32, i32, vp]
+        L.orc_dequant.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp]
         L.orc_round_bf16.argtypes = [vp, sz, vp]
         L.orc_round_f32.argtypes = [vp, sz, vp]
         L.orc_residual_bf16.argtypes = [vp, vp, sz, vp]
@@ -130,7 +131,9 @@ def _layer_struct(layer, x_is_bf16: bool, keep: list) -> _Layer:
                 x_is_bf16=1 if x_is_bf16 else 0, clamp_limit=float(layer.clamp or 0.0),
                 sidecar=None if sc is None else sc.ctypes.data,
                 activation=1 if act == "geglu" else 0,
-                down_sidecar=None if dsc is None else dsc.ctypes.data)
+                down_sidecar=None if dsc is None else dsc.ctypes.data,
+                bits=getattr(sh, "bits", 4), down_bits=getattr(sh, "down_bits", 4),
+                group_size=getattr(sh, "group_size", 64))
     for name, a in arrs.items():
         setattr(st, name, a.ctypes.data)
     return st
@@ -182,12 +185,17 @@ def router_logits(x: np.ndarray, w_router: np.ndarray) -> np.ndarray:
     return out
 
 
-def dequant(q: np.ndarray, s: np.ndarray, b: np.ndarray) -> np.ndarray:
+def dequant(q: np.ndarray, s: np.ndarray, b: np.ndarray, bits: int = 4, group: int = 64) -> np.ndarray:
+    """Dense fp64 [rows, cols] of one quantised matrix (q uint32 [rows, words])."""
     qc, sc, bc = _c(q, np.uint32), _c(s, np.uint16), _c(b, np.uint16)
     rows, words = qc.shape
-    cols = words * 8
+    if (words * 32) % bits:
+        raise ValueError("oracle dequant: words do not hold whole elements")
+    cols = words * 32 // bits
+    if cols % group or sc.shape != (rows, cols // group) or bc.shape != sc.shape:
+        raise ValueError("oracle dequant: scale/bias shape does not match the groups")
     out = np.zeros((rows, cols), np.float64)
-    lib().orc_dequant(_p(qc), _p(sc), _p(bc), rows, cols, _p(out))
+    lib().orc_dequant(_p(qc), _p(sc), _p(bc), rows, cols, bits, group, _p(out))
     return out
 
 

@@ -2,8 +2,9 @@
 
 Written independently of the C oracle, and differently on purpose:
   * weights are dequantised densely, nibbles taken byte by byte from a
-    little-endian uint8 view (low nibble of byte 0 first) and scales decoded
-    by numpy's own float16;
+    little-endian uint8 view (low nibble of byte 0 first), other widths read
+    from the row turned into one Python integer (little-endian bytes), and
+    scales decoded by numpy's own float16;
   * routing computes the full softmax over all experts, then a stable
     argsort of the negated logits, then renormalises the kept probabilities;
   * the combine runs a *dense* gate: every expert is evaluated for every
@@ -17,17 +18,36 @@ from __future__ import annotations
 import numpy as np
 
 
-def dequant_dense(q: np.ndarray, s: np.ndarray, b: np.ndarray) -> np.ndarray:
-    """q uint32 [..., rows, cols/8]; s, b fp16 bits [..., rows, cols/64] -> fp64."""
-    by = np.ascontiguousarray(q, dtype="<u4").view(np.uint8)  # [..., rows, cols/2]
-    lo = (by & 0x0F).astype(np.float64)
-    hi = (by >> 4).astype(np.float64)
-    nib = np.stack([lo, hi], axis=-1).reshape(*by.shape[:-1], by.shape[-1] * 2)
+def unpack_bigint(q: np.ndarray, bits: int) -> np.ndarray:
+    """q uint32 [..., words] -> element codes [..., words*32/bits]: each row
+    read as one little-endian integer, element c = bits c*bits.. of it."""
+    q = np.ascontiguousarray(q, dtype="<u4")
+    lead, words = q.shape[:-1], q.shape[-1]
+    cols = words * 32 // bits
+    flat = q.reshape(-1, words)
+    out = np.zeros((flat.shape[0], cols), np.float64)
+    mask = (1 << bits) - 1
+    for r in range(flat.shape[0]):
+        big = int.from_bytes(flat[r].tobytes(), "little")
+        for c in range(cols):
+            out[r, c] = (big >> (c * bits)) & mask
+    return out.reshape(*lead, cols)
+
+
+def dequant_dense(q: np.ndarray, s: np.ndarray, b: np.ndarray, bits: int = 4, group: int = 64) -> np.ndarray:
+    """q uint32 [..., rows, cols*bits/32]; s, b fp16 bits [..., rows, cols/group] -> fp64."""
+    if bits == 4:
+        by = np.ascontiguousarray(q, dtype="<u4").view(np.uint8)  # [..., rows, cols/2]
+        lo = (by & 0x0F).astype(np.float64)
+        hi = (by >> 4).astype(np.float64)
+        codes = np.stack([lo, hi], axis=-1).reshape(*by.shape[:-1], by.shape[-1] * 2)
+    else:
+        codes = unpack_bigint(q, bits)
     sc = np.asarray(s, np.uint16).view(np.float16).astype(np.float64)
     bi = np.asarray(b, np.uint16).view(np.float16).astype(np.float64)
-    sc = np.repeat(sc, 64, axis=-1)
-    bi = np.repeat(bi, 64, axis=-1)
-    return sc * nib + bi
+    sc = np.repeat(sc, group, axis=-1)
+    bi = np.repeat(bi, group, axis=-1)
+    return sc * codes + bi
 
 
 def route(logits: np.ndarray, k: int):
@@ -68,9 +88,10 @@ def moe_dense(layer, x: np.ndarray, logits: np.ndarray):
     for t in range(B):
         gate[t, idx[t]] = w[t]
     X = x_f64(x)
-    Wg = dequant_dense(layer.gate_q, layer.gate_s, layer.gate_b)  # [E,F,H]
-    Wu = dequant_dense(layer.up_q, layer.up_s, layer.up_b)
-    Wd = dequant_dense(layer.down_q, layer.down_s, layer.down_b)  # [E,H,F]
+    nb, nd, G = sh.bits, sh.down_bits, sh.group_size
+    Wg = dequant_dense(layer.gate_q, layer.gate_s, layer.gate_b, nb, G)  # [E,F,H]
+    Wu = dequant_dense(layer.up_q, layer.up_s, layer.up_b, nb, G)
+    Wd = dequant_dense(layer.down_q, layer.down_s, layer.down_b, nd, G)  # [E,H,F]
     out = np.zeros((B, sh.hidden))
     for e in range(E):
         if not layer.materialised[e]:
