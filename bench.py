@@ -23,8 +23,9 @@ capturing stream):
   3. ladder  : B = 4 / 8 (30 % sharing), B = 32 (Zipf 1.1) and prefill
      chunks of B = 256 / 1024 on the same layers -> sublinearity of the
      step time in B, and the expert GEMM rate of the large batches
-  4. next rows: the router projection (moe_router_logits) alone, and the
-     step with the GeGLU activation and a down-projection sidecar
+  4. next rows: the router projection (moe_router_logits) alone, the step
+     with the GeGLU activation and a down-projection sidecar, and the step
+     at other weight widths (4-bit gate/up with 6-bit down; 8-bit)
 The oracle (plain fp64 C, OpenMP) is timed on a bounded sample of the same
 workload on the host cores (rank 0, N = 1 only).
 
@@ -249,6 +250,39 @@ def run_geglu_down_sidecar(rot, regime, seed):
     return {"us_per_step": t / (2 * R) * 1e6, "steps_per_s": 2 * R / t}
 
 
+def run_widths(moe, shape, regime, seed, R=16, K=None):
+    """The single-token step at other weight widths (generic row kernels,
+    rows layout): 4-bit gate/up with 6-bit down, and 8-bit everywhere, both
+    in groups of 64, on R freshly drawn layers."""
+    import dataclasses
+
+    import torch
+    from moe_workloads import make_layer_device
+
+    res = {}
+    for nb, nd, grp in ((4, 6, 64), (8, 8, 64)):
+        sh = dataclasses.replace(shape, bits=nb, down_bits=nd, group_size=grp)
+        layers = []
+        for l in range(R):
+            t = make_layer_device(sh, l, torch.device("cuda"), seed=seed)
+            layers.append(moe.DeviceLayer.from_tensors(sh.hidden, sh.dff, sh.n_experts, sh.top_k, sh.act,
+                                                       sh.clamp, t, bits=nb, down_bits=nd, group_size=grp))
+            del t
+        torch.cuda.synchronize()
+        rot = Rotation(moe, sh, 1, regime, R, seed, layers=layers)
+        k = K or 8 * R
+        t, _ = run_steps(rot, k, R)
+        st = t / k
+        nu = float(np.mean(rot.n_unique()))
+        per_expert = sh.hidden * sh.dff * (2 * (nb / 8 + 4 / grp) + (nd / 8 + 4 / grp))
+        res[f"g{nb}u{nb}d{nd}_group{grp}"] = {"us_per_step": st * 1e6, "steps_per_s": 1 / st,
+                                              "unique_bytes": nu * per_expert,
+                                              "unique_gbps": nu * per_expert / st / 1e9}
+        del rot, layers
+        torch.cuda.empty_cache()
+    return res
+
+
 def unique_bytes(shape, n_unique):
     return n_unique * 3 * shape.hidden * shape.dff * BYTES_PER_WEIGHT
 
@@ -402,6 +436,13 @@ def main():
     log(f"[bench] GeGLU + down sidecar (next row): {gg['us_per_step']:.2f} us/step "
         f"({gg['step_time_vs_swiglu']:.3f}x the SwiGLU step)")
 
+    widths = None
+    if sh.name == "decode" and B == 1:
+        widths = run_widths(moe, sh, regime, args.seed)
+        for kname, v in widths.items():
+            log(f"[bench] widths {kname} (next row): {v['us_per_step']:.2f} us/step, "
+                f"{v['unique_gbps']:.0f} GB/s of unique expert bytes")
+
     ladder = []
     if not args.no_ladder and sh.name in ("decode", "cohort", "stack"):
         for wl in ("cohort4", "cohort8", "stack32", "prefill256", "prefill1024"):
@@ -454,7 +495,7 @@ def main():
                      "bytes_per_launch": gu_bytes, "us_per_launch": kt["route_gate_up"] * 1e6},
         "kernels": kernels,
         "ladder": ladder,
-        "next_rows": {"router_projection": rp, "geglu_down_sidecar": gg},
+        "next_rows": {"router_projection": rp, "geglu_down_sidecar": gg, "widths": widths},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

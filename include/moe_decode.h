@@ -72,17 +72,26 @@ typedef enum { MOE_ACT_SWIGLU = 0, MOE_ACT_GEGLU = 1 } moe_activation;
 #define MOE_MAX_TOKENS 65535
 
 /*
- * One MoE layer: stacked expert weights, affine 4-bit, groups of 64 along
- * the input dimension ("4-bit group 64" checkpoints; page "perf(moe):
- * batched decode scales 1.55x against 3.25x on dense", Current Behavior).
+ * One MoE layer: stacked expert weights, affine, groups along the input
+ * dimension ("4-bit group 64" checkpoints; page "perf(moe): batched decode
+ * scales 1.55x against 3.25x on dense", Current Behavior).
  *
- *   w = scale * q + bias,  q in 0..15
+ *   w = scale * q + bias,  q in 0 .. 2^bits - 1
  *
- * Weight matrices are stored as [expert][out][in/8] uint32 words; element
- * 8*w+i of a row sits in nibble i of word w, lowest nibble first.  Scales
- * and biases are fp16 bit patterns, [expert][out][in/64].
+ * `bits` (gate and up) and `down_bits` (down) are 4, 6 or 8, `group_size`
+ * (all three) 32, 64 or 128: the fused kernel is templated on bits and
+ * group size, and 4-bit gate/up with 6-bit down must keep working (same
+ * page, Implementation Notes).  A weight matrix is stored as
+ * [expert][out][in*bits/32] uint32 words, each row a little-endian bit
+ * stream: element c sits in stream bits c*bits .. c*bits+bits-1, stream bit
+ * j being bit j % 32 of word j / 32 (at 4 bits: element 8*w+i in nibble i
+ * of word w, lowest nibble first).  Scales and biases are fp16 bit
+ * patterns, [expert][out][in/group_size].
  *   gate, up : out = dff,    in = hidden
  *   down     : out = hidden, in = dff
+ * Layers with 4-bit gate, up and down in groups of 64 run the specialised
+ * kernels (either down layout, MFMA for large batches); every other format
+ * runs the generic row kernels and needs MOE_DOWN_ROWS.
  * Every `*_q` pointer must be 16-byte aligned, every scale/bias pointer
  * 4-byte aligned.  The struct itself lives in host memory; the pointers it
  * holds are device pointers.
@@ -112,15 +121,16 @@ typedef enum { MOE_ACT_SWIGLU = 0, MOE_ACT_GEGLU = 1 } moe_activation;
  * multiplies that expert's down-projection output y before the weighted
  * combine: the second of the "both sidecars" that page "perf(moe):
  * attribute ..." names (Problem / Background), which it does not define
- * further.  Both are appended after the v4 fields.
+ * further.  Fields after expert_scale were appended in ABI versions 5
+ * (down_scale, activation) and 6 (down_bits).
  */
 typedef struct {
     int32_t hidden;      /* H, multiple of 64 */
     int32_t dff;         /* expert intermediate size F, multiple of 64 */
     int32_t n_experts;   /* E, 1..MOE_MAX_EXPERTS */
     int32_t top_k;       /* k, 1..min(E, MOE_MAX_TOP_K) */
-    int32_t bits;        /* 4 */
-    int32_t group_size;  /* 64 */
+    int32_t bits;        /* 4, 6 or 8 (gate and up) */
+    int32_t group_size;  /* 32, 64 or 128; divides hidden and dff */
     int32_t act_dtype;   /* moe_dtype of x, residual and out */
     float clamp_limit;   /* >= 0; 0 disables the clamp */
     int32_t down_layout; /* moe_down_layout */
@@ -129,6 +139,7 @@ typedef struct {
     const float *expert_scale; /* [E] or NULL */
     const float *down_scale;   /* [E] or NULL */
     int32_t activation;        /* moe_activation */
+    int32_t down_bits;         /* 4, 6 or 8 (down projection) */
 } moe_layer_t;
 
 /*
@@ -289,7 +300,8 @@ moe_status moe_expert_down_combine(const moe_layer_t *layer, int32_t n_tokens,
  * read fastest: a wave then reads 64 consecutive output rows with one
  * coalesced 1 KiB load per 32 inputs.  A one-time, load-time step; pure byte
  * movement, nothing is re-quantised.  `layer` describes the source
- * (down_layout must be MOE_DOWN_ROWS); dst_q (16-byte aligned, E*hidden*dff/2
+ * (down_layout must be MOE_DOWN_ROWS; 4-bit weights in groups of 64 only,
+ * other formats return MOE_ERR_UNSUPPORTED); dst_q (16-byte aligned, E*hidden*dff/2
  * bytes), dst_s and dst_b (E*hidden*dff/64 fp16 each) are device buffers that
  * must not overlap the source.  Asynchronous on hip_stream.
  */

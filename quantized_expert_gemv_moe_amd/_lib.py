@@ -42,6 +42,7 @@ class LayerStruct(C.Structure):
         ("gate_s", C.c_void_p), ("gate_b", C.c_void_p), ("up_s", C.c_void_p), ("up_b", C.c_void_p),
         ("down_s", C.c_void_p), ("down_b", C.c_void_p),
         ("expert_scale", C.c_void_p), ("down_scale", C.c_void_p), ("activation", C.c_int32),
+        ("down_bits", C.c_int32),
     ]
 
 
@@ -144,24 +145,29 @@ class DeviceLayer:
     struct: LayerStruct
     down_layout: int = MOE_DOWN_ROWS
     activation: str = "swiglu"
+    bits: int = 4
+    down_bits: int = 4
+    group_size: int = 64
 
     @staticmethod
     def from_tensors(hidden, dff, n_experts, top_k, act: str, clamp_limit: float, tensors: dict,
-                     down_layout: int = MOE_DOWN_ROWS, activation: str = "swiglu"):
+                     down_layout: int = MOE_DOWN_ROWS, activation: str = "swiglu", bits: int = 4,
+                     down_bits: int = 4, group_size: int = 64):
         """``tensors``: gate_q/up_q/down_q (int32 or uint32 words), *_s/*_b (fp16 bits as
         int16/uint16), optional 'sidecar' (fp32 [E], on gate and up) and 'down_sidecar'
         (fp32 [E], on the down output); all on the same device.  ``activation`` is
-        "swiglu" or "geglu"."""
+        "swiglu" or "geglu"; ``bits`` (gate/up) and ``down_bits`` are 4, 6 or 8,
+        ``group_size`` 32, 64 or 128."""
         if activation not in _ACTIVATIONS:
             raise ValueError(f"activation must be one of {sorted(_ACTIVATIONS)}")
         t = {k: v for k, v in tensors.items() if v is not None}
         for k, v in t.items():
             if not v.is_contiguous():
                 raise ValueError(f"{k} must be contiguous")
-        st = LayerStruct(hidden=hidden, dff=dff, n_experts=n_experts, top_k=top_k, bits=4,
-                         group_size=64, act_dtype=MOE_DTYPE_BF16 if act == "bf16" else MOE_DTYPE_F32,
+        st = LayerStruct(hidden=hidden, dff=dff, n_experts=n_experts, top_k=top_k, bits=bits,
+                         group_size=group_size, act_dtype=MOE_DTYPE_BF16 if act == "bf16" else MOE_DTYPE_F32,
                          clamp_limit=float(clamp_limit), down_layout=down_layout,
-                         activation=_ACTIVATIONS[activation])
+                         activation=_ACTIVATIONS[activation], down_bits=down_bits)
         for name in ("gate_q", "up_q", "down_q", "gate_s", "gate_b", "up_s", "up_b", "down_s", "down_b"):
             setattr(st, name, t[name].data_ptr())
         sc = t.get("sidecar")
@@ -169,7 +175,7 @@ class DeviceLayer:
         ds = t.get("down_sidecar")
         st.down_scale = None if ds is None else ds.data_ptr()
         return DeviceLayer(hidden, dff, n_experts, top_k, st.act_dtype, float(clamp_limit), t, st, down_layout,
-                           activation)
+                           activation, bits, down_bits, group_size)
 
     def pack_down(self, stream=None, free_rows: bool = False) -> "DeviceLayer":
         """A copy of this layer whose down projection is regrouped to MOE_DOWN_COLS
@@ -187,7 +193,8 @@ class DeviceLayer:
         t["down_q"], t["down_s"], t["down_b"] = q, s, b
         act = "bf16" if self.act_dtype == MOE_DTYPE_BF16 else "f32"
         return DeviceLayer.from_tensors(self.hidden, self.dff, self.n_experts, self.top_k, act, self.clamp_limit,
-                                        t, down_layout=MOE_DOWN_COLS, activation=self.activation)
+                                        t, down_layout=MOE_DOWN_COLS, activation=self.activation, bits=self.bits,
+                                        down_bits=self.down_bits, group_size=self.group_size)
 
     @staticmethod
     def from_host(layer, device="cuda"):
@@ -207,7 +214,8 @@ class DeviceLayer:
         t["down_sidecar"] = (None if layer.down_sidecar is None
                              else dev(layer.down_sidecar.astype(np.float32), np.float32))
         return DeviceLayer.from_tensors(sh.hidden, sh.dff, sh.n_experts, sh.top_k, sh.act,
-                                        layer.clamp or 0.0, t, activation=layer.activation)
+                                        layer.clamp or 0.0, t, activation=layer.activation, bits=sh.bits,
+                                        down_bits=sh.down_bits, group_size=sh.group_size)
 
     def check(self) -> int:
         return lib().moe_layer_check(C.byref(self.struct))

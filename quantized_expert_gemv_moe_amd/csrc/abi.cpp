@@ -61,8 +61,11 @@ moe_status check_layer(const moe_layer_t *L) {
     if (L->n_experts > MOE_MAX_EXPERTS) return MOE_ERR_UNSUPPORTED;
     if (L->top_k > L->n_experts) return MOE_ERR_INVALID_ARG;
     if (L->top_k > MOE_MAX_TOP_K) return MOE_ERR_UNSUPPORTED;
-    if (L->bits != 4 || L->group_size != 64) return MOE_ERR_UNSUPPORTED;
+    for (int b : {L->bits, L->down_bits})
+        if (b != 4 && b != 6 && b != 8) return MOE_ERR_UNSUPPORTED;
+    if (L->group_size != 32 && L->group_size != 64 && L->group_size != 128) return MOE_ERR_UNSUPPORTED;
     if (L->hidden % 64 || L->dff % 64) return MOE_ERR_UNSUPPORTED;
+    if (L->hidden % L->group_size || L->dff % L->group_size) return MOE_ERR_UNSUPPORTED;
     if (L->act_dtype != MOE_DTYPE_F32 && L->act_dtype != MOE_DTYPE_BF16) return MOE_ERR_INVALID_ARG;
     if (!(L->clamp_limit >= 0.0f) || L->clamp_limit > 3.0e38f) return MOE_ERR_INVALID_ARG;
     const void *q[3] = {L->gate_q, L->up_q, L->down_q};
@@ -74,6 +77,13 @@ moe_status check_layer(const moe_layer_t *L) {
     if (L->expert_scale && !aligned(L->expert_scale, 4)) return MOE_ERR_INVALID_ARG;
     if (L->down_scale && !aligned(L->down_scale, 4)) return MOE_ERR_INVALID_ARG;
     if (L->activation != MOE_ACT_SWIGLU && L->activation != MOE_ACT_GEGLU) return MOE_ERR_INVALID_ARG;
+    if (L->down_layout != MOE_DOWN_ROWS && L->down_layout != MOE_DOWN_COLS) return MOE_ERR_INVALID_ARG;
+    if (!fast_format(L)) {  // the generic row kernels
+        int lpr, upl;
+        if (L->down_layout != MOE_DOWN_ROWS) return MOE_ERR_UNSUPPORTED;
+        if (!pick_generic(L->hidden, &lpr, &upl) || !pick_generic(L->dff, &lpr, &upl)) return MOE_ERR_UNSUPPORTED;
+        return MOE_OK;
+    }
     Geometry g;
     if (!pick_geometry_gate_up(L->hidden, &g)) return MOE_ERR_UNSUPPORTED;
     if (L->down_layout == MOE_DOWN_ROWS) {
@@ -139,6 +149,6 @@ const char *moe_status_str(moe_status s) {
     return "unknown status";
 }
 
-int32_t moe_abi_version(void) { return 5; }
+int32_t moe_abi_version(void) { return 6; }
 
 }  // extern "C"

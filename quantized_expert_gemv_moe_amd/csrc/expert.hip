@@ -30,17 +30,13 @@
 #include <math.h>
 
 #include "device_util.h"
+#include "expert_device.h"
 #include "moe_internal.h"
 #include "route_device.h"
 
 namespace moe {
 
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
-
-struct PlanView {
-    const int4 *work;          // {expert, first, count, first slot} per distinct expert
-    const int *sorted_slots;
-};
 
 struct GateUpArgs {
     const uint4 *gate_q, *up_q;
@@ -63,33 +59,6 @@ struct DownArgs {
     float *y;
     int hidden, dff, n_experts, n_slots, slots_per_stage;
 };
-
-// The work record of the workgroup's distinct expert (one 16-byte load);
-// false past the last distinct expert or on a malformed record, so no kernel
-// ever indexes out of bounds.
-struct Work {
-    int e, first, count, slot0;
-};
-__device__ __forceinline__ bool plan_expert(const PlanView &p, int u, int n_experts, int n_slots, Work *w) {
-    const int4 r = p.work[u];
-    if ((unsigned)r.x >= (unsigned)n_experts) return false;
-    if (r.y < 0 || r.z < 1 || r.y > n_slots - r.z || (unsigned)r.w >= (unsigned)n_slots) return false;
-    *w = Work{r.x, r.y, r.z, r.w};
-    return true;
-}
-
-// Slot i of the expert's list (the first one comes with the record).
-__device__ __forceinline__ int plan_slot(const PlanView &p, const Work &w, int i, int n_slots) {
-    const int s = i == 0 ? w.slot0 : p.sorted_slots[w.first + i];
-    return (unsigned)s < (unsigned)n_slots ? s : 0;  // malformed plan: stay in bounds
-}
-
-// Streaming 16-byte load of weights that are read once per step.
-__device__ __forceinline__ uint4 load_stream(const uint4 *p) {
-    typedef uint32_t v4u __attribute__((ext_vector_type(4)));
-    const v4u v = __builtin_nontemporal_load((const v4u *)p);
-    return make_uint4(v.x, v.y, v.z, v.w);
-}
 
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
@@ -244,20 +213,6 @@ __device__ __forceinline__ float wave_sum_all(float v) {
 }
 
 // ---------------------------------------------------------------- gate+up
-
-// h from the gate and up pre-activations: expert-scale sidecar, clamp, then
-// SiLU(g) * u, or GELU(g) * u (tanh form) for the GeGLU variant.
-__device__ __forceinline__ float act_mul(float g, float u, float sc, float lim, int activation) {
-    g *= sc;
-    u *= sc;
-    if (lim > 0.f) {
-        g = fminf(fmaxf(g, -lim), lim);
-        u = fminf(fmaxf(u, -lim), lim);
-    }
-    if (activation == MOE_ACT_GEGLU)
-        return 0.5f * g * (1.f + tanhf(0.7978845608028654f * (g + 0.044715f * g * g * g))) * u;
-    return g / (1.f + expf(-g)) * u;
-}
 
 // A lane's share of RI rows of one expert: its NV 16-byte chunks of each
 // gate and up row with their scales and biases (as fp32; with bf16
@@ -1553,10 +1508,11 @@ static moe_status launch_gate_up_mixed(const moe_layer_t *layer, const GateUpArg
 
 static moe_status enqueue_gate_up(const moe_layer_t *layer, const void *x, int n_tokens,
                                   const moe_plan_t *plan, void *workspace, hipStream_t stream) {
-    Geometry gu;
-    pick_geometry_gate_up(layer->hidden, &gu);
     const Workspace ws = workspace_layout(layer, n_tokens);
     float *h = (float *)((char *)workspace + ws.h_off);
+    if (!fast_format(layer)) return launch_generic_gate_up(layer, x, n_tokens, plan, h, stream);
+    Geometry gu;
+    pick_geometry_gate_up(layer->hidden, &gu);
     int nw = 0, gw = 0;
     const bool use_mfma = n_tokens >= kMfmaMinTokens && mfma_gate_up_shape(layer, &nw, &gw);
     GateUpArgs ga{(const uint4 *)layer->gate_q, (const uint4 *)layer->up_q, layer->gate_s,
@@ -1642,11 +1598,14 @@ static moe_status enqueue_down_combine(const moe_layer_t *layer, int n_tokens, c
     const float *h = (const float *)((char *)workspace + ws.h_off);
     float *y = (float *)((char *)workspace + ws.y_off);
     moe_status st;
-    if (n_tokens <= kTokenMajorMaxTokens) {
+    const bool fast = fast_format(layer);
+    if (fast && n_tokens <= kTokenMajorMaxTokens) {
         st = launch_down_token(layer, n_tokens, h, topk_idx, topk_w, residual, out, stream);
         if (st != MOE_ERR_UNSUPPORTED) return st;
     }
-    if (layer->down_layout == MOE_DOWN_COLS) {
+    if (!fast) {
+        st = launch_generic_down(layer, n_tokens, plan, h, y, stream);
+    } else if (layer->down_layout == MOE_DOWN_COLS) {
         int nw = 0, gw = 0;
         const bool mfma = n_tokens >= kMfmaMinTokens && mfma_down_shape(layer, &nw, &gw);
         const int gy = groups_y_of(layer, n_tokens), n_slots = n_tokens * layer->top_k;
@@ -1740,7 +1699,7 @@ extern "C" moe_status moe_route_gate_up(const moe_layer_t *layer, const float *l
     if ((st = check_x(x)) != MOE_OK) return st;
     hipStream_t stream = (hipStream_t)hip_stream;
     const int pl = per_lane_bucket(layer->n_experts);
-    if (n_tokens > kRouteMaxTokens || pl > 4 || n_tokens * layer->top_k > kWave) {
+    if (!fast_format(layer) || n_tokens > kRouteMaxTokens || pl > 4 || n_tokens * layer->top_k > kWave) {
         // router + planner launch, then the deduplicated gate+up
         st = moe_route_plan(logits, n_tokens, layer->n_experts, layer->top_k, topk_idx, topk_w, plan, hip_stream);
         if (st != MOE_OK) return st;

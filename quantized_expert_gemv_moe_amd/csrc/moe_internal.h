@@ -4,6 +4,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <hip/hip_runtime_api.h>
+
 #include "moe_decode.h"
 
 namespace moe {
@@ -20,6 +22,17 @@ bool pick_geometry_gate_up(int K, Geometry *g);
 // Waves per workgroup and 32-input chunks per wave of the column-layout down
 // kernel; false when that layout has no kernel for this dff.
 bool pick_down_cols(int dff, int *nw, int *cpw);
+
+// Weight formats: the 4-bit / group-64 kernels serve layers with 4-bit gate,
+// up and down in groups of 64; every other width or group size takes the
+// generic row kernels (rows layout only).  pick_generic gives their lanes per
+// row and 16-input units per lane for rows of K inputs.
+bool fast_format(const moe_layer_t *layer);
+bool pick_generic(int K, int *lpr, int *upl);
+moe_status launch_generic_gate_up(const moe_layer_t *layer, const void *x, int n_tokens,
+                                  const moe_plan_t *plan, float *h, hipStream_t stream);
+moe_status launch_generic_down(const moe_layer_t *layer, int n_tokens, const moe_plan_t *plan,
+                               const float *h, float *y, hipStream_t stream);
 
 // Validation without device access.
 moe_status check_layer(const moe_layer_t *layer);

@@ -32,7 +32,7 @@ def test_library_exports_every_declared_function():
     assert set(declared) == set(_lib.EXPORTS)
     for name in declared:
         assert hasattr(L, name), name
-    assert L.moe_abi_version() == 5
+    assert L.moe_abi_version() == 6
 
 
 def test_status_strings():
@@ -44,7 +44,7 @@ def test_status_strings():
 
 def layer(**kw):
     st = _lib.LayerStruct(hidden=2048, dff=768, n_experts=128, top_k=8, bits=4, group_size=64,
-                          act_dtype=moe.MOE_DTYPE_BF16, clamp_limit=0.0)
+                          act_dtype=moe.MOE_DTYPE_BF16, clamp_limit=0.0, down_bits=4)
     for i, n in enumerate(("gate_q", "up_q", "down_q", "gate_s", "gate_b", "up_s", "up_b", "down_s", "down_b")):
         setattr(st, n, FAKE + 0x100000 * i)
     st.expert_scale = None
@@ -65,11 +65,23 @@ def test_layer_check_accepts_the_workload_shapes():
     assert check(hidden=4096, dff=2048, n_experts=256, top_k=6, clamp_limit=10.0,
                  expert_scale=FAKE + 0x9000000) == moe.MOE_OK
     assert check(activation=moe.MOE_ACT_GEGLU, down_scale=FAKE + 0xA000000) == moe.MOE_OK
+    # other widths and group sizes: the generic row kernels (rows layout)
+    for bits, down_bits, group in ((8, 8, 64), (4, 6, 64), (6, 6, 32), (8, 4, 128), (4, 4, 32), (4, 4, 128)):
+        assert check(bits=bits, down_bits=down_bits, group_size=group) == moe.MOE_OK
+    assert check(hidden=4096, dff=2048, bits=6, down_bits=8, group_size=128) == moe.MOE_OK
 
 
 @pytest.mark.parametrize("kw,want", [
-    (dict(bits=8), moe.MOE_ERR_UNSUPPORTED),
-    (dict(group_size=32), moe.MOE_ERR_UNSUPPORTED),
+    (dict(bits=2), moe.MOE_ERR_UNSUPPORTED),
+    (dict(bits=5), moe.MOE_ERR_UNSUPPORTED),
+    (dict(down_bits=0), moe.MOE_ERR_UNSUPPORTED),
+    (dict(down_bits=3), moe.MOE_ERR_UNSUPPORTED),
+    (dict(group_size=16), moe.MOE_ERR_UNSUPPORTED),
+    (dict(group_size=48), moe.MOE_ERR_UNSUPPORTED),
+    (dict(dff=704, group_size=128), moe.MOE_ERR_UNSUPPORTED),          # group does not divide dff
+    (dict(bits=8, down_layout=moe.MOE_DOWN_COLS), moe.MOE_ERR_UNSUPPORTED),  # generic kernels: rows only
+    (dict(group_size=32, hidden=320 * 4, dff=320), moe.MOE_ERR_UNSUPPORTED),   # 20 units: no lane split
+    (dict(bits=8, hidden=16384), moe.MOE_ERR_UNSUPPORTED),             # 1024 units: over 8 per lane
     (dict(hidden=2000), moe.MOE_ERR_UNSUPPORTED),
     (dict(dff=1408), moe.MOE_ERR_UNSUPPORTED),      # 44 chunks: no lane geometry
     (dict(n_experts=2048), moe.MOE_ERR_UNSUPPORTED),
@@ -195,7 +207,7 @@ def test_decode_layer_validation_before_any_launch():
     assert g(C.byref(st), None, X, 1, I, WT, C.byref(p), W, ws_need, None) == moe.MOE_ERR_INVALID_ARG
     assert g(C.byref(st), G, None, 1, I, WT, C.byref(p), W, ws_need, None) == moe.MOE_ERR_INVALID_ARG
     assert g(C.byref(st), G, X, 1, I, WT, C.byref(p), W, ws_need - 1, None) == moe.MOE_ERR_WORKSPACE
-    assert g(C.byref(layer(group_size=128)), G, X, 1, I, WT, C.byref(p), W, ws_need, None) == \
+    assert g(C.byref(layer(group_size=48)), G, X, 1, I, WT, C.byref(p), W, ws_need, None) == \
         moe.MOE_ERR_UNSUPPORTED
 
 

@@ -363,6 +363,65 @@ def test_power_of_two_down_sidecar_scales_the_output_exactly(B):
     check_against_oracle(L, x, lg, GpuRun(L, x, lg, cols=True), f"down sidecar 2/4 B{B}")
 
 
+# ------------------------------------------- other widths and group sizes
+WIDTH_FORMATS = [(8, 8, 64), (4, 6, 64), (6, 6, 32), (8, 4, 128), (4, 4, 32), (4, 4, 128), (6, 8, 128)]
+
+
+@pytest.mark.parametrize("bits,down_bits,group", WIDTH_FORMATS)
+@pytest.mark.parametrize("name,B,regime", [("decode", 1, "normal"), ("cohort", 4, "sharing"),
+                                           ("cohort", 9, "same"), ("toy", 3, "normal")])
+def test_other_widths_match_oracle(bits, down_bits, group, name, B, regime):
+    """4/6/8-bit gate+up and down in groups of 32/64/128 (the generic row
+    kernels): routing, plan, h and outputs against the oracle; the "same"
+    routing puts 9 slots on each expert (several slot stages per pass)."""
+    import dataclasses
+    sh = dataclasses.replace(SHAPES[name], bits=bits, down_bits=down_bits, group_size=group)
+    log(f"[case] widths {bits}/{down_bits} g{group} {name} B={B} {regime}")
+    lg = make_logits(sh, B, regime=regime, seed=bits * 10 + down_bits)
+    L = layer_for(sh, lg, seed=group) if sh.n_experts > 8 else make_layer(sh, seed=group)
+    x = make_x(sh, B, seed=group)
+    run = GpuRun(L, x, lg)
+    check_against_oracle(L, x, lg, run, f"w{bits}/{down_bits}g{group} {name} B{B} {regime}")
+
+
+@pytest.mark.parametrize("bits,down_bits,group", [(8, 8, 128), (6, 4, 32)])
+def test_other_widths_on_the_wide_layer_with_geglu_and_sidecars(bits, down_bits, group):
+    """hidden 4096 (four units per lane), the expert-scale sidecar, clamp,
+    GeGLU and a down sidecar through the generic kernels."""
+    import dataclasses
+    sh = dataclasses.replace(SHAPES["wide"], bits=bits, down_bits=down_bits, group_size=group,
+                             activation="geglu", down_sidecar=True)
+    log(f"[case] widths wide {bits}/{down_bits} g{group}")
+    lg = make_logits(sh, 2, seed=7)
+    L = layer_for(sh, lg, seed=7)
+    x = make_x(sh, 2, seed=7, scale=4.0)  # some gate values beyond the clamp
+    run = GpuRun(L, x, lg)
+    check_against_oracle(L, x, lg, run, f"wide w{bits}/{down_bits}g{group}")
+
+
+def test_other_widths_batch_invariance_and_entry_points():
+    """A token alone equals the same token in a batch bit for bit; the
+    two-call path equals moe_decode_layer; the column layout is refused."""
+    import dataclasses
+    sh = dataclasses.replace(SHAPES["cohort"], bits=4, down_bits=6, group_size=64)
+    B = 6
+    lg = make_logits(sh, B, regime="sharing", seed=4)
+    L = layer_for(sh, lg, seed=4)
+    x = make_x(sh, B, seed=4)
+    dl = moe.DeviceLayer.from_host(L)
+    a = GpuRun(L, x, lg, dl=dl)
+    for t in range(B):
+        one = GpuRun(L, x[t:t + 1], lg[t:t + 1], dl=dl)
+        assert np.array_equal(one.out[0], a.out[t]), f"token {t}"
+    lgt = torch.from_numpy(lg).cuda()
+    idx2, w2, plan2 = moe.route_plan(lgt, sh.top_k)
+    out2 = moe.decode_step(dl, dev_x(x), idx2, w2, plan2)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(out2), a.out)
+    with pytest.raises(moe.MoeError):
+        dl.pack_down()
+
+
 # ------------------------------------------------------- large batches
 @pytest.mark.parametrize("B,layout", [(256, "rows"), (256, "cols"), (1024, "cols")])
 def test_prefill_sized_batch_on_sampled_tokens(B, layout):
