@@ -54,6 +54,7 @@ WORKLOADS = {
     # name: (shape, B, routing regime, description)
     "decode": ("decode", 1, "normal",
                "single-token decode MoE layer: hidden 2048, dff 768, 128 experts, top_k 8, B=1"),
+    "cohort2": ("cohort", 2, "sharing", "batched cohort, same layer, B=2, 30% of tokens share a top-8"),
     "cohort4": ("cohort", 4, "sharing", "batched cohort, same layer, B=4, 30% of tokens share a top-8"),
     "cohort8": ("cohort", 8, "sharing", "batched cohort, same layer, B=8, 30% of tokens share a top-8"),
     "stack32": ("stack", 32, "zipf", "one layer of the 48-layer stack, B=32, Zipf(1.1) expert popularity"),

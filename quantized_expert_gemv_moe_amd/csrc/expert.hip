@@ -1083,7 +1083,7 @@ __device__ __forceinline__ int xcd_block(int b, int n) {
     return (b % kXcds) * (n / kXcds) + b / kXcds;
 }
 
-template <int NW, int CPW, int KP, bool BF16>
+template <int NW, int CPW, int KP, int RB, bool BF16>
 __global__ __launch_bounds__(NW * kWave) void down_token_kernel(const uint4 *__restrict__ q,
                                                                 const uint16_t *__restrict__ sc,
                                                                 const uint16_t *__restrict__ bi,
@@ -1094,34 +1094,37 @@ __global__ __launch_bounds__(NW * kWave) void down_token_kernel(const uint4 *__r
                                                                 const void *residual, void *out,
                                                                 int hidden, int dff, int n_experts, int top_k) {
     constexpr int RW = kWave / KP;
+    constexpr int RWB = RW * RB;  // rows per workgroup: RB blocks of RW rows share the staged h
     // dff = 32 * NW * CPW (the geometry's own shape): compile-time strides
     constexpr int C = NW * CPW, F = 32 * C, G = C / 2, HS = F + kHPad;
     extern __shared__ float smem[];
     const int H = hidden;
-    float *hl = smem;                        // [k][HS]   h of the token's slots
-    float *gs = smem + top_k * HS;           // [k][G]    sums of h over each 64-group
-    float *part = gs + top_k * G;            // [NW][64]  per-wave sums
-    float *sl = part + NW * kWave;           // [2][k][G][RW] scales, then biases
+    float *hl = smem;                        // [k][HS]       h of the token's slots
+    float *gs = smem + top_k * HS;           // [k][G]        sums of h over each 64-group
+    float *part = gs + top_k * G;            // [NW][RB][64]  per-wave sums
+    float *sl = part + NW * RB * kWave;      // [2][k][G][RWB] scales, then biases
     const int t = blockIdx.y;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int j = lane / RW, r = lane % RW;
     const bool live = j < top_k;
-    const int mb = xcd_block(blockIdx.x, gridDim.x) * RW;
-    const int m = mb + r;
+    const int mb = xcd_block(blockIdx.x, gridDim.x) * RWB;
     const int e_raw = live ? topk_idx[t * top_k + j] : 0;
     const float wj = live ? topk_w[t * top_k + j] : 0.f;  // read now, used by the combine
     const int e = (unsigned)e_raw < (unsigned)n_experts ? e_raw : 0;  // invalid: NaN below
     const float dsj = (dscale && live) ? dscale[e] : 1.f;  // down-projection sidecar
     const int c0 = wave * CPW;
 
-    uint4 wq[CPW];
+    uint4 wq[RB][CPW];
 #pragma unroll
-    for (int jj = 0; jj < CPW; ++jj) wq[jj] = load_stream(q + ((size_t)e * C + (c0 + jj)) * H + m);
-    // Scales and biases of the block's RW rows, 4 rows (8 bytes) per load:
-    // unit u = ((sb * k + expert) * G + group) * RW/4 + quarter.  Loading them
+    for (int b = 0; b < RB; ++b)
+#pragma unroll
+        for (int jj = 0; jj < CPW; ++jj)
+            wq[b][jj] = load_stream(q + ((size_t)e * C + (c0 + jj)) * H + mb + b * RW + r);
+    // Scales and biases of the block's RWB rows, 4 rows (8 bytes) per load:
+    // unit u = ((sb * k + expert) * G + group) * RWB/4 + quarter.  Loading them
     // per lane would touch one cache line per 16 bytes used.
-    constexpr int QPR = RW / 4;  // RW >= 4 as top_k <= 16
+    constexpr int QPR = RWB / 4;  // RW >= 4 as top_k <= 16
     const int n_units = 2 * top_k * G * QPR;
     uint2 su[(2 * KP * G * QPR + NW * kWave - 1) / (NW * kWave)];
 #pragma unroll
@@ -1171,31 +1174,15 @@ __global__ __launch_bounds__(NW * kWave) void down_token_kernel(const uint4 *__r
         }
     }
     __syncthreads();
-    float ws[CPW], wb[CPW];
-#pragma unroll
-    for (int jj = 0; jj < CPW; ++jj) {
-        const int c = c0 + jj, g = c / 2;
-        ws[jj] = sl[((size_t)j * G + g) * RW + r];
-        wb[jj] = (c & 1) ? 0.f : sl[(((size_t)top_k + j) * G + g) * RW + r];
-    }
 
-    float acc = 0.f;
+    float acc[RB];
+#pragma unroll
+    for (int b = 0; b < RB; ++b) acc[b] = 0.f;
     if (live) {
 #pragma unroll
         for (int jj = 0; jj < CPW; ++jj) {
-            const int c = c0 + jj;
-            float wf[32];
-            const uint32_t wd[4] = {wq[jj].x, wq[jj].y, wq[jj].z, wq[jj].w};
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const uint32_t lo = wd[k] & 0x0F0F0F0Fu, hi = (wd[k] >> 4) & 0x0F0F0F0Fu;
-#pragma unroll
-                for (int b = 0; b < 4; ++b) {
-                    wf[8 * k + 2 * b] = (float)((lo >> (8 * b)) & 0xFFu);
-                    wf[8 * k + 2 * b + 1] = (float)((hi >> (8 * b)) & 0xFFu);
-                }
-            }
-            const float gsum = (c & 1) ? 0.f : gs[j * G + c / 2];
+            const int c = c0 + jj, g = c / 2;
+            const float gsum = (c & 1) ? 0.f : gs[j * G + g];
             const float4 *hc = (const float4 *)(hl + j * HS + c * 32);
             float hv[32];
 #pragma unroll
@@ -1206,35 +1193,52 @@ __global__ __launch_bounds__(NW * kWave) void down_token_kernel(const uint4 *__r
                 hv[4 * i + 2] = v.z;
                 hv[4 * i + 3] = v.w;
             }
-            float d0 = 0.f, d1 = 0.f, d2 = 0.f, d3 = 0.f;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                d0 = fmaf(wf[i], hv[i], d0);
-                d1 = fmaf(wf[8 + i], hv[8 + i], d1);
-                d2 = fmaf(wf[16 + i], hv[16 + i], d2);
-                d3 = fmaf(wf[24 + i], hv[24 + i], d3);
+            for (int b = 0; b < RB; ++b) {
+                const float ws = sl[((size_t)j * G + g) * RWB + b * RW + r];
+                const float wb = (c & 1) ? 0.f : sl[(((size_t)top_k + j) * G + g) * RWB + b * RW + r];
+                float wf[32];
+                const uint32_t wd[4] = {wq[b][jj].x, wq[b][jj].y, wq[b][jj].z, wq[b][jj].w};
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const uint32_t lo = wd[k] & 0x0F0F0F0Fu, hi = (wd[k] >> 4) & 0x0F0F0F0Fu;
+#pragma unroll
+                    for (int bb = 0; bb < 4; ++bb) {
+                        wf[8 * k + 2 * bb] = (float)((lo >> (8 * bb)) & 0xFFu);
+                        wf[8 * k + 2 * bb + 1] = (float)((hi >> (8 * bb)) & 0xFFu);
+                    }
+                }
+                float d0 = 0.f, d1 = 0.f, d2 = 0.f, d3 = 0.f;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    d0 = fmaf(wf[i], hv[i], d0);
+                    d1 = fmaf(wf[8 + i], hv[8 + i], d1);
+                    d2 = fmaf(wf[16 + i], hv[16 + i], d2);
+                    d3 = fmaf(wf[24 + i], hv[24 + i], d3);
+                }
+                acc[b] += fmaf(ws, (d0 + d1) + (d2 + d3), wb * gsum);
             }
-            acc += fmaf(ws[jj], (d0 + d1) + (d2 + d3), wb[jj] * gsum);
         }
     }
     const bool bad = __builtin_amdgcn_ballot_w64(live && (unsigned)e_raw >= (unsigned)n_experts) != 0;
-    part[wave * kWave + lane] = acc;
-    __syncthreads();
-    if (wave == 0) {
-        // lane (j, r): expert j's result for row r, the waves' sums in wave order
-        float y = part[lane];
 #pragma unroll
-        for (int w = 1; w < NW; ++w) y += part[w * kWave + lane];
-        part[lane] = y * dsj;  // LDS operations of one wave complete in order
+    for (int b = 0; b < RB; ++b) part[(wave * RB + b) * kWave + lane] = acc[b];
+    __syncthreads();
+    // wave w finishes row blocks w, w + NW, ...: lane (j, r) sums expert j's
+    // partials for row r in wave order, then lanes r < RW combine in j order
+    for (int b = wave; b < RB; b += NW) {
+        float y = part[b * kWave + lane];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) y += part[(w * RB + b) * kWave + lane];
+        part[b * kWave + lane] = y * dsj;  // LDS operations of one wave complete in order
         __builtin_amdgcn_wave_barrier();
-        // lane r < RW: the combine of row r in j order
         float o = 0.f;
         for (int jk = 0; jk < top_k; ++jk) {
             const float wk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wj), jk * RW));
-            o = fmaf(wk, part[jk * RW + r], o);
+            o = fmaf(wk, part[b * kWave + jk * RW + r], o);
         }
         if (bad) o = __builtin_nanf("");
-        if (lane < RW) store_out<BF16>(o, residual, out, (size_t)t * H + m);
+        if (lane < RW) store_out<BF16>(o, residual, out, (size_t)t * H + mb + b * RW + r);
     }
 }
 
@@ -1340,40 +1344,69 @@ static int pow2_at_least(int k) {
     return p;
 }
 
-static size_t down_token_lds(const moe_layer_t *L, int nw) {
+// LDS budget of the token-major down kernel, and the token counts from
+// which it takes two and four row blocks per workgroup.
+constexpr size_t kDownTokenLds = 65536;
+constexpr int kTokenRb2 = 2, kTokenRb4 = 4;
+
+static size_t down_token_lds(const moe_layer_t *L, int nw, int rb) {
     const int F = L->dff, G = F / kGroup, k = L->top_k;
     const int rw = kWave / pow2_at_least(k);
-    return ((size_t)k * (F + kHPad) + (size_t)k * G + (size_t)nw * kWave + (size_t)2 * k * G * rw) * sizeof(float);
+    return ((size_t)k * (F + kHPad) + (size_t)k * G + (size_t)nw * rb * kWave + (size_t)2 * k * G * rw * rb) *
+           sizeof(float);
+}
+
+template <int NW, int CPW, int KP, int RB>
+static void launch_down_token_rb(const moe_layer_t *L, int n_tokens, const float *h, const int32_t *idx,
+                                 const float *w, const void *residual, void *out, size_t lds, hipStream_t s) {
+    const dim3 grid(L->hidden / (kWave / KP * RB), n_tokens);
+    const uint4 *q = (const uint4 *)L->down_q;
+    if (L->act_dtype == MOE_DTYPE_BF16)
+        hipLaunchKernelGGL((down_token_kernel<NW, CPW, KP, RB, true>), grid, dim3(NW * kWave), lds, s, q,
+                           L->down_s, L->down_b, h, idx, w, L->down_scale, residual, out, L->hidden, L->dff,
+                           L->n_experts, L->top_k);
+    else
+        hipLaunchKernelGGL((down_token_kernel<NW, CPW, KP, RB, false>), grid, dim3(NW * kWave), lds, s, q,
+                           L->down_s, L->down_b, h, idx, w, L->down_scale, residual, out, L->hidden, L->dff,
+                           L->n_experts, L->top_k);
 }
 
 template <int NW, int CPW, int KP>
 static void launch_down_token_t(const moe_layer_t *L, int n_tokens, const float *h, const int32_t *idx,
-                                const float *w, const void *residual, void *out, size_t lds, hipStream_t s) {
-    const dim3 grid(L->hidden / (kWave / KP), n_tokens);
-    const uint4 *q = (const uint4 *)L->down_q;
-    if (L->act_dtype == MOE_DTYPE_BF16)
-        hipLaunchKernelGGL((down_token_kernel<NW, CPW, KP, true>), grid, dim3(NW * kWave), lds, s, q, L->down_s,
-                           L->down_b, h, idx, w, L->down_scale, residual, out, L->hidden, L->dff, L->n_experts,
-                           L->top_k);
+                                const float *w, const void *residual, void *out, int rb, hipStream_t s) {
+    const size_t lds = down_token_lds(L, NW, rb);
+    if (rb == 4)
+        launch_down_token_rb<NW, CPW, KP, 4>(L, n_tokens, h, idx, w, residual, out, lds, s);
+    else if (rb == 2)
+        launch_down_token_rb<NW, CPW, KP, 2>(L, n_tokens, h, idx, w, residual, out, lds, s);
     else
-        hipLaunchKernelGGL((down_token_kernel<NW, CPW, KP, false>), grid, dim3(NW * kWave), lds, s, q, L->down_s,
-                           L->down_b, h, idx, w, L->down_scale, residual, out, L->hidden, L->dff, L->n_experts,
-                           L->top_k);
+        launch_down_token_rb<NW, CPW, KP, 1>(L, n_tokens, h, idx, w, residual, out, lds, s);
 }
 
 template <int NW, int CPW>
 static moe_status launch_down_token_k(const moe_layer_t *L, int n_tokens, const float *h, const int32_t *idx,
-                                      const float *w, const void *residual, void *out, size_t lds,
+                                      const float *w, const void *residual, void *out, int rb,
                                       hipStream_t s) {
     switch (pow2_at_least(L->top_k)) {
-        case 1: launch_down_token_t<NW, CPW, 1>(L, n_tokens, h, idx, w, residual, out, lds, s); break;
-        case 2: launch_down_token_t<NW, CPW, 2>(L, n_tokens, h, idx, w, residual, out, lds, s); break;
-        case 4: launch_down_token_t<NW, CPW, 4>(L, n_tokens, h, idx, w, residual, out, lds, s); break;
-        case 8: launch_down_token_t<NW, CPW, 8>(L, n_tokens, h, idx, w, residual, out, lds, s); break;
-        case 16: launch_down_token_t<NW, CPW, 16>(L, n_tokens, h, idx, w, residual, out, lds, s); break;
+        case 1: launch_down_token_t<NW, CPW, 1>(L, n_tokens, h, idx, w, residual, out, rb, s); break;
+        case 2: launch_down_token_t<NW, CPW, 2>(L, n_tokens, h, idx, w, residual, out, rb, s); break;
+        case 4: launch_down_token_t<NW, CPW, 4>(L, n_tokens, h, idx, w, residual, out, rb, s); break;
+        case 8: launch_down_token_t<NW, CPW, 8>(L, n_tokens, h, idx, w, residual, out, rb, s); break;
+        case 16: launch_down_token_t<NW, CPW, 16>(L, n_tokens, h, idx, w, residual, out, rb, s); break;
         default: return MOE_ERR_UNSUPPORTED;
     }
     return MOE_OK;
+}
+
+// Row blocks per workgroup of the token-major down kernel: one for a single
+// token (the most workgroups, the shortest path), more as tokens add
+// workgroups, so the staged h of a token serves more rows; bounded by the
+// LDS budget and by hidden.
+static int down_token_rb(const moe_layer_t *L, int n_tokens, int nw) {
+    const int rw = kWave / pow2_at_least(L->top_k);
+    for (int rb = n_tokens >= kTokenRb4 ? 4 : n_tokens >= kTokenRb2 ? 2 : 1; rb > 1; rb /= 2)
+        if (L->hidden % (rw * rb) == 0 && down_token_lds(L, nw, rb) <= kDownTokenLds) return rb;
+    return 1;
 }
 
 // The token-major down + combine kernel, when the layer has column-layout
@@ -1384,11 +1417,11 @@ static moe_status launch_down_token(const moe_layer_t *L, int n_tokens, const fl
     int nw, cpw;
     if (L->down_layout != MOE_DOWN_COLS || !pick_down_cols(L->dff, &nw, &cpw)) return MOE_ERR_UNSUPPORTED;
     if (L->hidden % (kWave / pow2_at_least(L->top_k))) return MOE_ERR_UNSUPPORTED;
-    const size_t lds = down_token_lds(L, nw);
-    if (lds > 65536) return MOE_ERR_UNSUPPORTED;
+    if (down_token_lds(L, nw, 1) > kDownTokenLds) return MOE_ERR_UNSUPPORTED;
+    const int rb = down_token_rb(L, n_tokens, nw);
     switch (nw * 100 + cpw) {
 #define MOE_DT(NW, CPW) \
-    case NW * 100 + CPW: return launch_down_token_k<NW, CPW>(L, n_tokens, h, idx, w, residual, out, lds, s);
+    case NW * 100 + CPW: return launch_down_token_k<NW, CPW>(L, n_tokens, h, idx, w, residual, out, rb, s);
         MOE_DT(4, 1) MOE_DT(4, 3) MOE_DT(4, 5) MOE_DT(4, 7)
         MOE_DT(8, 1) MOE_DT(8, 2) MOE_DT(8, 3)
         MOE_DT(16, 2) MOE_DT(16, 3) MOE_DT(16, 4)
