@@ -1109,38 +1109,20 @@ __global__ __launch_bounds__(NW * kWave) void down_token_kernel(const uint4 *__r
     const int j = lane / RW, r = lane % RW;
     const bool live = j < top_k;
     const int mb = xcd_block(blockIdx.x, gridDim.x) * RWB;
-    const int e_raw = live ? topk_idx[t * top_k + j] : 0;
-    const float wj = live ? topk_w[t * top_k + j] : 0.f;  // read now, used by the combine
-    const int e = (unsigned)e_raw < (unsigned)n_experts ? e_raw : 0;  // invalid: NaN below
-    const float dsj = (dscale && live) ? dscale[e] : 1.f;  // down-projection sidecar
+    // Every load ahead of the weights is unconditional (clamped indices, the
+    // value selected afterwards): a load under a branch makes the compiler
+    // wait for all loads in flight where the branch joins.
+    const int jc = live ? j : top_k - 1;
+    const int e_ld = topk_idx[t * top_k + jc];
+    const float w_ld = topk_w[t * top_k + jc];
+    const int e_raw = live ? e_ld : 0;
+    const float wj = live ? w_ld : 0.f;  // read now, used by the combine
     const int c0 = wave * CPW;
 
-    uint4 wq[RB][CPW];
-#pragma unroll
-    for (int b = 0; b < RB; ++b)
-#pragma unroll
-        for (int jj = 0; jj < CPW; ++jj)
-            wq[b][jj] = load_stream(q + ((size_t)e * C + (c0 + jj)) * H + mb + b * RW + r);
-    // Scales and biases of the block's RWB rows, 4 rows (8 bytes) per load:
-    // unit u = ((sb * k + expert) * G + group) * RWB/4 + quarter.  Loading them
-    // per lane would touch one cache line per 16 bytes used.
-    constexpr int QPR = RWB / 4;  // RW >= 4 as top_k <= 16
-    const int n_units = 2 * top_k * G * QPR;
-    uint2 su[(2 * KP * G * QPR + NW * kWave - 1) / (NW * kWave)];
-#pragma unroll
-    for (int i = 0; i < (int)(sizeof(su) / sizeof(su[0])); ++i) {
-        const int u = threadIdx.x + i * NW * kWave;
-        su[i] = make_uint2(0, 0);
-        if (u < n_units) {
-            const int qq = u % QPR, g = (u / QPR) % G, jx = (u / (QPR * G)) % top_k, sb = u / (QPR * G * top_k);
-            const int ex_raw = topk_idx[t * top_k + jx];
-            const int ex = (unsigned)ex_raw < (unsigned)n_experts ? ex_raw : 0;
-            const uint16_t *src = sb ? bi : sc;
-            su[i] = *(const uint2 *)(src + ((size_t)ex * G + g) * H + mb + 4 * qq);
-        }
-    }
-    // stage h and its group sums: wave w takes the (slot, group) pairs
-    // w, w + NW, ... (at most MAXP of them), all loads in flight at once
+    // h of the token's slots, staged below: wave w takes the (slot, group)
+    // pairs w, w + NW, ... (at most MAXP of them).  These loads need no
+    // expert id, so they go out first, behind only the id load itself, and
+    // the weights' latency overlaps theirs.
     constexpr int MAXP = (KP * CPW + 1) / 2;  // k * G / NW <= KP * (NW * CPW / 2) / NW
     const float *ht = h + (size_t)t * top_k * F;
     const int n_pairs = top_k * G;
@@ -1148,18 +1130,57 @@ __global__ __launch_bounds__(NW * kWave) void down_token_kernel(const uint4 *__r
 #pragma unroll
     for (int i = 0; i < MAXP; ++i) {
         const int p = wave + i * NW;
-        const int jp = p / G, g = p - jp * G;
-        hv0[i] = p < n_pairs ? ht[(size_t)jp * F + g * kGroup + lane] : 0.f;
+        const int pc = p < n_pairs ? p : n_pairs - 1;  // past the end: loaded, not used
+        const int jp = pc / G, g = pc - jp * G;
+        hv0[i] = ht[(size_t)jp * F + g * kGroup + lane];
     }
+    __builtin_amdgcn_sched_barrier(0);  // keep the h loads ahead of the dependent ones
+
+    const int e = (unsigned)e_raw < (unsigned)n_experts ? e_raw : 0;  // invalid: NaN below
+    // Scales and biases of the block's RWB rows, 4 rows (8 bytes) per load:
+    // unit u = ((sb * k + expert) * G + group) * RWB/4 + quarter.  Loading them
+    // per lane would touch one cache line per 16 bytes used.  They go out
+    // before the weights, so converting them waits for them alone.
+    constexpr int QPR = RWB / 4;  // RW >= 4 as top_k <= 16
+    const int n_units = 2 * top_k * G * QPR;
+    uint2 su[(2 * KP * G * QPR + NW * kWave - 1) / (NW * kWave)];
+#pragma unroll
+    for (int i = 0; i < (int)(sizeof(su) / sizeof(su[0])); ++i) {
+        const int u = threadIdx.x + i * NW * kWave;
+        const int uc = u < n_units ? u : n_units - 1;  // past the end: loaded, not used
+        const int qq = uc % QPR, g = (uc / QPR) % G, jx = (uc / (QPR * G)) % top_k, sb = uc / (QPR * G * top_k);
+        // expert of slot jx from lane (jx, 0), which holds it already: a
+        // second load of topk_idx here would wait for every load before it
+        // (vector loads retire in order)
+        const int ex = __builtin_amdgcn_ds_bpermute(jx * RW * 4, e);
+        const uint16_t *src = sb ? bi : sc;
+        su[i] = *(const uint2 *)(src + ((size_t)ex * G + g) * H + mb + 4 * qq);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    uint4 wq[RB][CPW];
+#pragma unroll
+    for (int b = 0; b < RB; ++b)
+#pragma unroll
+        for (int jj = 0; jj < CPW; ++jj)
+            wq[b][jj] = load_stream(q + ((size_t)e * C + (c0 + jj)) * H + mb + b * RW + r);
+    // down-projection sidecar; without one, a load of topk_w[0] (used by no
+    // one) keeps the load unconditional and in the global address space (a
+    // generic-pointer load would wait for every load in flight)
+    const float ds_ld = dscale ? dscale[e] : topk_w[0];
+    const float dsj = (dscale && live) ? ds_ld : 1.f;
+    __builtin_amdgcn_sched_barrier(0);
+
+    // stage h and its group sums while the weights are in flight; a pair
+    // past the end repeats the last pair's value and sum into the same LDS
+    // words as the wave that owns it
 #pragma unroll
     for (int i = 0; i < MAXP; ++i) {
         const int p = wave + i * NW;
-        if (p < n_pairs) {
-            const int jp = p / G, g = p - jp * G;
-            hl[jp * HS + g * kGroup + lane] = hv0[i];
-            const float sum = wave_sum_all(hv0[i]);
-            if (lane == 0) gs[jp * G + g] = sum;
-        }
+        const int pc = p < n_pairs ? p : n_pairs - 1;
+        const int jp = pc / G, g = pc - jp * G;
+        hl[jp * HS + g * kGroup + lane] = hv0[i];
+        const float sum = wave_sum_all(hv0[i]);
+        if (lane == 0) gs[jp * G + g] = sum;
     }
 #pragma unroll
     for (int i = 0; i < (int)(sizeof(su) / sizeof(su[0])); ++i) {
