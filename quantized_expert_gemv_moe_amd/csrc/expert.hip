@@ -95,10 +95,19 @@ __device__ __forceinline__ float dot32_q4_bf16(uint4 q, const uint32_t *xp) {
 
 // 32 bf16 activations starting at element c0 of row xr, as loaded 16-byte
 // words.
+// The loads go through a global-address-space pointer: the activations
+// reach the kernels inside argument structs, where the compiler cannot
+// prove the address space, and a generic (flat) load makes every later
+// wait for memory also wait for all loads in flight.
+typedef uint32_t gv4u __attribute__((ext_vector_type(4)));
+typedef const __attribute__((address_space(1))) gv4u *gv4u_gptr;
 __device__ __forceinline__ void load_x32_bf16(const uint16_t *x, size_t xr, int c0, uint4 *raw) {
-    const uint4 *p = (const uint4 *)(x + xr + c0);
+    const gv4u_gptr p = (gv4u_gptr)(x + xr + c0);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) raw[i] = p[i];
+    for (int i = 0; i < 4; ++i) {
+        const gv4u v = p[i];
+        raw[i] = make_uint4(v.x, v.y, v.z, v.w);
+    }
 }
 
 // The 16 pairs used by dot8_q4_bf16 from the loaded words, and the sum of
@@ -340,42 +349,66 @@ __device__ __forceinline__ void gate_up_valu_block(const GateUpArgs &a, int rb, 
     constexpr int TCH = (XBF16 && NV == 1) ? 2 : 1;
     const int lane = threadIdx.x & (kWave - 1);
     const int sl = lane % LPR;
-    // With one token in the batch its activations are known before the plan
-    // record arrives: issue those loads now, so the record's round trip and
-    // theirs overlap.
-    const bool one_token = XBF16 && a.n_slots == a.top_k;
-    uint4 xraw0[XBF16 ? NV : 1][4];
-    if constexpr (XBF16) {
-        if (one_token) {
-#pragma unroll
-            for (int v = 0; v < NV; ++v) load_x32_bf16((const uint16_t *)a.x, 0, (v * LPR + sl) * 32, xraw0[v]);
-        }
-    }
     Work wk;
     if (!plan_expert(a.plan, u, a.n_experts, a.n_slots, &wk)) return;
     if (wk.count > a.max_count) return;  // the MFMA kernel's expert
     const int e = wk.e, count = wk.count;
     const int row0 = rb * ROWS_WG + lane / LPR;
 
+    // The first TCH tokens' activations go out ahead of the weights, and
+    // each pass fetches the next TCH tokens' before it computes, so no
+    // activation load waits behind the weights.  Loads are unconditional
+    // (past the last token they repeat it, unused): a load under a branch
+    // would make the compiler wait for every load in flight where it joins.
+    int slot_n[TCH];
+    uint4 raw_n[TCH][XBF16 ? NV : 1][4];
+#pragma unroll
+    for (int i = 0; i < TCH; ++i) {
+        slot_n[i] = plan_slot(a.plan, wk, i < count ? i : count - 1, a.n_slots);
+        if constexpr (XBF16) {
+#pragma unroll
+            for (int v = 0; v < NV; ++v)
+                load_x32_bf16((const uint16_t *)a.x, (size_t)(slot_n[i] / a.top_k) * a.hidden,
+                              (v * LPR + sl) * 32, raw_n[i][v]);
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
     GateUpRows<RI, NV> w;
     load_gate_up_rows<LPR, NV, RI, XBF16>(a, e, row0, sl, w);
     const float sc = a.expert_scale ? a.expert_scale[e] : 1.f;
     const float lim = a.clamp_limit;
+    __builtin_amdgcn_sched_barrier(0);
 
     for (int t0 = 0; t0 < count; t0 += TCH) {
         int slot[TCH];
-        GateUpX<LPR, NV, XBF16> x[TCH];
+        uint4 raw[TCH][XBF16 ? NV : 1][4];
 #pragma unroll
         for (int i = 0; i < TCH; ++i) {
-            slot[i] = -1;
-            if (i > 0 && t0 + i >= count) break;  // uniform: the chunk's tail is empty
-            slot[i] = plan_slot(a.plan, wk, t0 + i, a.n_slots);
-            load_gate_up_x<LPR, NV, XBF16>(a, slot[i] / a.top_k, sl, x[i], one_token ? xraw0 : nullptr);
+            slot[i] = slot_n[i];
+#pragma unroll
+            for (int v = 0; v < (XBF16 ? NV : 1); ++v)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) raw[i][v][q] = raw_n[i][v][q];
+        }
+        if constexpr (XBF16) {
+#pragma unroll
+            for (int i = 0; i < TCH; ++i) {
+                const int tn = t0 + TCH + i;
+                slot_n[i] = plan_slot(a.plan, wk, tn < count ? tn : count - 1, a.n_slots);
+#pragma unroll
+                for (int v = 0; v < NV; ++v)
+                    load_x32_bf16((const uint16_t *)a.x, (size_t)(slot_n[i] / a.top_k) * a.hidden,
+                                  (v * LPR + sl) * 32, raw_n[i][v]);
+            }
+        } else {
+            slot_n[0] = plan_slot(a.plan, wk, t0 + 1 < count ? t0 + 1 : count - 1, a.n_slots);
         }
 #pragma unroll
         for (int i = 0; i < TCH; ++i) {
-            if (i > 0 && t0 + i >= count) break;
-            gate_up_token_rows<LPR, NV, RI, XBF16>(a, w, x[i], slot[i], row0, sc, lim);
+            if (i > 0 && t0 + i >= count) break;  // uniform: the chunk's tail is empty
+            GateUpX<LPR, NV, XBF16> x;
+            load_gate_up_x<LPR, NV, XBF16>(a, slot[i] / a.top_k, sl, x, XBF16 ? raw[i] : nullptr);
+            gate_up_token_rows<LPR, NV, RI, XBF16>(a, w, x, slot[i], row0, sc, lim);
         }
     }
 }
@@ -773,12 +806,19 @@ __global__ __launch_bounds__(kBlock) void down_kernel(DownArgs a) {
 // -------------------------------------------------- down, column layout
 
 // MOE_DOWN_COLS: lane = output row, so the 32 h values of a chunk are the
-// same for the whole wave and come in through scalar loads (no LDS staging,
-// no cross-lane dot reductions).  NW waves split dff, CPW chunks of 32
-// inputs each, and their partial sums meet in LDS, added in wave order.
-// Chunks are the outer loop and up to kDownColsStage slots the inner one:
-// a chunk's 32 weights are converted once for all the expert's tokens.
-constexpr int kDownColsStage = 8;  // slots per LDS stage
+// same for the whole wave.  NW waves split dff, CPW chunks of 32 inputs
+// each, and their partial sums meet in LDS, added in wave order.  Chunks are
+// the outer loop and up to S slots the inner one: a chunk's 32 weights are
+// converted once for all the expert's tokens.  Each wave fetches the 64-input
+// groups its chunks fall in for every slot of a stage at once (one 256-byte
+// load each, all in flight together), forms the group sums from them, and
+// parks them in its own LDS rows, from which the chunk values are read back
+// as broadcasts; nothing waits for memory inside the chunk loop.
+// Slots per stage: most experts of a batch hold one or two tokens, and every
+// stage issues its S loads per group whether or not its slots are all used;
+// two at 16 waves, where a lane has 128 registers.
+template <int NW>
+constexpr int down_cols_stage() { return NW >= 16 ? 2 : 4; }
 
 template <int NW, int CPW>
 __global__ __launch_bounds__(NW * kWave) void down_cols_kernel(const uint4 *__restrict__ q,
@@ -788,8 +828,10 @@ __global__ __launch_bounds__(NW * kWave) void down_cols_kernel(const uint4 *__re
                                                                float *__restrict__ y, PlanView plan,
                                                                int hidden, int dff, int n_experts,
                                                                int n_slots, int max_count) {
-    constexpr int S = kDownColsStage;
+    constexpr int S = down_cols_stage<NW>();
+    constexpr int NG = CPW / 2 + 1;  // groups a wave's CPW chunks can touch
     __shared__ float part[NW][S][kWave];
+    __shared__ float4 hw[NW][S][NG][kGroup / 4];  // each wave's groups of h
     Work wk;
     if (!plan_expert(plan, blockIdx.y, n_experts, n_slots, &wk)) return;
     if (wk.count > max_count) return;  // the MFMA kernel's expert
@@ -799,6 +841,7 @@ __global__ __launch_bounds__(NW * kWave) void down_cols_kernel(const uint4 *__re
     const int H = hidden, F = dff, C = F / 32, G = F / kGroup;
     const int m = blockIdx.x * kWave + lane;  // hidden % 64 == 0: always a row
     const int c0 = wave * CPW;
+    const int g0 = c0 / 2;  // first group of the wave's chunks
 
     uint4 wq[CPW];
     float ws[CPW], wb[CPW];
@@ -814,15 +857,32 @@ __global__ __launch_bounds__(NW * kWave) void down_cols_kernel(const uint4 *__re
 
     for (int s0 = 0; s0 < wk.count; s0 += S) {
         const int ns = wk.count - s0 < S ? wk.count - s0 : S;
-        const float *hs[S];
+        // every (slot, group) load is unconditional: slots past the stage
+        // repeat its last one and groups past dff its last group, unused
+        float hv[S][NG];
 #pragma unroll
-        for (int i = 0; i < S; ++i) hs[i] = h + (size_t)plan_slot(plan, wk, i < ns ? s0 + i : s0, n_slots) * F;
+        for (int i = 0; i < S; ++i) {
+            const float *hs = h + (size_t)plan_slot(plan, wk, s0 + (i < ns ? i : ns - 1), n_slots) * F;
+#pragma unroll
+            for (int gg = 0; gg < NG; ++gg) {
+                const int g = g0 + gg < G ? g0 + gg : G - 1;
+                hv[i][gg] = hs[g * kGroup + lane];
+            }
+        }
+        float gsum[S][NG];
+#pragma unroll
+        for (int i = 0; i < S; ++i)
+#pragma unroll
+            for (int gg = 0; gg < NG; ++gg) {
+                ((float *)hw[wave][i][gg])[lane] = hv[i][gg];
+                gsum[i][gg] = wave_sum_all(hv[i][gg]);
+            }
         float acc[S];
 #pragma unroll
         for (int i = 0; i < S; ++i) acc[i] = 0.f;
 #pragma unroll
         for (int j = 0; j < CPW; ++j) {
-            const int c = c0 + j;
+            const int c = c0 + j, gg = c / 2 - g0;
             float wf[32];
             const uint32_t wd[4] = {wq[j].x, wq[j].y, wq[j].z, wq[j].w};
 #pragma unroll
@@ -837,8 +897,17 @@ __global__ __launch_bounds__(NW * kWave) void down_cols_kernel(const uint4 *__re
 #pragma unroll
             for (int i = 0; i < S; ++i) {
                 if (i >= ns) break;  // uniform
-                const float gsum = (c & 1) ? 0.f : wave_sum_all(hs[i][(c / 2) * kGroup + lane]);
-                const float *hc = hs[i] + c * 32;  // wave-uniform: scalar loads
+                const float gs = (c & 1) ? 0.f : gsum[i][gg];
+                const float4 *hc4 = &hw[wave][i][gg][(c & 1) * 8];  // uniform address: broadcast reads
+                float hc[32];
+#pragma unroll
+                for (int t = 0; t < 8; ++t) {
+                    const float4 v = hc4[t];
+                    hc[4 * t] = v.x;
+                    hc[4 * t + 1] = v.y;
+                    hc[4 * t + 2] = v.z;
+                    hc[4 * t + 3] = v.w;
+                }
                 float d0 = 0.f, d1 = 0.f, d2 = 0.f, d3 = 0.f;
 #pragma unroll
                 for (int t = 0; t < 8; ++t) {
@@ -847,7 +916,7 @@ __global__ __launch_bounds__(NW * kWave) void down_cols_kernel(const uint4 *__re
                     d2 = fmaf(wf[16 + t], hc[16 + t], d2);
                     d3 = fmaf(wf[24 + t], hc[24 + t], d3);
                 }
-                acc[i] += fmaf(ws[j], (d0 + d1) + (d2 + d3), wb[j] * gsum);
+                acc[i] += fmaf(ws[j], (d0 + d1) + (d2 + d3), wb[j] * gs);
             }
         }
 #pragma unroll
