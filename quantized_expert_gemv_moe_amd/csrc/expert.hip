@@ -413,8 +413,16 @@ __device__ __forceinline__ void gate_up_valu_block(const GateUpArgs &a, int rb, 
     }
 }
 
+// At least four waves per SIMD for the one-chunk bf16 rows (they fit in 128
+// registers without spilling): left to itself the compiler sizes this
+// one-wave kernel's registers for two, and a CU then holds too few waves to
+// keep enough loads in flight.
+template <int LPR, int NV, bool XBF16>
+constexpr int gate_up_waves_per_simd() { return (NV == 1 && XBF16) ? 4 : 1; }
+
 template <int LPR, int NV, int RI, bool XBF16>
-__global__ __launch_bounds__(kWave) void gate_up_kernel(GateUpArgs a) {
+__global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(gate_up_waves_per_simd<LPR, NV, XBF16>())))
+void gate_up_kernel(GateUpArgs a) {
     gate_up_valu_block<LPR, NV, RI, XBF16>(a, blockIdx.x, blockIdx.y);
 }
 
@@ -535,6 +543,10 @@ __device__ __forceinline__ void x8_pairs(uint4 w, uint32_t *o, float *acc) {
 
 constexpr int kMfmaTokens = 16;  // token tile
 
+// 16-row tiles per MFMA gate+up workgroup: one from eight waves up (the
+// workgroup's registers then leave room for two workgroups per CU), two below.
+constexpr int mfma_row_tiles(int nw) { return nw >= 8 ? 1 : 2; }
+
 // Streaming 8-byte load (two words of one row).
 __device__ __forceinline__ uint2 load_stream2(const uint2 *p) {
     typedef uint32_t v2u __attribute__((ext_vector_type(2)));
@@ -553,9 +565,16 @@ __device__ __forceinline__ void load_x_mfma(const GateUpArgs &a, int slot, bool 
     const uint16_t *xr = (const uint16_t *)a.x + (size_t)(slot / a.top_k) * a.hidden;
 #pragma unroll
     for (int gi = 0; gi < GW; ++gi) {
-        const uint4 *xp = (const uint4 *)(xr + (g0 + gi) * kGroup + 16 * kq);
-        xw[gi][0] = live ? xp[0] : make_uint4(0, 0, 0, 0);
-        xw[gi][1] = live ? xp[1] : make_uint4(0, 0, 0, 0);
+        // unconditional loads (the slot is valid either way), masked after:
+        // a load under a branch would make the compiler wait for every load
+        // in flight where the branch joins.  The mask is opaque to the
+        // optimizer, which would otherwise move the loads into a branch.
+        uint32_t mk = live ? 0xFFFFFFFFu : 0u;
+        asm volatile("" : "+v"(mk));
+        const gv4u_gptr xp = (gv4u_gptr)(xr + (g0 + gi) * kGroup + 16 * kq);
+        const gv4u v0 = xp[0], v1 = xp[1];
+        xw[gi][0] = make_uint4(v0.x & mk, v0.y & mk, v0.z & mk, v0.w & mk);
+        xw[gi][1] = make_uint4(v1.x & mk, v1.y & mk, v1.z & mk, v1.w & mk);
     }
 }
 
@@ -572,10 +591,10 @@ __device__ __forceinline__ void gate_up_mfma_block(const GateUpArgs &a, int rb, 
     const int r16 = lane & 15, kq = lane >> 4;
     const int row0 = rb * ROWS;
     const int g0 = wave * GW;
-    // the first token tile's slots and activations, in flight with the weights
-    int slot = r16 < wk.count ? plan_slot(a.plan, wk, r16, a.n_slots) : 0;
-    uint4 xw[GW][2];
-    load_x_mfma<GW>(a, slot, r16 < wk.count, g0, kq, xw);
+    // order of issue: the first token tile's slot lookup, the weights, then
+    // the activations that need the slot (their wait covers the lookup alone)
+    int slot = plan_slot(a.plan, wk, r16 < wk.count ? r16 : wk.count - 1, a.n_slots);
+    __builtin_amdgcn_sched_barrier(0);
 
     // this wave's weights: words 2kq and 2kq+1 of each group, per row tile
     uint2 wgq[GW][RT], wuq[GW][RT];
@@ -592,6 +611,10 @@ __device__ __forceinline__ void gate_up_mfma_block(const GateUpArgs &a, int rb, 
             }
         }
     }
+    __builtin_amdgcn_sched_barrier(0);
+    slot = r16 < wk.count ? slot : 0;
+    uint4 xw[GW][2];
+    load_x_mfma<GW>(a, slot, r16 < wk.count, g0, kq, xw);
     // per [group][row]: 16 * scale, and bias - 16 * scale (the weights go
     // into the MFMA as 1 + q / 16)
     float *sg = smem, *bg = smem + G * ROWS, *su = smem + 2 * G * ROWS, *bu = smem + 3 * G * ROWS;
@@ -666,28 +689,35 @@ __device__ __forceinline__ void gate_up_mfma_block(const GateUpArgs &a, int rb, 
                 mine[t * 8 + 4 + i] = accu[t][i];
             }
         __syncthreads();
-        if (wave == 0 && live) {  // add the partials in wave order and finish the rows
+        // add the partials in wave order and finish the rows: output o =
+        // (row tile, row of the lane's four) goes to wave o % NW
+        if (live) {
+            for (int o = wave; o < 4 * RT; o += NW) {
+                const int t = o / 4, i = o % 4;
+                float g = 0.f, u = 0.f;
 #pragma unroll
-            for (int t = 0; t < RT; ++t)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    float g = 0.f, u = 0.f;
-#pragma unroll
-                    for (int w = 0; w < NW; ++w) {
-                        const float *pw = part + ((size_t)w * kWave + lane) * (8 * RT);
-                        g += pw[t * 8 + i];
-                        u += pw[t * 8 + 4 + i];
-                    }
-                    const int row = row0 + 16 * t + 4 * kq + i;
-                    if (row < F) a.h[(size_t)slot * F + row] = act_mul(g, u, sc, lim, a.activation);
+                for (int w = 0; w < NW; ++w) {
+                    const float *pw = part + ((size_t)w * kWave + lane) * (8 * RT);
+                    g += pw[t * 8 + i];
+                    u += pw[t * 8 + 4 + i];
                 }
+                const int row = row0 + 16 * t + 4 * kq + i;
+                if (row < F) a.h[(size_t)slot * F + row] = act_mul(g, u, sc, lim, a.activation);
+            }
         }
         __syncthreads();
     }
 }
 
+// Workgroups of eight or more waves fit four waves per SIMD (two workgroups
+// per CU at eight) in 128 registers; the compiler would otherwise size them
+// for two waves per SIMD.
+template <int NW>
+constexpr int mfma_waves_per_simd() { return NW >= 8 ? 4 : 1; }
+
 template <int NW, int GW, int RT>
-__global__ __launch_bounds__(NW * kWave) void gate_up_mfma_kernel(GateUpArgs a, int min_count) {
+__global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(mfma_waves_per_simd<NW>())))
+void gate_up_mfma_kernel(GateUpArgs a, int min_count) {
     extern __shared__ float smem[];
     gate_up_mfma_block<NW, GW, RT>(a, blockIdx.x, blockIdx.y, smem, min_count);
 }
@@ -698,7 +728,8 @@ __global__ __launch_bounds__(NW * kWave) void gate_up_mfma_kernel(GateUpArgs a, 
 // block, distinct expert) for the others.  The two kinds run side by side
 // instead of one launch after the other.
 template <int LPR, int NV, int RI, int NW, int GW, int RT>
-__global__ __launch_bounds__(NW * kWave) void gate_up_mixed_kernel(GateUpArgs a, int mfma_blocks, int rb_mfma,
+__global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(mfma_waves_per_simd<NW>())))
+void gate_up_mixed_kernel(GateUpArgs a, int mfma_blocks, int rb_mfma,
                                                                    int rb_valu, int n_valu, int min_count) {
     extern __shared__ float smem[];
     const int b = blockIdx.x;
@@ -986,6 +1017,33 @@ __global__ __launch_bounds__(NW * kWave) void down_mfma_kernel(const uint32_t *_
     const int m0 = blockIdx.x * ROWS;
     const int g0 = wave * GW;
 
+    // h of the lane's token (8 values of chunk 2g and 8 of chunk 2g + 1 per
+    // group); unconditional loads (a lane without a token reads slot 0's
+    // row and zeroes it), so the first tile's go out with the weights
+    float hv[GW][2][8];
+    auto load_h = [&](int slot, bool live) {
+        const float *hr = h + (size_t)slot * F;
+#pragma unroll
+        for (int gi = 0; gi < GW; ++gi)
+#pragma unroll
+            for (int c2 = 0; c2 < 2; ++c2) {
+                const float4 *p4 = (const float4 *)(hr + (2 * (g0 + gi) + c2) * 32 + 8 * kq);
+                const float4 lo = p4[0], hi = p4[1];
+                hv[gi][c2][0] = lo.x; hv[gi][c2][1] = lo.y; hv[gi][c2][2] = lo.z; hv[gi][c2][3] = lo.w;
+                hv[gi][c2][4] = hi.x; hv[gi][c2][5] = hi.y; hv[gi][c2][6] = hi.z; hv[gi][c2][7] = hi.w;
+            }
+#pragma unroll
+        for (int gi = 0; gi < GW; ++gi)
+#pragma unroll
+            for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+                for (int i = 0; i < 8; ++i) hv[gi][c2][i] = live ? hv[gi][c2][i] : 0.f;
+    };
+    // order of issue: the first tile's slot lookup, the weights, then the h
+    // that needs the slot (its wait then covers the lookup alone)
+    int slot = plan_slot(plan, wk, r16 < wk.count ? r16 : wk.count - 1, n_slots);
+    __builtin_amdgcn_sched_barrier(0);
+
     // this wave's weights: word kq of chunks 2g, 2g + 1 of each row tile
     uint32_t wa[GW][RT][2];
 #pragma unroll
@@ -997,6 +1055,9 @@ __global__ __launch_bounds__(NW * kWave) void down_mfma_kernel(const uint32_t *_
                 const int c = 2 * (g0 + gi) + c2;
                 wa[gi][t][c2] = __builtin_nontemporal_load(q + (((size_t)wk.e * C + c) * H + m0 + 16 * t + r16) * 4 + kq);
             }
+    __builtin_amdgcn_sched_barrier(0);
+    slot = r16 < wk.count ? slot : 0;
+    load_h(slot, r16 < wk.count);
     // per [group][row]: 16 * scale, and bias - 16 * scale (the weights go
     // into the MFMA as 1 + q / 16)
     float *ss = smem, *sb = smem + G * ROWS;
@@ -1013,20 +1074,10 @@ __global__ __launch_bounds__(NW * kWave) void down_mfma_kernel(const uint32_t *_
     for (int t0 = 0; t0 < wk.count; t0 += kMfmaTokens) {
         const int nt = wk.count - t0 < kMfmaTokens ? wk.count - t0 : kMfmaTokens;
         const bool live = r16 < nt;  // this lane's token column
-        const int slot = live ? plan_slot(plan, wk, t0 + r16, n_slots) : 0;
-        const float *hr = h + (size_t)slot * F;
-        // h of the token: 8 values of chunk 2g and 8 of chunk 2g + 1 per group
-        float hv[GW][2][8];
-#pragma unroll
-        for (int gi = 0; gi < GW; ++gi)
-#pragma unroll
-            for (int c2 = 0; c2 < 2; ++c2) {
-                const float4 *p4 = (const float4 *)(hr + (2 * (g0 + gi) + c2) * 32 + 8 * kq);
-                const float4 lo = live ? p4[0] : make_float4(0.f, 0.f, 0.f, 0.f);
-                const float4 hi = live ? p4[1] : make_float4(0.f, 0.f, 0.f, 0.f);
-                hv[gi][c2][0] = lo.x; hv[gi][c2][1] = lo.y; hv[gi][c2][2] = lo.z; hv[gi][c2][3] = lo.w;
-                hv[gi][c2][4] = hi.x; hv[gi][c2][5] = hi.y; hv[gi][c2][6] = hi.z; hv[gi][c2][7] = hi.w;
-            }
+        if (t0 > 0) {
+            slot = live ? plan_slot(plan, wk, t0 + r16, n_slots) : 0;
+            load_h(slot, live);
+        }
         f32x4_t acc[RT];
 #pragma unroll
         for (int t = 0; t < RT; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -1068,16 +1119,16 @@ __global__ __launch_bounds__(NW * kWave) void down_mfma_kernel(const uint32_t *_
 #pragma unroll
             for (int i = 0; i < 4; ++i) mine[t * 4 + i] = acc[t][i];
         __syncthreads();
-        if (wave == 0 && live) {  // add the partials in wave order
+        // add the partials in wave order: output o = (row tile, row of the
+        // lane's four) goes to wave o % NW
+        if (live) {
+            for (int o = wave; o < 4 * RT; o += NW) {
+                const int t = o / 4, i = o % 4;
+                float v = 0.f;
 #pragma unroll
-            for (int t = 0; t < RT; ++t)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    float v = 0.f;
-#pragma unroll
-                    for (int w = 0; w < NW; ++w) v += part[((size_t)w * kWave + lane) * (4 * RT) + t * 4 + i];
-                    y[(size_t)slot * H + m0 + 16 * t + 4 * kq + i] = v;
-                }
+                for (int w = 0; w < NW; ++w) v += part[((size_t)w * kWave + lane) * (4 * RT) + t * 4 + i];
+                y[(size_t)slot * H + m0 + 16 * t + 4 * kq + i] = v;
+            }
         }
         __syncthreads();
     }
@@ -1578,7 +1629,6 @@ constexpr int kMfmaMinCount = 3;
 constexpr int kMfmaMinTokens = 16;
 // 16-row tiles per workgroup: two, or one where a wave's registers would not
 // hold two (more than eight waves, i.e. hidden above 2048).
-static int mfma_row_tiles(int nw) { return nw > 8 ? 1 : 2; }
 
 // Waves (NW) and 64-groups per wave (GW) of the MFMA gate+up kernel for a
 // hidden size; false when it has no instance.
@@ -1599,7 +1649,7 @@ static size_t mfma_gate_up_lds(const moe_layer_t *layer, int nw) {
 template <int LPR, int NV, int NW, int GW>
 static moe_status launch_gate_up_mixed_t(const moe_layer_t *layer, const GateUpArgs &ga, int groups_y,
                                          hipStream_t stream) {
-    constexpr int RT = NW <= 8 ? 2 : 1;
+    constexpr int RT = mfma_row_tiles(NW);
     constexpr int RI = gate_up_ri<LPR, NV>();
     const int rb_mfma = (layer->dff + 16 * RT - 1) / (16 * RT);
     const int rows_valu = (kWave / LPR) * RI;
@@ -1658,7 +1708,7 @@ static moe_status enqueue_gate_up(const moe_layer_t *layer, const void *x, int n
     switch (nw * 100 + gw) {
 #define MOE_GUM(NW, GW)                                                                                  \
     case NW * 100 + GW:                                                                                  \
-        hipLaunchKernelGGL((gate_up_mfma_kernel<NW, GW, NW <= 8 ? 2 : 1>), grid, dim3(NW * kWave), lds, stream, \
+        hipLaunchKernelGGL((gate_up_mfma_kernel<NW, GW, mfma_row_tiles(NW)>), grid, dim3(NW * kWave), lds, stream, \
                            ga, kMfmaMinCount);                                                           \
         break;
         MOE_GUM(1, 4) MOE_GUM(2, 4) MOE_GUM(4, 4) MOE_GUM(6, 4) MOE_GUM(8, 4) MOE_GUM(12, 4) MOE_GUM(16, 4)

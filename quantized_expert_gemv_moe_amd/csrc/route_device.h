@@ -85,31 +85,52 @@ __device__ __forceinline__ int route_take(uint32_t *key, uint32_t *best) {
     return win;
 }
 
-// Top-k of one token's logits by the calling wave: top_k selection rounds.
-// Lane j < top_k returns the j-th expert id in *id and its weight in *w
-// (softmax of the kept logits relative to the largest, the denominator
-// summed in j order); returns false for lanes j >= top_k.
+// Top-k of NT tokens at once from their order keys (route_keys): top_k
+// selection rounds per token, the tokens' rounds interleaved so their
+// dependent exchange chains overlap.  Lane j < top_k gets token n's j-th
+// expert id in id[n] and its weight in w[n] (softmax of the kept logits
+// relative to the largest, the denominator summed in j order).
+template <int PER_LANE, int NT>
+__device__ __forceinline__ void route_select(uint32_t (*key)[PER_LANE], int top_k, int *id, float *w) {
+    const int lane = threadIdx.x & (kWave - 1);
+    uint32_t mine[NT];
+    int mine_id[NT];
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+        mine[n] = 0u;
+        mine_id[n] = 0;
+    }
+    for (int j = 0; j < top_k; ++j) {
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+            uint32_t best;
+            const int win = route_take<PER_LANE>(key[n], &best);
+            mine[n] = lane == j ? best : mine[n];
+            mine_id[n] = lane == j ? win : mine_id[n];
+        }
+    }
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+        const float v = key_value(mine[n]);
+        const float v0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+        const float ex = lane < top_k ? expf(v - v0) : 0.f;
+        float den = 0.f;
+        for (int j = 0; j < top_k; ++j) den += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ex), j));
+        id[n] = mine_id[n];
+        w[n] = ex / den;
+    }
+}
+
+// Top-k of one token's logits by the calling wave.  Lane j < top_k returns
+// the j-th expert id in *id and its weight in *w; returns false for lanes
+// j >= top_k.
 template <int PER_LANE>
 __device__ __forceinline__ bool route_token(const float *__restrict__ row, int n_experts, int top_k,
                                             int *id, float *w) {
     const int lane = threadIdx.x & (kWave - 1);
-    uint32_t key[PER_LANE];
-    route_keys<PER_LANE>(row, n_experts, key);
-    uint32_t mine = 0u;
-    int mine_id = 0;
-    for (int j = 0; j < top_k; ++j) {
-        uint32_t best;
-        const int win = route_take<PER_LANE>(key, &best);
-        mine = lane == j ? best : mine;
-        mine_id = lane == j ? win : mine_id;
-    }
-    const float v = key_value(mine);
-    const float v0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
-    const float ex = lane < top_k ? expf(v - v0) : 0.f;
-    float den = 0.f;
-    for (int j = 0; j < top_k; ++j) den += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ex), j));
-    *id = mine_id;
-    *w = ex / den;
+    uint32_t key[1][PER_LANE];
+    route_keys<PER_LANE>(row, n_experts, key[0]);
+    route_select<PER_LANE, 1>(key, top_k, id, w);
     return lane < top_k;
 }
 
