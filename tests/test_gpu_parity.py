@@ -112,6 +112,9 @@ def test_plan_matches_oracle(E, k, B, kind):
     (128, 8, 1, "normal"), (8, 2, 1, "normal"), (128, 8, 4, "sharing"), (128, 8, 32, "zipf"),
     (256, 6, 4, "normal"), (1024, 16, 64, "normal"), (128, 8, 65, "normal"), (64, 16, 200, "normal"),
     (1, 1, 3, "normal"),
+    # more tokens than the workgroup's 16 waves: two tokens per wave routed
+    # together, with a lone last token on some waves
+    (128, 8, 17, "normal"), (128, 8, 47, "zipf"), (64, 4, 33, "same"), (256, 6, 50, "sharing"),
 ])
 def test_route_plan_matches_oracle(E, k, B, regime):
     """The fused router+planner (one workgroup up to 64 tokens, two kernels beyond)."""
@@ -216,6 +219,26 @@ def test_decode_step_column_layout_geometries(H, F, E, k):
     x = make_x(sh, B, seed=H * F)
     run = GpuRun(L, x, lg, cols=True)
     check_against_oracle(L, x, lg, run, f"cols {H}x{F}x{E}x{k}")
+
+
+@pytest.mark.parametrize("H,F,E,k,B,regime", [
+    (2048, 768, 128, 8, 12, "same"),    # 8 waves, 4-slot stages: every expert holds all 12 tokens
+    (2048, 768, 128, 8, 9, "sharing"),  # stages of 1..4 slots
+    (512, 2048, 16, 4, 10, "same"),     # 16 waves, 2-slot stages: five stages per expert
+    (256, 1536, 8, 2, 11, "normal"),    # 16 waves x 3 chunks
+    (128, 896, 8, 2, 13, "same"),       # 4 waves x 7 chunks: four groups per wave and slot
+])
+def test_column_down_in_stages(H, F, E, k, B, regime):
+    """The column-layout down kernel between 9 and 15 tokens (no MFMA, no
+    token-major kernel): every expert's slots in stages, each stage's h
+    groups fetched at once and read back from per-wave LDS rows."""
+    sh = Shape(f"c{H}x{F}", 41, H, F, E, k, "bf16")
+    log(f"[case] column down stages {H}x{F}x{E}x{k} B={B} {regime}")
+    lg = make_logits(sh, B, regime=regime, seed=F + B)
+    L = layer_for(sh, lg, seed=F + B) if E > 8 else make_layer(sh, seed=F + B)
+    x = make_x(sh, B, seed=F + B)
+    run = GpuRun(L, x, lg, cols=True)
+    check_against_oracle(L, x, lg, run, f"cols stages {H}x{F}x{E}x{k} B{B} {regime}")
 
 
 @pytest.mark.parametrize("layout", ["rows", "cols"])
