@@ -89,9 +89,11 @@ typedef enum { MOE_ACT_SWIGLU = 0, MOE_ACT_GEGLU = 1 } moe_activation;
  * patterns, [expert][out][in/group_size].
  *   gate, up : out = dff,    in = hidden
  *   down     : out = hidden, in = dff
- * Layers with 4-bit gate, up and down in groups of 64 run the specialised
- * kernels (either down layout, MFMA for large batches); every other format
- * runs the generic row kernels and needs MOE_DOWN_ROWS.
+ * Each projection picks its kernels by its own width: 4-bit gate and up in
+ * groups of 64 run the specialised gate+up kernels (MFMA for large
+ * batches), 4-bit down in groups of 64 the specialised down kernels (either
+ * down layout); a projection of any other width or group size runs the
+ * generic row kernels, and a down projection on them needs MOE_DOWN_ROWS.
  * Every `*_q` pointer must be 16-byte aligned, every scale/bias pointer
  * 4-byte aligned.  The struct itself lives in host memory; the pointers it
  * holds are device pointers.

@@ -78,14 +78,16 @@ moe_status check_layer(const moe_layer_t *L) {
     if (L->down_scale && !aligned(L->down_scale, 4)) return MOE_ERR_INVALID_ARG;
     if (L->activation != MOE_ACT_SWIGLU && L->activation != MOE_ACT_GEGLU) return MOE_ERR_INVALID_ARG;
     if (L->down_layout != MOE_DOWN_ROWS && L->down_layout != MOE_DOWN_COLS) return MOE_ERR_INVALID_ARG;
-    if (!fast_format(L)) {  // the generic row kernels
-        int lpr, upl;
-        if (L->down_layout != MOE_DOWN_ROWS) return MOE_ERR_UNSUPPORTED;
-        if (!pick_generic(L->hidden, &lpr, &upl) || !pick_generic(L->dff, &lpr, &upl)) return MOE_ERR_UNSUPPORTED;
-        return MOE_OK;
-    }
+    // each projection by its own width: specialised kernels for 4-bit in
+    // groups of 64, the generic row kernels otherwise
     Geometry g;
-    if (!pick_geometry_gate_up(L->hidden, &g)) return MOE_ERR_UNSUPPORTED;
+    int lpr, upl;
+    if (fast_gate_up(L) ? !pick_geometry_gate_up(L->hidden, &g) : !pick_generic(L->hidden, &lpr, &upl))
+        return MOE_ERR_UNSUPPORTED;
+    if (!fast_down(L)) {
+        if (L->down_layout != MOE_DOWN_ROWS) return MOE_ERR_UNSUPPORTED;
+        return pick_generic(L->dff, &lpr, &upl) ? MOE_OK : MOE_ERR_UNSUPPORTED;
+    }
     if (L->down_layout == MOE_DOWN_ROWS) {
         if (!pick_geometry(L->dff, &g)) return MOE_ERR_UNSUPPORTED;
     } else if (L->down_layout == MOE_DOWN_COLS) {

@@ -1683,7 +1683,7 @@ static moe_status enqueue_gate_up(const moe_layer_t *layer, const void *x, int n
                                   const moe_plan_t *plan, void *workspace, hipStream_t stream) {
     const Workspace ws = workspace_layout(layer, n_tokens);
     float *h = (float *)((char *)workspace + ws.h_off);
-    if (!fast_format(layer)) return launch_generic_gate_up(layer, x, n_tokens, plan, h, stream);
+    if (!fast_gate_up(layer)) return launch_generic_gate_up(layer, x, n_tokens, plan, h, stream);
     Geometry gu;
     pick_geometry_gate_up(layer->hidden, &gu);
     int nw = 0, gw = 0;
@@ -1771,7 +1771,7 @@ static moe_status enqueue_down_combine(const moe_layer_t *layer, int n_tokens, c
     const float *h = (const float *)((char *)workspace + ws.h_off);
     float *y = (float *)((char *)workspace + ws.y_off);
     moe_status st;
-    const bool fast = fast_format(layer);
+    const bool fast = fast_down(layer);
     if (fast && n_tokens <= kTokenMajorMaxTokens) {
         st = launch_down_token(layer, n_tokens, h, topk_idx, topk_w, residual, out, stream);
         if (st != MOE_ERR_UNSUPPORTED) return st;
@@ -1872,7 +1872,7 @@ extern "C" moe_status moe_route_gate_up(const moe_layer_t *layer, const float *l
     if ((st = check_x(x)) != MOE_OK) return st;
     hipStream_t stream = (hipStream_t)hip_stream;
     const int pl = per_lane_bucket(layer->n_experts);
-    if (!fast_format(layer) || n_tokens > kRouteMaxTokens || pl > 4 || n_tokens * layer->top_k > kWave) {
+    if (!fast_gate_up(layer) || n_tokens > kRouteMaxTokens || pl > 4 || n_tokens * layer->top_k > kWave) {
         // router + planner launch, then the deduplicated gate+up
         st = moe_route_plan(logits, n_tokens, layer->n_experts, layer->top_k, topk_idx, topk_w, plan, hip_stream);
         if (st != MOE_OK) return st;

@@ -201,7 +201,8 @@ __global__ __launch_bounds__(kGenBlock) void generic_rows_kernel(GenericArgs a) 
 
 // ------------------------------------------------------------- host side
 
-bool fast_format(const moe_layer_t *L) { return L->bits == 4 && L->down_bits == 4 && L->group_size == 64; }
+bool fast_gate_up(const moe_layer_t *L) { return L->bits == 4 && L->group_size == 64; }
+bool fast_down(const moe_layer_t *L) { return L->down_bits == 4 && L->group_size == 64; }
 
 // Lanes per row and units per lane for rows of K inputs: the most lanes (a
 // power of two up to 64) dividing K/16 units with at most kGenMaxUpl units

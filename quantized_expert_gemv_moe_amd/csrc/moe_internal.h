@@ -23,11 +23,14 @@ bool pick_geometry_gate_up(int K, Geometry *g);
 // kernel; false when that layout has no kernel for this dff.
 bool pick_down_cols(int dff, int *nw, int *cpw);
 
-// Weight formats: the 4-bit / group-64 kernels serve layers with 4-bit gate,
-// up and down in groups of 64; every other width or group size takes the
-// generic row kernels (rows layout only).  pick_generic gives their lanes per
-// row and 16-input units per lane for rows of K inputs.
-bool fast_format(const moe_layer_t *layer);
+// Weight formats, per projection: gate and up in 4 bits and groups of 64
+// take the specialised gate+up kernels (fast_gate_up), a down projection in
+// 4 bits and groups of 64 the specialised down kernels (fast_down); any other
+// width or group size takes the generic row kernels (rows layout only for
+// down).  pick_generic gives their lanes per row and 16-input units per lane
+// for rows of K inputs.
+bool fast_gate_up(const moe_layer_t *layer);
+bool fast_down(const moe_layer_t *layer);
 bool pick_generic(int K, int *lpr, int *upl);
 moe_status launch_generic_gate_up(const moe_layer_t *layer, const void *x, int n_tokens,
                                   const moe_plan_t *plan, float *h, hipStream_t stream);

@@ -69,6 +69,10 @@ def test_layer_check_accepts_the_workload_shapes():
     for bits, down_bits, group in ((8, 8, 64), (4, 6, 64), (6, 6, 32), (8, 4, 128), (4, 4, 32), (4, 4, 128)):
         assert check(bits=bits, down_bits=down_bits, group_size=group) == moe.MOE_OK
     assert check(hidden=4096, dff=2048, bits=6, down_bits=8, group_size=128) == moe.MOE_OK
+    # each projection by its own width: a 4-bit group-64 down projection keeps
+    # the column layout under generic gate+up kernels
+    assert check(bits=8, down_layout=moe.MOE_DOWN_COLS) == moe.MOE_OK
+    assert check(bits=6, hidden=4096, dff=2048, down_layout=moe.MOE_DOWN_COLS) == moe.MOE_OK
 
 
 @pytest.mark.parametrize("kw,want", [
@@ -79,7 +83,8 @@ def test_layer_check_accepts_the_workload_shapes():
     (dict(group_size=16), moe.MOE_ERR_UNSUPPORTED),
     (dict(group_size=48), moe.MOE_ERR_UNSUPPORTED),
     (dict(dff=704, group_size=128), moe.MOE_ERR_UNSUPPORTED),          # group does not divide dff
-    (dict(bits=8, down_layout=moe.MOE_DOWN_COLS), moe.MOE_ERR_UNSUPPORTED),  # generic kernels: rows only
+    (dict(down_bits=8, down_layout=moe.MOE_DOWN_COLS), moe.MOE_ERR_UNSUPPORTED),  # generic down: rows only
+    (dict(group_size=32, down_layout=moe.MOE_DOWN_COLS), moe.MOE_ERR_UNSUPPORTED),
     (dict(group_size=32, hidden=320 * 4, dff=320), moe.MOE_ERR_UNSUPPORTED),   # 20 units: no lane split
     (dict(bits=8, hidden=16384), moe.MOE_ERR_UNSUPPORTED),             # 1024 units: over 8 per lane
     (dict(hidden=2000), moe.MOE_ERR_UNSUPPORTED),

@@ -422,6 +422,25 @@ def test_other_widths_on_the_wide_layer_with_geglu_and_sidecars(bits, down_bits,
     check_against_oracle(L, x, lg, run, f"wide w{bits}/{down_bits}g{group}")
 
 
+@pytest.mark.parametrize("bits,down_bits,layout,B", [
+    (8, 4, "cols", 1), (8, 4, "cols", 4), (8, 4, "cols", 12), (8, 4, "cols", 20), (8, 4, "rows", 8),
+    (4, 8, "rows", 1), (4, 8, "rows", 8), (4, 8, "rows", 20),
+])
+def test_mixed_width_layers_take_each_projections_kernels(bits, down_bits, layout, B):
+    """Group-64 layers with one projection in 4 bits: the 4-bit projection
+    runs the specialised kernels (the routing gate+up kernel at few tokens,
+    MFMA from 16 tokens, the token-major or column-layout down kernels), the
+    other the generic row kernels; results against the oracle."""
+    import dataclasses
+    sh = dataclasses.replace(SHAPES["cohort"], bits=bits, down_bits=down_bits, group_size=64)
+    log(f"[case] mixed widths {bits}/{down_bits} {layout} B={B}")
+    lg = make_logits(sh, B, regime="sharing", seed=bits + B)
+    L = layer_for(sh, lg, seed=bits + B)
+    x = make_x(sh, B, seed=bits + B)
+    run = GpuRun(L, x, lg, cols=layout == "cols")
+    check_against_oracle(L, x, lg, run, f"mixed {bits}/{down_bits} {layout} B{B}")
+
+
 def test_other_widths_batch_invariance_and_entry_points():
     """A token alone equals the same token in a batch bit for bit; the
     two-call path equals moe_decode_layer; the column layout is refused."""
