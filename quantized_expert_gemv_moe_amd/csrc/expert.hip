@@ -1726,8 +1726,10 @@ static moe_status enqueue_gate_up(const moe_layer_t *layer, const void *x, int n
 constexpr int kTokenMajorMaxTokens = 8;
 
 // The MFMA down kernel: waves (NW) and 64-groups per wave (GW) for a dff,
-// 16-row tiles per workgroup; false when it has no instance.
-constexpr int kMfmaDownRowTiles = 4;
+// 16-row tiles per workgroup (two: measured against one, four and eight at
+// 32 and 256 tokens, more workgroups in flight beat fewer h re-reads); false
+// when it has no instance.
+constexpr int kMfmaDownRowTiles = 2;
 static bool mfma_down_shape(const moe_layer_t *layer, int *nw, int *gw) {
     if (layer->down_layout != MOE_DOWN_COLS || layer->dff % kGroup) return false;
     if (layer->hidden % (16 * kMfmaDownRowTiles)) return false;
