@@ -29,8 +29,9 @@ capturing stream):
 The oracle (plain fp64 C, OpenMP) is timed on a bounded sample of the same
 workload on the host cores (rank 0, N = 1 only).
 
-Prints ONE JSON line.  ``--gpus N`` with N > 1 exits: this build runs on
-one GPU.
+Prints ONE JSON line.  ``--gpus N`` with N > 1 exits: the library and its
+benchmark run on one GPU (how the path would shard is described, not
+implemented).
 """
 
 from __future__ import annotations
@@ -385,8 +386,8 @@ def copy_calibration():
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported by this build "
-              "(the multi-GPU sharding is a design note, not code)", file=sys.stderr, flush=True)
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(multi-GPU sharding is described, not implemented)", file=sys.stderr, flush=True)
         sys.exit(2)
     import torch
 

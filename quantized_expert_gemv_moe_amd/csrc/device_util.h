@@ -9,9 +9,11 @@ namespace moe {
 constexpr int kWave = 64;      // CDNA wavefront width
 constexpr int kBlock = 256;    // four waves per workgroup
 constexpr int kGroup = 64;     // quantisation group along the input dimension
-// batches routed and planned by one workgroup in moe_route_plan
-constexpr int kRoutePlanMaxTokens = 64;
-constexpr int kRoutePlanMaxSlots = 2048;
+// batches routed and planned by one workgroup in moe_route_plan: one wave
+// per token (at 32 tokens the router kernel on many workgroups plus the
+// planner measured faster than one workgroup routing two tokens per wave)
+constexpr int kRoutePlanMaxTokens = 16;
+constexpr int kRoutePlanMaxSlots = kRoutePlanMaxTokens * 16;  // top_k <= 16
 
 // fp16 bit pattern -> fp32 (exact; v_cvt_f32_f16).
 __device__ __forceinline__ float f16_bits_to_f32(uint16_t b) {

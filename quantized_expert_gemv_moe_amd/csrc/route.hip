@@ -75,36 +75,13 @@ __global__ __launch_bounds__(kRoutePlanThreads) void route_plan_kernel(const flo
     __shared__ int idx_lds[kRoutePlanMaxSlots];
     const int lane = threadIdx.x & (kWave - 1);
     const int n_waves = blockDim.x / kWave;
-    // With more tokens than waves, tokens t and t + n_waves go together: both
-    // rows' logits in flight at once and their selection rounds interleaved
-    // (a lone last token is routed twice, the second copy dropped).
-    const int t_step = n_tokens > n_waves ? 2 * n_waves : n_waves;
-    for (int t = threadIdx.x / kWave; t < n_tokens && n_tokens <= n_waves; t += n_waves) {
+    for (int t = threadIdx.x / kWave; t < n_tokens; t += n_waves) {  // one wave per token
         int id;
         float w;
         if (route_token<PER_LANE>(logits + (size_t)t * n_experts, n_experts, top_k, &id, &w)) {
             topk_idx[(size_t)t * top_k + lane] = id;
             topk_w[(size_t)t * top_k + lane] = w;
             idx_lds[t * top_k + lane] = id;
-        }
-    }
-    for (int t = threadIdx.x / kWave; t < n_tokens && n_tokens > n_waves; t += t_step) {
-        const int t2 = t + n_waves < n_tokens ? t + n_waves : t;
-        uint32_t key[2][PER_LANE];
-        route_keys<PER_LANE>(logits + (size_t)t * n_experts, n_experts, key[0]);
-        route_keys<PER_LANE>(logits + (size_t)t2 * n_experts, n_experts, key[1]);
-        int id[2];
-        float w[2];
-        route_select<PER_LANE, 2>(key, top_k, id, w);
-        if (lane < top_k) {
-            topk_idx[(size_t)t * top_k + lane] = id[0];
-            topk_w[(size_t)t * top_k + lane] = w[0];
-            idx_lds[t * top_k + lane] = id[0];
-            if (t2 != t) {
-                topk_idx[(size_t)t2 * top_k + lane] = id[1];
-                topk_w[(size_t)t2 * top_k + lane] = w[1];
-                idx_lds[t2 * top_k + lane] = id[1];
-            }
         }
     }
     __syncthreads();

@@ -112,12 +112,12 @@ def test_plan_matches_oracle(E, k, B, kind):
     (128, 8, 1, "normal"), (8, 2, 1, "normal"), (128, 8, 4, "sharing"), (128, 8, 32, "zipf"),
     (256, 6, 4, "normal"), (1024, 16, 64, "normal"), (128, 8, 65, "normal"), (64, 16, 200, "normal"),
     (1, 1, 3, "normal"),
-    # more tokens than the workgroup's 16 waves: two tokens per wave routed
-    # together, with a lone last token on some waves
+    # just past the fused kernel's 16 tokens (the router and planner kernels),
+    # odd counts and tied logits
     (128, 8, 17, "normal"), (128, 8, 47, "zipf"), (64, 4, 33, "same"), (256, 6, 50, "sharing"),
 ])
 def test_route_plan_matches_oracle(E, k, B, regime):
-    """The fused router+planner (one workgroup up to 64 tokens, two kernels beyond)."""
+    """The fused router+planner (one workgroup up to 16 tokens, two kernels beyond)."""
     sh = Shape("rp", 33, 64, 64, E, k, "f32")
     lg = make_logits(sh, B, regime=regime, seed=E * k + B)
     idx, w, plan = moe.route_plan(torch.from_numpy(lg).cuda(), k)
