@@ -460,6 +460,7 @@ def main():
             ladder.append({"workload": wl, "B": b2, "steps_per_s": 1.0 / st, "us_per_step": st * 1e6,
                            "tokens_per_s": b2 / st,
                            "unique_experts": nu2, "unique_gbps": unique_bytes(s2h, nu2) / st / 1e9,
+                           "hbm_frac": unique_bytes(s2h, nu2) / st / 1e9 / HBM_PEAK_GBPS,
                            "expert_tflops": tflops,
                            "step_time_vs_B1": st / (secs / args.steps)})
             log(f"[bench] ladder {wl}: {st * 1e6:.2f} us/step, n_unique {nu2:.1f}, "
