@@ -186,10 +186,10 @@ moe_status moe_expert_plan(const int32_t *topk_idx, int32_t n_tokens, int32_t n_
                            int32_t top_k, const moe_plan_t *plan, void *hip_stream);
 
 /*
- * Router and planner of one step in a single launch (one workgroup) when
- * n_tokens <= 64 and n_tokens*top_k <= 2048; larger batches run the two
- * kernels of moe_route_topk and moe_expert_plan.  Same arguments and results
- * as those two calls.
+ * Router and planner of one step in a single launch (one workgroup, one
+ * wave per token) when n_tokens <= 16; larger batches run the two kernels of
+ * moe_route_topk and moe_expert_plan.  Same arguments and results as those
+ * two calls.
  */
 moe_status moe_route_plan(const float *logits, int32_t n_tokens, int32_t n_experts, int32_t top_k,
                           int32_t *topk_idx, float *topk_w, const moe_plan_t *plan,
