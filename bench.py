@@ -78,6 +78,10 @@ def parse():
     ap.add_argument("--steps", type=int, default=480)
     ap.add_argument("--warmup", type=int, default=48)
     ap.add_argument("--workload", default="decode", choices=sorted(WORKLOADS))
+    ap.add_argument("--regime", default=None,
+                    help="routing regime override (normal, sharing, disjoint, zipf, same)")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="only the headline steps of the workload (for profiler runs)")
     ap.add_argument("--layers", type=int, default=0, help="rotation length (default: >= 1 GB touched)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -403,6 +407,9 @@ def main():
         return
 
     shape_name, B, regime, desc = WORKLOADS[args.workload]
+    if args.regime:
+        regime = args.regime
+        desc = f"{desc} ({regime} routing)"
     sh = SHAPES[shape_name]
     per_layer = sh.n_experts * 3 * sh.hidden * sh.dff * BYTES_PER_WEIGHT
     R = args.layers or max(8, min(48, int(math.ceil(16.3e9 / per_layer))))
@@ -417,6 +424,11 @@ def main():
     gbps = ub / (secs / args.steps) / 1e9
     log(f"[bench] {args.workload}: {ms * 1e3:.2f} us/step, {steps_per_s:.0f} steps/s, "
         f"unique {ub / 1e6:.2f} MB/step -> {gbps:.0f} GB/s ({gbps / HBM_PEAK_GBPS:.1%} of peak); wall {wall:.2f}s")
+
+    if args.headline_only:
+        print(json.dumps({"workload": args.workload, "regime": regime, "us_per_step": ms * 1e3,
+                          "unique_experts": avg_unique, "unique_gbps": gbps}), flush=True)
+        return
 
     kt = run_kernel_pass(rot)
     gu_bytes = gate_up_bytes(sh, avg_unique)

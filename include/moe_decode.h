@@ -238,8 +238,15 @@ size_t moe_workspace_size(const moe_layer_t *layer, int32_t max_tokens);
  *
  * The fp32 partials with one final rounding follow page "perf(moe):
  * batched decode scales 1.55x against 3.25x on dense", Implementation
- * Notes.  A token's result depends only on that token (bitwise the same
- * whatever else is in the batch), and repeated calls are bitwise equal.
+ * Notes.  Repeated calls are bitwise equal.  Batch invariance: below 16
+ * tokens a token's result depends only on that token (bitwise the same
+ * whatever else is in the batch).  From 16 tokens up, an expert that holds
+ * 3 or more of the batch's tokens runs on the MFMA kernels, which add the
+ * same exact fp32 products in another order; a token routed to such an
+ * expert may then differ from its single-token result by fp32 rounding
+ * only (relative L2 within 5e-4 of each other, both within the output
+ * tolerance of the fp64 definition).  Tokens whose experts all hold fewer
+ * than 3 tokens stay bitwise equal.
  */
 moe_status moe_decode_step(const moe_layer_t *layer, const void *x, int32_t n_tokens,
                            const int32_t *topk_idx, const float *topk_w,
@@ -256,10 +263,12 @@ moe_status moe_decode_step(const moe_layer_t *layer, const void *x, int32_t n_to
  * expert gather", Proposed Solution); at a few tokens each of those is a
  * short, latency-bound kernel.  So a batch of up to 8 tokens (with at most
  * 256 experts and n_tokens * top_k <= 64) takes two launches
- * instead of three or more: every gate+up wave selects its own expert from
- * the logits (one block also writes topk_idx, topk_w and the plan), and one
- * kernel does the down projection and the combine, token by token.  Results
- * are bitwise those of the longer path.
+ * instead of three or more: the gate+up workgroups select their own expert
+ * from the logits and, with more than one token, deduplicate among
+ * themselves so each distinct expert's gate and up rows are streamed once
+ * for every token routed to it (one block also writes topk_idx, topk_w and
+ * the plan); then one kernel does the down projection and the combine,
+ * token by token.  Results are bitwise those of the longer path.
  */
 moe_status moe_decode_layer(const moe_layer_t *layer, const float *logits, const void *x,
                             int32_t n_tokens, int32_t *topk_idx, float *topk_w,

@@ -130,6 +130,61 @@ def _stream(stream) -> C.c_void_p:
     return C.c_void_p(stream.cuda_stream)
 
 
+# ------------------------------------------------------- argument checks
+# The C ABI validates everything it can see on the host (shapes in the layer
+# struct, alignment, workspace size); the extents and dtypes of the device
+# buffers it is handed are the caller's contract.  These checks hold every
+# tensor to that contract before the call, so a wrong-sized buffer raises
+# here instead of reaching a kernel.
+def _act_dtype(layer: "DeviceLayer"):
+    return torch.bfloat16 if layer.act_dtype == MOE_DTYPE_BF16 else torch.float32
+
+
+def _need(t: Optional[torch.Tensor], name: str, dtype, shape):
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if t.dtype != dtype or tuple(t.shape) != tuple(shape) or not t.is_contiguous() or not t.is_cuda:
+        raise ValueError(f"{name} must be a contiguous {dtype} device tensor of shape {tuple(shape)}, "
+                         f"got {t.dtype} {tuple(t.shape)}")
+
+
+def _check_x(layer: "DeviceLayer", x: torch.Tensor, name: str = "x") -> int:
+    if x is None or x.dim() != 2:
+        raise ValueError(f"{name} must be a [B, hidden] tensor")
+    _need(x, name, _act_dtype(layer), (x.shape[0], layer.hidden))
+    return x.shape[0]
+
+
+def _check_routing(layer: "DeviceLayer", B: int, idx: torch.Tensor, w: torch.Tensor):
+    _need(idx, "idx", torch.int32, (B, layer.top_k))
+    _need(w, "w", torch.float32, (B, layer.top_k))
+
+
+def _check_plan(layer: "DeviceLayer", plan: "Plan", B: int):
+    E = layer.n_experts
+    if (plan.counts.numel() < E or plan.offsets.numel() < E + 1 or plan.unique_experts.numel() < E
+            or plan.work.numel() < 4 * E or plan.sorted_slots.numel() < B * layer.top_k):
+        raise ValueError("plan buffers are too small for this layer and batch")
+    for t in (plan.counts, plan.offsets, plan.sorted_slots, plan.unique_experts, plan.n_unique, plan.work):
+        if t.dtype != torch.int32 or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError("plan buffers must be contiguous int32 device tensors")
+
+
+def _check_out(layer: "DeviceLayer", B: int, out: torch.Tensor, residual: Optional[torch.Tensor]):
+    _need(out, "out", _act_dtype(layer), (B, layer.hidden))
+    if residual is not None:
+        _need(residual, "residual", _act_dtype(layer), (B, layer.hidden))
+
+
+def _check_workspace(layer: "DeviceLayer", B: int, workspace: torch.Tensor):
+    if workspace is None or not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous device tensor")
+    need = workspace_size(layer, B)
+    have = workspace.numel() * workspace.element_size()
+    if have < need:
+        raise ValueError(f"workspace holds {have} bytes, {need} needed for {B} tokens")
+
+
 # ------------------------------------------------------------------- layer
 @dataclass
 class DeviceLayer:
@@ -325,14 +380,15 @@ def decode_step(layer: DeviceLayer, x: torch.Tensor, idx: torch.Tensor, w: torch
                 out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
                 residual: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """moe_decode_step: x [B,H] (bf16 or fp32 per the layer) -> out [B,H]."""
-    want = torch.bfloat16 if layer.act_dtype == MOE_DTYPE_BF16 else torch.float32
-    if x.dtype != want or x.dim() != 2 or not x.is_contiguous():
-        raise ValueError(f"x must be a contiguous {want} [B, H] tensor")
-    B = x.shape[0]
+    B = _check_x(layer, x)
+    _check_routing(layer, B, idx, w)
+    _check_plan(layer, plan, B)
     if out is None:
         out = torch.empty_like(x)
+    _check_out(layer, B, out, residual)
     if workspace is None:
         workspace = alloc_workspace(layer, B, device=x.device)
+    _check_workspace(layer, B, workspace)
     _check(lib().moe_decode_step(C.byref(layer.struct), _ptr(x), B, _ptr(idx), _ptr(w), C.byref(plan.struct),
                                  _ptr(residual), _ptr(out), _ptr(workspace), workspace.numel(),
                                  _stream(stream)), "moe_decode_step")
@@ -342,6 +398,11 @@ def decode_step(layer: DeviceLayer, x: torch.Tensor, idx: torch.Tensor, w: torch
 def route_gate_up(layer: DeviceLayer, x: torch.Tensor, logits: torch.Tensor, idx: torch.Tensor, w: torch.Tensor,
                   plan: Plan, workspace: torch.Tensor, stream=None):
     """moe_route_gate_up: first half of decode_layer (routing, plan, h into the workspace)."""
+    B = _check_x(layer, x)
+    _need(logits, "logits", torch.float32, (B, layer.n_experts))
+    _check_routing(layer, B, idx, w)
+    _check_plan(layer, plan, B)
+    _check_workspace(layer, B, workspace)
     _check(lib().moe_route_gate_up(C.byref(layer.struct), _ptr(logits), _ptr(x), x.shape[0], _ptr(idx), _ptr(w),
                                    C.byref(plan.struct), _ptr(workspace), workspace.numel(), _stream(stream)),
            "moe_route_gate_up")
@@ -350,6 +411,9 @@ def route_gate_up(layer: DeviceLayer, x: torch.Tensor, logits: torch.Tensor, idx
 
 def expert_gate_up(layer: DeviceLayer, x: torch.Tensor, plan: Plan, workspace: torch.Tensor, stream=None):
     """moe_expert_gate_up: first half of decode_step (h into the workspace)."""
+    B = _check_x(layer, x)
+    _check_plan(layer, plan, B)
+    _check_workspace(layer, B, workspace)
     _check(lib().moe_expert_gate_up(C.byref(layer.struct), _ptr(x), x.shape[0], C.byref(plan.struct),
                                     _ptr(workspace), workspace.numel(), _stream(stream)), "moe_expert_gate_up")
 
@@ -358,6 +422,11 @@ def expert_down_combine(layer: DeviceLayer, n_tokens: int, idx: torch.Tensor, w:
                         out: torch.Tensor, workspace: torch.Tensor, residual: Optional[torch.Tensor] = None,
                         stream=None):
     """moe_expert_down_combine: second half of decode_step."""
+    B = int(n_tokens)
+    _check_routing(layer, B, idx, w)
+    _check_plan(layer, plan, B)
+    _check_out(layer, B, out, residual)
+    _check_workspace(layer, B, workspace)
     _check(lib().moe_expert_down_combine(C.byref(layer.struct), n_tokens, _ptr(idx), _ptr(w), C.byref(plan.struct),
                                          _ptr(residual), _ptr(out), _ptr(workspace), workspace.numel(),
                                          _stream(stream)), "moe_expert_down_combine")
@@ -369,14 +438,9 @@ def decode_layer(layer: DeviceLayer, x: torch.Tensor, logits: torch.Tensor, plan
                  residual: Optional[torch.Tensor] = None, bufs: Optional[dict] = None, stream=None):
     """moe_decode_layer: one layer step from router logits (router, planner,
     expert block); returns (out, idx, w, plan)."""
-    want = torch.bfloat16 if layer.act_dtype == MOE_DTYPE_BF16 else torch.float32
-    if x.dtype != want or x.dim() != 2 or not x.is_contiguous():
-        raise ValueError(f"x must be a contiguous {want} [B, H] tensor")
-    if logits.dtype != torch.float32 or logits.dim() != 2 or not logits.is_contiguous():
-        raise ValueError("logits must be a contiguous fp32 [B, E] tensor")
-    B, E = logits.shape
-    if x.shape[0] != B or E != layer.n_experts:
-        raise ValueError("x, logits and the layer disagree on the batch or the expert count")
+    B = _check_x(layer, x)
+    E = layer.n_experts
+    _need(logits, "logits", torch.float32, (B, E))
     bufs = bufs or {}
     k = layer.top_k
     idx = bufs.get("idx")
@@ -387,12 +451,14 @@ def decode_layer(layer: DeviceLayer, x: torch.Tensor, logits: torch.Tensor, plan
         w = torch.empty((B, k), dtype=torch.float32, device=logits.device)
     if plan is None:
         plan = Plan.allocate(E, B * k, device=logits.device)
-    if plan.sorted_slots.numel() < B * k or plan.counts.numel() < E:
-        raise ValueError("plan buffers are too small")
+    _check_routing(layer, B, idx, w)
+    _check_plan(layer, plan, B)
     if out is None:
         out = torch.empty_like(x)
+    _check_out(layer, B, out, residual)
     if workspace is None:
         workspace = alloc_workspace(layer, B, device=x.device)
+    _check_workspace(layer, B, workspace)
     _check(lib().moe_decode_layer(C.byref(layer.struct), _ptr(logits), _ptr(x), B, _ptr(idx), _ptr(w),
                                   C.byref(plan.struct), _ptr(residual), _ptr(out), _ptr(workspace),
                                   workspace.numel(), _stream(stream)), "moe_decode_layer")

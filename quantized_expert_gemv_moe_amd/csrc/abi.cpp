@@ -90,6 +90,7 @@ moe_status check_layer(const moe_layer_t *L) {
     }
     if (L->down_layout == MOE_DOWN_ROWS) {
         if (!pick_geometry(L->dff, &g)) return MOE_ERR_UNSUPPORTED;
+        if (down_rows_slot_bytes(L->dff) > kDownRowsLdsBytes) return MOE_ERR_UNSUPPORTED;
     } else if (L->down_layout == MOE_DOWN_COLS) {
         int nw, cpw;
         if (!pick_down_cols(L->dff, &nw, &cpw)) return MOE_ERR_UNSUPPORTED;
@@ -117,6 +118,34 @@ moe_status check_plan_args(const void *idx, int32_t n_tokens, int32_t n_experts,
         return MOE_ERR_INVALID_ARG;
     if (n_tokens > 0 && (!idx || !plan->sorted_slots)) return MOE_ERR_INVALID_ARG;
     if ((int64_t)n_tokens * top_k > INT32_MAX / 2) return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+
+// Host-side checks shared by the three expert entry points.
+moe_status check_step(const moe_layer_t *layer, int32_t n_tokens, const moe_plan_t *plan,
+                             void *workspace, size_t workspace_bytes) {
+    moe_status st = check_layer(layer);
+    if (st != MOE_OK) return st;
+    if (n_tokens < 0) return MOE_ERR_INVALID_ARG;
+    if (n_tokens > MOE_MAX_TOKENS) return MOE_ERR_UNSUPPORTED;
+    if (n_tokens == 0) return MOE_OK;
+    if (!plan || !plan->work || !plan->sorted_slots || (uintptr_t)plan->work % 16)
+        return MOE_ERR_INVALID_ARG;
+    if (!workspace || (uintptr_t)workspace % 256) return MOE_ERR_INVALID_ARG;
+    if (workspace_bytes < workspace_layout(layer, n_tokens).total) return MOE_ERR_WORKSPACE;
+    return MOE_OK;
+}
+
+moe_status check_x(const void *x) {
+    if (!x || (uintptr_t)x % 16) return MOE_ERR_INVALID_ARG;
+    return MOE_OK;
+}
+
+moe_status check_out(const void *x, const int32_t *topk_idx, const float *topk_w,
+                            const void *residual, const void *out) {
+    if (!topk_idx || !topk_w || !out) return MOE_ERR_INVALID_ARG;
+    if (out == x || (residual && out == residual)) return MOE_ERR_INVALID_ARG;
+    if ((uintptr_t)out % 4 || (residual && (uintptr_t)residual % 4)) return MOE_ERR_INVALID_ARG;
     return MOE_OK;
 }
 

@@ -31,456 +31,16 @@
 
 #include "device_util.h"
 #include "expert_device.h"
+#include "gate_up_device.h"
 #include "moe_internal.h"
 #include "route_device.h"
 
 namespace moe {
 
-typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
-
-struct GateUpArgs {
-    const uint4 *gate_q, *up_q;
-    const uint16_t *gate_s, *gate_b, *up_s, *up_b;
-    const float *expert_scale;
-    float clamp_limit;
-    const void *x;
-    PlanView plan;
-    float *h;
-    int hidden, dff, n_experts, top_k, n_slots;
-    int max_count;  // the VALU kernel leaves experts with more slots to the MFMA kernel
-    int activation;  // moe_activation
-};
-
-struct DownArgs {
-    const uint4 *down_q;
-    const uint16_t *down_s, *down_b;
-    const float *h;
-    PlanView plan;
-    float *y;
-    int hidden, dff, n_experts, n_slots, slots_per_stage;
-};
-
-__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
-                                           __builtin_bit_cast(bf16x2_t, b), c, false);
-}
-
-// Eight nibbles of `w` against eight bf16 activations given as the pairs
-// xp[p] = (x[p], x[p + 4]).  Each nibble pair becomes a bf16 pair of value
-// (128 + q[p], 128 + q[p + 4]) by masking into the mantissa of 128.0; the
-// products are exact in fp32.
-__device__ __forceinline__ float dot8_q4_bf16(uint32_t w, const uint32_t *xp, float acc) {
-    // The mask in an SGPR and the 128.0 pair in a VGPR, opaque to constant
-    // folding: then (w & M) | B is one v_and_or_b32 (gfx9's three-operand
-    // encoding takes no literal, so with both as literals the compiler
-    // emits a separate and + or per nibble pair).
-    uint32_t M, B;
-    asm("s_mov_b32 %0, 0xf000f" : "=s"(M));
-    asm("v_mov_b32 %0, 0x43004300" : "=v"(B));
-    acc = dot2_bf16((w & M) | B, xp[0], acc);
-    acc = dot2_bf16(((w >> 4) & M) | B, xp[1], acc);
-    acc = dot2_bf16(((w >> 8) & M) | B, xp[2], acc);
-    acc = dot2_bf16(((w >> 12) & M) | B, xp[3], acc);
-    return acc;
-}
-
-// sum_i (128 + q_i) x_i over the 32 weights of one 16-byte chunk.
-__device__ __forceinline__ float dot32_q4_bf16(uint4 q, const uint32_t *xp) {
-    const float a0 = dot8_q4_bf16(q.x, xp + 0, 0.f);
-    const float a1 = dot8_q4_bf16(q.y, xp + 4, 0.f);
-    const float a2 = dot8_q4_bf16(q.z, xp + 8, 0.f);
-    const float a3 = dot8_q4_bf16(q.w, xp + 12, 0.f);
-    return (a0 + a1) + (a2 + a3);
-}
-
-// 32 bf16 activations starting at element c0 of row xr, as loaded 16-byte
-// words.
-// The loads go through a global-address-space pointer: the activations
-// reach the kernels inside argument structs, where the compiler cannot
-// prove the address space, and a generic (flat) load makes every later
-// wait for memory also wait for all loads in flight.
-typedef uint32_t gv4u __attribute__((ext_vector_type(4)));
-typedef const __attribute__((address_space(1))) gv4u *gv4u_gptr;
-__device__ __forceinline__ void load_x32_bf16(const uint16_t *x, size_t xr, int c0, uint4 *raw) {
-    const gv4u_gptr p = (gv4u_gptr)(x + xr + c0);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const gv4u v = p[i];
-        raw[i] = make_uint4(v.x, v.y, v.z, v.w);
-    }
-}
-
-// The 16 pairs used by dot8_q4_bf16 from the loaded words, and the sum of
-// the 32 activations (dot2 against the pair (1, 1): exact products, fp32
-// accumulation).
-__device__ __forceinline__ float x32_pairs(const uint4 *raw, uint32_t *xp) {
-    const uint32_t ones = 0x3F803F80u;  // bf16 (1.0, 1.0)
-    float s0 = 0.f, s1 = 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const uint4 w = raw[i];  // elements 8i .. 8i+7 as (x0,x1),(x2,x3),(x4,x5),(x6,x7)
-        xp[4 * i + 0] = (w.x & 0xFFFFu) | (w.z << 16);
-        xp[4 * i + 1] = (w.x >> 16) | (w.z & 0xFFFF0000u);
-        xp[4 * i + 2] = (w.y & 0xFFFFu) | (w.w << 16);
-        xp[4 * i + 3] = (w.y >> 16) | (w.w & 0xFFFF0000u);
-        s0 = dot2_bf16(w.x, ones, dot2_bf16(w.y, ones, s0));
-        s1 = dot2_bf16(w.z, ones, dot2_bf16(w.w, ones, s1));
-    }
-    return s0 + s1;
-}
-
-// 32 fp32 activations starting at element c0 of row xr and their sum.
-__device__ __forceinline__ float load_x32_f32(const float *x, size_t xr, int c0, float *dst) {
-    const float4 *p = (const float4 *)(x + xr + c0);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const float4 w = p[i];
-        dst[4 * i + 0] = w.x;
-        dst[4 * i + 1] = w.y;
-        dst[4 * i + 2] = w.z;
-        dst[4 * i + 3] = w.w;
-    }
-    float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        s0 += dst[4 * i + 0];
-        s1 += dst[4 * i + 1];
-        s2 += dst[4 * i + 2];
-        s3 += dst[4 * i + 3];
-    }
-    return (s0 + s1) + (s2 + s3);
-}
-
-// ------------------------------------------------------- cross-lane sums
-
-template <int CTRL>
-__device__ __forceinline__ float dpp(float v) {
-    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
-}
-constexpr int kDppQuad1032 = 0xB1;  // quad_perm [1,0,3,2]
-constexpr int kDppQuad2301 = 0x4E;  // quad_perm [2,3,0,1]
-constexpr int kDppHalfMirror = 0x141;
-constexpr int kDppMirror = 0x140;
-
-// Sum over aligned segments of LPR lanes; every lane of a segment gets the
-// same value (each step adds the same two numbers on both partner lanes).
-template <int LPR>
-__device__ __forceinline__ float seg_sum(float v) {
-    if constexpr (LPR >= 2) v += dpp<kDppQuad1032>(v);
-    if constexpr (LPR >= 4) v += dpp<kDppQuad2301>(v);
-    if constexpr (LPR >= 8) v += dpp<kDppHalfMirror>(v);
-    if constexpr (LPR >= 16) v += dpp<kDppMirror>(v);
-    if constexpr (LPR >= 32) v += __shfl_xor(v, 16, kWave);
-    if constexpr (LPR >= 64) v += __shfl_xor(v, 32, kWave);
-    return v;
-}
-
-// Sum of lo and hi 32-lane halves of a and b at once: lanes 0..31 return
-// a[l] + a[l+32], lanes 32..63 return b[l-32] + b[l] (v_permlane32_swap).
-__device__ __forceinline__ float swap32_sum(float a, float b) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-// Same on 16-lane rows: rows (0,1) of a go to row 0, of b to row 1, rows
-// (2,3) of a to row 2, of b to row 3 (v_permlane16_swap).
-__device__ __forceinline__ float swap16_sum(float a, float b) {
-    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-// Wave-wide sums of eight per-lane values at once.  Lane l returns the total
-// of v[2 * (l >> 4) + ((l >> 3) & 1)]: lanes 16r..16r+7 hold v[2r] and lanes
-// 16r+8..16r+15 hold v[2r+1].  ~23 VALU ops instead of 8 separate trees.
-__device__ __forceinline__ float wave_sum8(const float *v) {
-    const int lane = threadIdx.x & (kWave - 1);
-    float w[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) w[i] = swap32_sum(v[i], v[i + 4]);
-    // w[i]: lanes 0..31 partial of v[i], lanes 32..63 partial of v[i+4]
-    const float z0 = swap16_sum(w[0], w[2]);  // rows: v0 v2 v4 v6
-    const float z1 = swap16_sum(w[1], w[3]);  // rows: v1 v3 v5 v7
-    const bool upper = lane & 8;
-    const float t = upper ? z1 : z0;
-    const float s = upper ? z0 : z1;
-    float m = t + dpp<kDppMirror>(s);
-    m += dpp<kDppHalfMirror>(m);
-    m += dpp<kDppQuad2301>(m);
-    m += dpp<kDppQuad1032>(m);
-    return m;
-}
-
-// Wave-wide sum; every lane gets the same total.
-__device__ __forceinline__ float wave_sum_all(float v) {
-    v += dpp<kDppQuad1032>(v);
-    v += dpp<kDppQuad2301>(v);
-    v += dpp<kDppHalfMirror>(v);
-    v += dpp<kDppMirror>(v);  // every lane: its 16-lane row total
-    v = swap16_sum(v, v);     // rows (0,1) and (2,3)
-    v = swap32_sum(v, v);     // halves
-    return v;
-}
-
-// ---------------------------------------------------------------- gate+up
-
-// A lane's share of RI rows of one expert: its NV 16-byte chunks of each
-// gate and up row with their scales and biases (as fp32; with bf16
-// activations the bias also carries the -128 * scale of the nibble trick).
-template <int RI, int NV>
-struct GateUpRows {
-    uint4 wg[RI][NV], wu[RI][NV];
-    float sg[RI][NV], bg[RI][NV], su[RI][NV], bu[RI][NV];
-};
-
-template <int LPR, int NV, int RI, bool XBF16>
-__device__ __forceinline__ void load_gate_up_rows(const GateUpArgs &a, int e, int row0, int sl,
-                                                  GateUpRows<RI, NV> &w) {
-    constexpr int RPI = kWave / LPR;
-    const int H = a.hidden, F = a.dff;
-    const int qrow = H / 32, grow = H / kGroup;
-#pragma unroll
-    for (int r = 0; r < RI; ++r) {
-        const int row = row0 + r * RPI;
-        const int rr = row < F ? row : F - 1;
-        const size_t rq = ((size_t)e * F + rr) * qrow;
-        const size_t rs = ((size_t)e * F + rr) * grow;
-#pragma unroll
-        for (int v = 0; v < NV; ++v) {
-            const int ch = v * LPR + sl;
-            w.wg[r][v] = load_stream(a.gate_q + rq + ch);
-            w.wu[r][v] = load_stream(a.up_q + rq + ch);
-            w.sg[r][v] = f16_bits_to_f32(a.gate_s[rs + ch / 2]);
-            w.bg[r][v] = f16_bits_to_f32(a.gate_b[rs + ch / 2]);
-            w.su[r][v] = f16_bits_to_f32(a.up_s[rs + ch / 2]);
-            w.bu[r][v] = f16_bits_to_f32(a.up_b[rs + ch / 2]);
-            if constexpr (XBF16) {  // fold the +128 of the bf16 nibble trick into the bias
-                w.bg[r][v] = fmaf(-128.f, w.sg[r][v], w.bg[r][v]);
-                w.bu[r][v] = fmaf(-128.f, w.su[r][v], w.bu[r][v]);
-            }
-        }
-    }
-}
-
-// One token's activations for this lane's chunks: bf16 pairs (or fp32
-// values) and the sum of each chunk's 32 activations.
-template <int LPR, int NV, bool XBF16>
-struct GateUpX {
-    uint32_t xp[XBF16 ? NV : 1][XBF16 ? 16 : 1];
-    float xf[XBF16 ? 1 : NV][XBF16 ? 1 : 32];
-    float xs[NV];
-};
-
-template <int LPR, int NV, bool XBF16>
-__device__ __forceinline__ void load_gate_up_x(const GateUpArgs &a, int token, int sl, GateUpX<LPR, NV, XBF16> &x,
-                                               const uint4 (*pre)[4] = nullptr) {
-    const size_t xr = (size_t)token * a.hidden;
-#pragma unroll
-    for (int v = 0; v < NV; ++v) {
-        const int c0 = (v * LPR + sl) * 32;
-        if constexpr (XBF16) {
-            uint4 raw[4];
-            if (pre) {
-#pragma unroll
-                for (int q = 0; q < 4; ++q) raw[q] = pre[v][q];
-            } else {
-                load_x32_bf16((const uint16_t *)a.x, xr, c0, raw);
-            }
-            x.xs[v] = x32_pairs(raw, x.xp[v]);
-        } else {
-            x.xs[v] = load_x32_f32((const float *)a.x, xr, c0, x.xf[v]);
-        }
-    }
-}
-
-// h = silu(g) * u of one token for the segment's RI rows, into slot `slot`.
-template <int LPR, int NV, int RI, bool XBF16>
-__device__ __forceinline__ void gate_up_token_rows(const GateUpArgs &a, const GateUpRows<RI, NV> &w,
-                                                   const GateUpX<LPR, NV, XBF16> &x, int slot, int row0,
-                                                   float sc, float lim) {
-    constexpr int RPI = kWave / LPR;
-    constexpr bool WAVE8 = (LPR == kWave && RI == 4);
-    const int lane = threadIdx.x & (kWave - 1);
-    const int sl = lane % LPR;
-    const int F = a.dff;
-    float part[2 * RI];
-#pragma unroll
-    for (int r = 0; r < RI; ++r) {
-        float g = 0.f, u = 0.f;
-#pragma unroll
-        for (int v = 0; v < NV; ++v) {
-            float dg, du;
-            if constexpr (XBF16) {
-                dg = dot32_q4_bf16(w.wg[r][v], x.xp[v]);
-                du = dot32_q4_bf16(w.wu[r][v], x.xp[v]);
-            } else {
-                dg = dot32_q4(w.wg[r][v], x.xf[v]);
-                du = dot32_q4(w.wu[r][v], x.xf[v]);
-            }
-            g += fmaf(w.sg[r][v], dg, w.bg[r][v] * x.xs[v]);
-            u += fmaf(w.su[r][v], du, w.bu[r][v] * x.xs[v]);
-        }
-        part[2 * r] = g;
-        part[2 * r + 1] = u;
-    }
-    if constexpr (WAVE8) {
-        const float tot = wave_sum8(part);
-        const float other = dpp<kDppMirror>(tot);  // lane 16r reads lane 16r+15 (the u)
-        const int r = lane >> 4;
-        const int row = row0 + r * RPI;
-        if ((lane & 15) == 0 && row < F) a.h[(size_t)slot * F + row] = act_mul(tot, other, sc, lim, a.activation);
-    } else {
-#pragma unroll
-        for (int r = 0; r < RI; ++r) {
-            const float g = seg_sum<LPR>(part[2 * r]);
-            const float u = seg_sum<LPR>(part[2 * r + 1]);
-            const int row = row0 + r * RPI;
-            if (sl == 0 && row < F) a.h[(size_t)slot * F + row] = act_mul(g, u, sc, lim, a.activation);
-        }
-    }
-}
-
-// One wave: row block rb of distinct expert u.  LPR lanes per row, NV
-// chunks per lane, RI rows per segment; TCH tokens' activations in
-// registers at a time.
-template <int LPR, int NV, int RI, bool XBF16>
-__device__ __forceinline__ void gate_up_valu_block(const GateUpArgs &a, int rb, int u) {
-    constexpr int RPI = kWave / LPR;  // rows per wave-wide pass
-    constexpr int ROWS_WG = RPI * RI;
-    constexpr int TCH = (XBF16 && NV == 1) ? 2 : 1;
-    const int lane = threadIdx.x & (kWave - 1);
-    const int sl = lane % LPR;
-    Work wk;
-    if (!plan_expert(a.plan, u, a.n_experts, a.n_slots, &wk)) return;
-    if (wk.count > a.max_count) return;  // the MFMA kernel's expert
-    const int e = wk.e, count = wk.count;
-    const int row0 = rb * ROWS_WG + lane / LPR;
-
-    // The first TCH tokens' activations go out ahead of the weights, and
-    // each pass fetches the next TCH tokens' before it computes, so no
-    // activation load waits behind the weights.  Loads are unconditional
-    // (past the last token they repeat it, unused): a load under a branch
-    // would make the compiler wait for every load in flight where it joins.
-    int slot_n[TCH];
-    uint4 raw_n[TCH][XBF16 ? NV : 1][4];
-#pragma unroll
-    for (int i = 0; i < TCH; ++i) {
-        slot_n[i] = plan_slot(a.plan, wk, i < count ? i : count - 1, a.n_slots);
-        if constexpr (XBF16) {
-#pragma unroll
-            for (int v = 0; v < NV; ++v)
-                load_x32_bf16((const uint16_t *)a.x, (size_t)(slot_n[i] / a.top_k) * a.hidden,
-                              (v * LPR + sl) * 32, raw_n[i][v]);
-        }
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    GateUpRows<RI, NV> w;
-    load_gate_up_rows<LPR, NV, RI, XBF16>(a, e, row0, sl, w);
-    const float sc = a.expert_scale ? a.expert_scale[e] : 1.f;
-    const float lim = a.clamp_limit;
-    __builtin_amdgcn_sched_barrier(0);
-
-    for (int t0 = 0; t0 < count; t0 += TCH) {
-        int slot[TCH];
-        uint4 raw[TCH][XBF16 ? NV : 1][4];
-#pragma unroll
-        for (int i = 0; i < TCH; ++i) {
-            slot[i] = slot_n[i];
-#pragma unroll
-            for (int v = 0; v < (XBF16 ? NV : 1); ++v)
-#pragma unroll
-                for (int q = 0; q < 4; ++q) raw[i][v][q] = raw_n[i][v][q];
-        }
-        if constexpr (XBF16) {
-#pragma unroll
-            for (int i = 0; i < TCH; ++i) {
-                const int tn = t0 + TCH + i;
-                slot_n[i] = plan_slot(a.plan, wk, tn < count ? tn : count - 1, a.n_slots);
-#pragma unroll
-                for (int v = 0; v < NV; ++v)
-                    load_x32_bf16((const uint16_t *)a.x, (size_t)(slot_n[i] / a.top_k) * a.hidden,
-                                  (v * LPR + sl) * 32, raw_n[i][v]);
-            }
-        } else {
-            slot_n[0] = plan_slot(a.plan, wk, t0 + 1 < count ? t0 + 1 : count - 1, a.n_slots);
-        }
-#pragma unroll
-        for (int i = 0; i < TCH; ++i) {
-            if (i > 0 && t0 + i >= count) break;  // uniform: the chunk's tail is empty
-            GateUpX<LPR, NV, XBF16> x;
-            load_gate_up_x<LPR, NV, XBF16>(a, slot[i] / a.top_k, sl, x, XBF16 ? raw[i] : nullptr);
-            gate_up_token_rows<LPR, NV, RI, XBF16>(a, w, x, slot[i], row0, sc, lim);
-        }
-    }
-}
-
-// At least four waves per SIMD for the one-chunk bf16 rows (they fit in 128
-// registers without spilling): left to itself the compiler sizes this
-// one-wave kernel's registers for two, and a CU then holds too few waves to
-// keep enough loads in flight.
-template <int LPR, int NV, bool XBF16>
-constexpr int gate_up_waves_per_simd() { return (NV == 1 && XBF16) ? 4 : 1; }
-
 template <int LPR, int NV, int RI, bool XBF16>
 __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(gate_up_waves_per_simd<LPR, NV, XBF16>())))
 void gate_up_kernel(GateUpArgs a) {
     gate_up_valu_block<LPR, NV, RI, XBF16>(a, blockIdx.x, blockIdx.y);
-}
-
-// A small batch (up to BW tokens), routed here, on a 1-D grid of BW-wave
-// blocks.  Block 0 routes every token in full, one wave per token, and
-// writes topk_idx, topk_w and the plan, exactly as
-// moe_route_plan would.  Every wave of the other blocks is one item (token
-// t, rank j, row block): it finds the token's expert of rank j itself from
-// the logits (j + 1 selection rounds) instead of waiting for a router launch
-// and a plan, and computes that expert's rows for that token alone (no
-// deduplication: with so few tokens it would save little and cost a
-// launch).  The arithmetic per row is gate_up_kernel's, so h is bitwise the
-// same as on the batched path.
-constexpr int kRouteMaxTokens = 8;
-
-template <int LPR, int NV, int RI, bool XBF16, int PL, int BW>
-__global__ __launch_bounds__(BW * kWave) void gate_up_route_kernel(
-    GateUpArgs a, const float *__restrict__ logits, int *__restrict__ topk_idx, float *__restrict__ topk_w,
-    PlanOut p, int row_blocks, int n_tokens) {
-    constexpr int RPI = kWave / LPR;
-    constexpr int ROWS_WG = RPI * RI;
-    const int lane = threadIdx.x & (kWave - 1);
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const int sl = lane % LPR;
-    const int E = a.n_experts, k = a.top_k;
-    if (blockIdx.x == 0) {
-        __shared__ int idx_lds[kWave];  // n_tokens * top_k <= 64
-        __shared__ int cnt[MOE_MAX_EXPERTS], off[MOE_MAX_EXPERTS], uix[MOE_MAX_EXPERTS];
-        if (wave < n_tokens) {
-            int id;
-            float wt;
-            if (route_token<PL>(logits + (size_t)wave * E, E, k, &id, &wt)) {
-                topk_idx[wave * k + lane] = id;
-                topk_w[wave * k + lane] = wt;
-                idx_lds[wave * k + lane] = id;
-            }
-        }
-        __syncthreads();
-        if (wave == 0) plan_wave_small<PL>(idx_lds, n_tokens * k, E, p, cnt, off, uix);
-        return;
-    }
-    const int item = (blockIdx.x - 1) * BW + wave;
-    if (item >= n_tokens * k * row_blocks) return;
-    const int rb = item % row_blocks, j = (item / row_blocks) % k, t = item / (row_blocks * k);
-    const int row0 = rb * ROWS_WG + lane / LPR;
-    uint4 xraw0[XBF16 ? NV : 1][4];
-    if constexpr (XBF16) {
-#pragma unroll
-        for (int v = 0; v < NV; ++v)
-            load_x32_bf16((const uint16_t *)a.x, (size_t)t * a.hidden, (v * LPR + sl) * 32, xraw0[v]);
-    }
-    const int e = route_rank<PL>(logits + (size_t)t * E, E, j);
-    GateUpRows<RI, NV> w;
-    load_gate_up_rows<LPR, NV, RI, XBF16>(a, e, row0, sl, w);
-    const float sc = a.expert_scale ? a.expert_scale[e] : 1.f;
-    GateUpX<LPR, NV, XBF16> x;
-    load_gate_up_x<LPR, NV, XBF16>(a, t, sl, x, XBF16 ? xraw0 : nullptr);
-    gate_up_token_rows<LPR, NV, RI, XBF16>(a, w, x, t * k + j, row0, sc, a.clamp_limit);
 }
 
 // ----------------------------------------------------- gate+up, MFMA tiles
@@ -1386,14 +946,6 @@ __global__ __launch_bounds__(NW * kWave) void down_token_kernel(const uint4 *__r
 
 // ------------------------------------------------------------ dispatching
 
-// Rows per lane segment of the gate+up kernels: four for the whole-wave rows
-// (the 8-value transposed reduction), fewer when a lane holds many chunks.
-// Both gate+up kernels take the same value, so they reduce in the same order.
-template <int LPR, int NV>
-constexpr int gate_up_ri() {
-    return (LPR == kWave) ? (NV <= 2 ? 4 : 2) : (NV <= 2 ? 2 : 1);
-}
-
 template <int LPR, int NV>
 static moe_status launch_gate_up(const GateUpArgs &a, bool bf16, int groups_y, hipStream_t s) {
     constexpr int RI = gate_up_ri<LPR, NV>();
@@ -1406,47 +958,12 @@ static moe_status launch_gate_up(const GateUpArgs &a, bool bf16, int groups_y, h
     return MOE_OK;
 }
 
-// The routing gate+up kernel of a one-token batch: a planner block, then
-// row blocks x top_k.
-template <int LPR, int NV>
-static moe_status launch_gate_up_route(const GateUpArgs &a, bool bf16, int pl, const float *logits,
-                                       int32_t *idx, float *w, const PlanOut &p, int n_tokens, hipStream_t s) {
-    constexpr int RI = gate_up_ri<LPR, NV>();
-    constexpr int rows = (kWave / LPR) * RI;
-    const int row_blocks = (a.dff + rows - 1) / rows;
-    const int items = n_tokens * a.top_k * row_blocks;
-    // 4-wave blocks up to 4 tokens, 8-wave blocks beyond (measured best at
-    // either end)
-    const int bw = n_tokens <= 4 ? 4 : 8;
-    const dim3 grid(1 + (items + bw - 1) / bw), block(bw * kWave);
-#define MOE_GUR(PL, BW)                                                                                    \
-    if (bf16)                                                                                              \
-        hipLaunchKernelGGL((gate_up_route_kernel<LPR, NV, RI, true, PL, BW>), grid, block, 0, s, a, logits, \
-                           idx, w, p, row_blocks, n_tokens);                                               \
-    else                                                                                                   \
-        hipLaunchKernelGGL((gate_up_route_kernel<LPR, NV, RI, false, PL, BW>), grid, block, 0, s, a, logits, \
-                           idx, w, p, row_blocks, n_tokens);
-    switch (pl * 10 + bw / 4) {
-        case 11: MOE_GUR(1, 4) break;
-        case 21: MOE_GUR(2, 4) break;
-        case 41: MOE_GUR(4, 4) break;
-        case 12: MOE_GUR(1, 8) break;
-        case 22: MOE_GUR(2, 8) break;
-        case 42: MOE_GUR(4, 8) break;
-        default: return MOE_ERR_UNSUPPORTED;
-    }
-#undef MOE_GUR
-    return MOE_OK;
-}
-
-constexpr size_t kDownLdsBytes = 32768;
-
 template <int LPR, int NV>
 static moe_status launch_down(DownArgs a, int groups_y, int max_count, hipStream_t s) {
     constexpr int RI = 1;
     constexpr int rows = (kWave / LPR) * RI * (kBlock / kWave);
-    const size_t per_slot = ((size_t)a.dff + a.dff / kGroup) * sizeof(float);
-    int S = (int)(kDownLdsBytes / per_slot);
+    const size_t per_slot = down_rows_slot_bytes(a.dff);
+    int S = (int)(kDownRowsLdsBytes / per_slot);
     if (S < 1) return MOE_ERR_UNSUPPORTED;
     if (S > max_count) S = max_count;
     a.slots_per_stage = S;
@@ -1572,48 +1089,6 @@ static moe_status launch_down_token(const moe_layer_t *L, int n_tokens, const fl
     }
 }
 
-// Every (lanes per row, chunks per lane) pair that the geometry pickers return.
-#define MOE_GEOMETRY_SWITCH(G, RET, FN, ...)                           \
-    switch ((G).lpr * 8 + (G).nv) {                                    \
-        case 64 * 8 + 1: RET = FN<64, 1>(__VA_ARGS__); break;          \
-        case 64 * 8 + 2: RET = FN<64, 2>(__VA_ARGS__); break;          \
-        case 64 * 8 + 3: RET = FN<64, 3>(__VA_ARGS__); break;          \
-        case 64 * 8 + 4: RET = FN<64, 4>(__VA_ARGS__); break;          \
-        case 32 * 8 + 3: RET = FN<32, 3>(__VA_ARGS__); break;          \
-        case 32 * 8 + 4: RET = FN<32, 4>(__VA_ARGS__); break;          \
-        case 16 * 8 + 3: RET = FN<16, 3>(__VA_ARGS__); break;          \
-        case 16 * 8 + 4: RET = FN<16, 4>(__VA_ARGS__); break;          \
-        case 8 * 8 + 3: RET = FN<8, 3>(__VA_ARGS__); break;            \
-        case 8 * 8 + 4: RET = FN<8, 4>(__VA_ARGS__); break;            \
-        case 4 * 8 + 3: RET = FN<4, 3>(__VA_ARGS__); break;            \
-        case 4 * 8 + 4: RET = FN<4, 4>(__VA_ARGS__); break;            \
-        case 2 * 8 + 3: RET = FN<2, 3>(__VA_ARGS__); break;            \
-        case 2 * 8 + 4: RET = FN<2, 4>(__VA_ARGS__); break;            \
-        case 1 * 8 + 2: RET = FN<1, 2>(__VA_ARGS__); break;            \
-        case 1 * 8 + 3: RET = FN<1, 3>(__VA_ARGS__); break;            \
-        case 1 * 8 + 4: RET = FN<1, 4>(__VA_ARGS__); break;            \
-        default: RET = MOE_ERR_UNSUPPORTED; break;                     \
-    }
-
-// Host-side checks shared by the three expert entry points.
-static moe_status check_step(const moe_layer_t *layer, int32_t n_tokens, const moe_plan_t *plan,
-                             void *workspace, size_t workspace_bytes) {
-    moe_status st = check_layer(layer);
-    if (st != MOE_OK) return st;
-    if (n_tokens < 0) return MOE_ERR_INVALID_ARG;
-    if (n_tokens > MOE_MAX_TOKENS) return MOE_ERR_UNSUPPORTED;
-    if (n_tokens == 0) return MOE_OK;
-    if (!plan || !plan->work || !plan->sorted_slots || (uintptr_t)plan->work % 16)
-        return MOE_ERR_INVALID_ARG;
-    if (!workspace || (uintptr_t)workspace % 256) return MOE_ERR_INVALID_ARG;
-    if (workspace_bytes < workspace_layout(layer, n_tokens).total) return MOE_ERR_WORKSPACE;
-    return MOE_OK;
-}
-
-static PlanView plan_view(const moe_plan_t *plan) {
-    return PlanView{(const int4 *)plan->work, plan->sorted_slots};
-}
-
 static int groups_y_of(const moe_layer_t *layer, int n_tokens) {
     const int n_slots = n_tokens * layer->top_k;
     return n_slots < layer->n_experts ? n_slots : layer->n_experts;
@@ -1636,7 +1111,11 @@ constexpr int kMfmaMinTokens = 16;
 static bool mfma_gate_up_shape(const moe_layer_t *layer, int *nw, int *gw) {
     if (layer->act_dtype != MOE_DTYPE_BF16 || layer->hidden % kGroup) return false;
     const int G = layer->hidden / kGroup;
-    if (G % 4 || G / 4 > 16) return false;
+    if (G % 4) return false;
+    switch (G / 4) {  // the instantiated workgroup sizes (MOE_GUM below)
+        case 1: case 2: case 4: case 6: case 8: case 12: case 16: break;
+        default: return false;  // dot2 kernels at every batch size
+    }
     *gw = 4;
     *nw = G / 4;
     return true;
@@ -1680,8 +1159,8 @@ static moe_status launch_gate_up_mixed(const moe_layer_t *layer, const GateUpArg
     }
 }
 
-static moe_status enqueue_gate_up(const moe_layer_t *layer, const void *x, int n_tokens,
-                                  const moe_plan_t *plan, void *workspace, hipStream_t stream) {
+moe_status enqueue_gate_up(const moe_layer_t *layer, const void *x, int n_tokens, const moe_plan_t *plan,
+                           void *workspace, hipStream_t stream) {
     const Workspace ws = workspace_layout(layer, n_tokens);
     float *h = (float *)((char *)workspace + ws.h_off);
     if (!fast_gate_up(layer)) return launch_generic_gate_up(layer, x, n_tokens, plan, h, stream);
@@ -1805,19 +1284,6 @@ static moe_status enqueue_down_combine(const moe_layer_t *layer, int n_tokens, c
     return MOE_OK;
 }
 
-static moe_status check_x(const void *x) {
-    if (!x || (uintptr_t)x % 16) return MOE_ERR_INVALID_ARG;
-    return MOE_OK;
-}
-
-static moe_status check_out(const void *x, const int32_t *topk_idx, const float *topk_w,
-                            const void *residual, const void *out) {
-    if (!topk_idx || !topk_w || !out) return MOE_ERR_INVALID_ARG;
-    if (out == x || (residual && out == residual)) return MOE_ERR_INVALID_ARG;
-    if ((uintptr_t)out % 4 || (residual && (uintptr_t)residual % 4)) return MOE_ERR_INVALID_ARG;
-    return MOE_OK;
-}
-
 }  // namespace moe
 
 using namespace moe;
@@ -1859,41 +1325,6 @@ extern "C" moe_status moe_decode_step(const moe_layer_t *layer, const void *x, i
     st = enqueue_gate_up(layer, x, n_tokens, plan, workspace, stream);
     if (st != MOE_OK) return st;
     st = enqueue_down_combine(layer, n_tokens, topk_idx, topk_w, plan, residual, out, workspace, stream);
-    if (st != MOE_OK) return st;
-    return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_DEVICE;
-}
-
-extern "C" moe_status moe_route_gate_up(const moe_layer_t *layer, const float *logits, const void *x,
-                                        int32_t n_tokens, int32_t *topk_idx, float *topk_w,
-                                        const moe_plan_t *plan, void *workspace, size_t workspace_bytes,
-                                        void *hip_stream) {
-    moe_status st = check_step(layer, n_tokens, plan, workspace, workspace_bytes);
-    if (st != MOE_OK || n_tokens == 0) return st;
-    if ((st = check_route_args(logits, n_tokens, layer->n_experts, layer->top_k, topk_idx, topk_w)) != MOE_OK)
-        return st;
-    if ((st = check_plan_args(topk_idx, n_tokens, layer->n_experts, layer->top_k, plan)) != MOE_OK) return st;
-    if ((st = check_x(x)) != MOE_OK) return st;
-    hipStream_t stream = (hipStream_t)hip_stream;
-    const int pl = per_lane_bucket(layer->n_experts);
-    if (!fast_gate_up(layer) || n_tokens > kRouteMaxTokens || pl > 4 || n_tokens * layer->top_k > kWave) {
-        // router + planner launch, then the deduplicated gate+up
-        st = moe_route_plan(logits, n_tokens, layer->n_experts, layer->top_k, topk_idx, topk_w, plan, hip_stream);
-        if (st != MOE_OK) return st;
-        st = enqueue_gate_up(layer, x, n_tokens, plan, workspace, stream);
-    } else {  // a few tokens: one launch that routes for itself
-        Geometry gu;
-        pick_geometry_gate_up(layer->hidden, &gu);
-        const Workspace ws = workspace_layout(layer, n_tokens);
-        float *h = (float *)((char *)workspace + ws.h_off);
-        const GateUpArgs ga{(const uint4 *)layer->gate_q, (const uint4 *)layer->up_q, layer->gate_s,
-                            layer->gate_b, layer->up_s, layer->up_b, layer->expert_scale,
-                            layer->clamp_limit, x, plan_view(plan), h, layer->hidden, layer->dff,
-                            layer->n_experts, layer->top_k, n_tokens * layer->top_k, INT_MAX, layer->activation};
-        const PlanOut po{plan->counts, plan->offsets, plan->sorted_slots, plan->unique_experts, plan->n_unique,
-                         (int4 *)plan->work};
-        MOE_GEOMETRY_SWITCH(gu, st, launch_gate_up_route, ga, layer->act_dtype == MOE_DTYPE_BF16, pl, logits,
-                            topk_idx, topk_w, po, n_tokens, stream)
-    }
     if (st != MOE_OK) return st;
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_DEVICE;
 }

@@ -30,6 +30,11 @@ __device__ __forceinline__ bool plan_expert(const PlanView &p, int u, int n_expe
     return true;
 }
 
+// Device view of a plan (host side).
+inline PlanView plan_view(const moe_plan_t *plan) {
+    return PlanView{(const int4 *)plan->work, plan->sorted_slots};
+}
+
 // Slot i of the expert's list (the first one comes with the record).
 __device__ __forceinline__ int plan_slot(const PlanView &p, const Work &w, int i, int n_slots) {
     const int s = i == 0 ? w.slot0 : p.sorted_slots[w.first + i];

@@ -150,6 +150,30 @@ __device__ __forceinline__ int route_rank(const float *__restrict__ row, int n_e
     return win;
 }
 
+// Rank of expert e (wave-uniform, < n_experts) among one token's experts in
+// the router's order -- descending logit, ties to the lower id -- from that
+// token's order keys (route_keys): the number of experts placed before it.
+// The token holds e among its top k exactly when this is below k, and then
+// e is its expert of that rank: the same order route_take walks.
+template <int PER_LANE>
+__device__ __forceinline__ int route_rank_of(const uint32_t *key, int e) {
+    const int lane = threadIdx.x & (kWave - 1);
+    uint32_t ke = 0;
+#pragma unroll
+    for (int q = 0; q < PER_LANE; ++q) {
+        const uint32_t v = __builtin_amdgcn_readlane(key[q], e & (kWave - 1));
+        ke = (q == (e >> 6)) ? v : ke;
+    }
+    int n = 0;
+#pragma unroll
+    for (int q = 0; q < PER_LANE; ++q) {
+        const int id = lane + kWave * q;
+        const bool before = key[q] > ke || (key[q] == ke && id < e);
+        n += __popcll(__builtin_amdgcn_ballot_w64(before));
+    }
+    return n;
+}
+
 // ---------------------------------------------------------------- planner
 
 // Exclusive scan of one int per thread over a block of NT threads; returns

@@ -73,6 +73,10 @@ def test_layer_check_accepts_the_workload_shapes():
     # the column layout under generic gate+up kernels
     assert check(bits=8, down_layout=moe.MOE_DOWN_COLS) == moe.MOE_OK
     assert check(bits=6, hidden=4096, dff=2048, down_layout=moe.MOE_DOWN_COLS) == moe.MOE_OK
+    # the largest dff the row-layout down kernel stages in LDS
+    assert check(dff=6144) == moe.MOE_OK
+    # a generic (8-bit) down projection has no such limit
+    assert check(dff=8192, down_bits=8) == moe.MOE_OK
 
 
 @pytest.mark.parametrize("kw,want", [
@@ -106,6 +110,10 @@ def test_layer_check_accepts_the_workload_shapes():
     (dict(down_scale=FAKE + 2), moe.MOE_ERR_INVALID_ARG),   # not 4-byte aligned
     (dict(dff=1152, down_layout=moe.MOE_DOWN_COLS), moe.MOE_ERR_UNSUPPORTED),  # 36 chunks: no column kernel
     (dict(dff=192, down_layout=moe.MOE_DOWN_COLS), moe.MOE_ERR_UNSUPPORTED),   # dff % 128 != 0
+    # the row-layout down kernel stages one slot's h (and group sums) in
+    # 32 KiB of LDS: dff 8192 has a lane geometry but no room there, so the
+    # layer is refused before anything is enqueued (not after gate+up ran)
+    (dict(dff=8192), moe.MOE_ERR_UNSUPPORTED),
 ])
 def test_layer_check_rejects(kw, want):
     assert check(**kw) == want

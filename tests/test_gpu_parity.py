@@ -249,6 +249,7 @@ def test_column_down_in_stages(H, F, E, k, B, regime):
     (4096, 256, 2, 2, 16),    # the wide hidden size: the two variants in two launches
     (1024, 64, 8, 8, 16),     # k = E: every expert holds all 16 tokens
     (1536, 128, 8, 1, 17),    # one to five tokens per expert
+    (768, 256, 4, 2, 16),     # 12 groups: no MFMA workgroup shape, dot2 for every expert
 ])
 def test_gate_up_mfma_path(H, F, E, k, B, layout):
     """In batches of 16 or more tokens, experts with >= 3 tokens run the
