@@ -306,6 +306,31 @@ moe_status moe_expert_down_combine(const moe_layer_t *layer, int32_t n_tokens,
                                    void *workspace, size_t workspace_bytes, void *hip_stream);
 
 /*
+ * moe_decode_layer for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments, checks and results as moe_decode_layer
+ * (bitwise), without the workspace: the h and y intermediates live in a
+ * device array of MOE_STATIC_SCRATCH_BYTES that the library reserves per
+ * GPU when it is loaded and holds until the process ends.
+ *   - MOE_ERR_WORKSPACE when moe_workspace_size(layer, n_tokens) exceeds
+ *     MOE_STATIC_SCRATCH_BYTES (8 MiB: up to 93 tokens of the 2048 x 768
+ *     top-8 layer).
+ *   - hip_stream must belong to the current device (else
+ *     MOE_ERR_INVALID_ARG).  The first call on a device looks up the
+ *     array's device address; make that call outside graph capture.
+ *   - Every call on one GPU shares that GPU's array, which keeps the last
+ *     call's contents (nothing in it needs clearing: each step writes h
+ *     and y before reading them).  Calls that may overlap on one GPU (other
+ *     streams, other host threads) race on it: serialise them.
+ * Calls no hipMalloc, hipFree or other allocating routine.
+ */
+#define MOE_STATIC_SCRATCH_BYTES ((size_t)8 << 20)
+moe_status moe_decode_layer_static(const moe_layer_t *layer, const float *logits, const void *x,
+                                   int32_t n_tokens, int32_t *topk_idx, float *topk_w,
+                                   const moe_plan_t *plan, const void *residual, void *out,
+                                   void *hip_stream);
+
+/*
  * Regroup a layer's down projection from MOE_DOWN_ROWS (as stored by the
  * pages' 4-bit checkpoints) to MOE_DOWN_COLS, the layout the decode kernels
  * read fastest: a wave then reads 64 consecutive output rows with one
@@ -326,7 +351,7 @@ moe_status moe_layer_check(const moe_layer_t *layer);
 /* Static description of a status code. */
 const char *moe_status_str(moe_status status);
 
-/* ABI version: bumped when a signature or struct changes. */
+/* ABI version: bumped when a signature or struct changes (7: moe_decode_layer_static). */
 int32_t moe_abi_version(void);
 
 #ifdef __cplusplus

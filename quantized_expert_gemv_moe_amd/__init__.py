@@ -18,6 +18,7 @@ from ._lib import (  # noqa: F401
     MOE_ERR_UNSUPPORTED,
     MOE_ERR_WORKSPACE,
     MOE_OK,
+    MOE_STATIC_SCRATCH_BYTES,
     DeviceLayer,
     LayerStruct,
     MoeError,
@@ -25,6 +26,7 @@ from ._lib import (  # noqa: F401
     PlanStruct,
     alloc_workspace,
     decode_layer,
+    decode_layer_static,
     decode_step,
     expert_down_combine,
     expert_gate_up,

@@ -25,6 +25,7 @@ _ACTIVATIONS = {"swiglu": MOE_ACT_SWIGLU, "geglu": MOE_ACT_GEGLU}
 MOE_MAX_EXPERTS = 1024
 MOE_MAX_TOP_K = 16
 MOE_MAX_TOKENS = 65535
+MOE_STATIC_SCRATCH_BYTES = 8 << 20
 
 
 class MoeError(RuntimeError):
@@ -55,7 +56,7 @@ _lib = None
 
 EXPORTS = ("moe_router_logits", "moe_route_topk", "moe_expert_plan", "moe_route_plan", "moe_workspace_size",
            "moe_decode_step",
-           "moe_decode_layer", "moe_route_gate_up", "moe_expert_gate_up", "moe_expert_down_combine", "moe_pack_down",
+           "moe_decode_layer", "moe_decode_layer_static", "moe_route_gate_up", "moe_expert_gate_up", "moe_expert_down_combine", "moe_pack_down",
            "moe_layer_check", "moe_status_str", "moe_abi_version")
 
 
@@ -90,6 +91,9 @@ def lib() -> C.CDLL:
         L.moe_decode_layer.argtypes = [C.POINTER(LayerStruct), vp, vp, i32, vp, vp, C.POINTER(PlanStruct),
                                        vp, vp, vp, C.c_size_t, vp]
         L.moe_decode_layer.restype = C.c_int
+        L.moe_decode_layer_static.argtypes = [C.POINTER(LayerStruct), vp, vp, i32, vp, vp, C.POINTER(PlanStruct),
+                                              vp, vp, vp]
+        L.moe_decode_layer_static.restype = C.c_int
         L.moe_route_gate_up.argtypes = [C.POINTER(LayerStruct), vp, vp, i32, vp, vp, C.POINTER(PlanStruct),
                                         vp, C.c_size_t, vp]
         L.moe_route_gate_up.restype = C.c_int
@@ -463,3 +467,19 @@ def decode_layer(layer: DeviceLayer, x: torch.Tensor, logits: torch.Tensor, plan
                                   C.byref(plan.struct), _ptr(residual), _ptr(out), _ptr(workspace),
                                   workspace.numel(), _stream(stream)), "moe_decode_layer")
     return out, idx, w, plan
+
+
+def decode_layer_static(layer: DeviceLayer, x: torch.Tensor, logits: torch.Tensor, plan: Plan, out: torch.Tensor,
+                        idx: torch.Tensor, w: torch.Tensor, residual: Optional[torch.Tensor] = None, stream=None):
+    """moe_decode_layer_static: moe_decode_layer without a workspace (the library's
+    per-device scratch array holds h and y).  Every buffer is the caller's:
+    nothing is allocated here either."""
+    B = _check_x(layer, x)
+    _need(logits, "logits", torch.float32, (B, layer.n_experts))
+    _check_routing(layer, B, idx, w)
+    _check_plan(layer, plan, B)
+    _check_out(layer, B, out, residual)
+    _check(lib().moe_decode_layer_static(C.byref(layer.struct), _ptr(logits), _ptr(x), B, _ptr(idx), _ptr(w),
+                                         C.byref(plan.struct), _ptr(residual), _ptr(out), _stream(stream)),
+           "moe_decode_layer_static")
+    return out

@@ -180,6 +180,6 @@ const char *moe_status_str(moe_status s) {
     return "unknown status";
 }
 
-int32_t moe_abi_version(void) { return 6; }
+int32_t moe_abi_version(void) { return 7; }
 
 }  // extern "C"

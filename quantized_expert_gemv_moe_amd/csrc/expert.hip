@@ -29,6 +29,8 @@
 #include <limits.h>
 #include <math.h>
 
+#include <mutex>
+
 #include "device_util.h"
 #include "expert_device.h"
 #include "gate_up_device.h"
@@ -1344,4 +1346,55 @@ extern "C" moe_status moe_decode_layer(const moe_layer_t *layer, const float *lo
                               (hipStream_t)hip_stream);
     if (st != MOE_OK) return st;
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_DEVICE;
+}
+
+// ------------------------------------------- the allocation-free variant
+
+// Device memory of moe_decode_layer_static: the h and y workspace of the
+// step in one array per device, reserved when the library is loaded and
+// held until the process ends.  In host code `scratch` only names the
+// symbol; its device address comes from hipGetSymbolAddress, once per
+// device, and is what the kernels get.
+static __device__ __align__(256) unsigned char scratch[MOE_STATIC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void *scratch_dev[kMaxDevices];  // device address of `scratch` per device, once looked up
+}  // namespace
+
+// The scratch array's address on the device of `stream`, which must be the
+// current device (the lookup answers for the current device).
+static moe_status scratch_of(hipStream_t stream, void **ptr) {
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess || cur < 0 || cur >= kMaxDevices) return MOE_ERR_DEVICE;
+    if (stream) {
+        hipDevice_t sd = -1;
+        if (hipStreamGetDevice(stream, &sd) != hipSuccess) return MOE_ERR_INVALID_ARG;
+        if (sd != cur) return MOE_ERR_INVALID_ARG;
+    }
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if (!scratch_dev[cur]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_ERR_DEVICE;
+        scratch_dev[cur] = p;
+    }
+    *ptr = scratch_dev[cur];
+    return MOE_OK;
+}
+
+extern "C" moe_status moe_decode_layer_static(const moe_layer_t *layer, const float *logits, const void *x,
+                                              int32_t n_tokens, int32_t *topk_idx, float *topk_w,
+                                              const moe_plan_t *plan, const void *residual, void *out,
+                                              void *hip_stream) {
+    moe_status st = check_layer(layer);
+    if (st != MOE_OK) return st;
+    if (n_tokens < 0) return MOE_ERR_INVALID_ARG;
+    if (n_tokens > MOE_MAX_TOKENS) return MOE_ERR_UNSUPPORTED;
+    if (n_tokens == 0) return MOE_OK;
+    if (workspace_layout(layer, n_tokens).total > MOE_STATIC_SCRATCH_BYTES) return MOE_ERR_WORKSPACE;
+    void *ws = nullptr;
+    if ((st = scratch_of((hipStream_t)hip_stream, &ws)) != MOE_OK) return st;
+    return moe_decode_layer(layer, logits, x, n_tokens, topk_idx, topk_w, plan, residual, out, ws,
+                            MOE_STATIC_SCRATCH_BYTES, hip_stream);
 }

@@ -32,7 +32,7 @@ def test_library_exports_every_declared_function():
     assert set(declared) == set(_lib.EXPORTS)
     for name in declared:
         assert hasattr(L, name), name
-    assert L.moe_abi_version() == 6
+    assert L.moe_abi_version() == 7
 
 
 def test_status_strings():
@@ -268,3 +268,21 @@ def test_binding_requires_the_built_library(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "library_path", lambda: str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="not built"):
         _lib.lib()
+
+
+def test_static_entry_point_refuses_what_its_scratch_cannot_hold():
+    """moe_decode_layer_static checks the layer and the size on the host,
+    before it looks up its device array: no device is touched here."""
+    L = moe.lib()
+    st = layer()
+    p = moe.PlanStruct(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+    f = L.moe_decode_layer_static
+    X, LG, I, WT, O = FAKE + 0x1000000, FAKE + 0x2000000, FAKE + 0x3000000, FAKE + 0x4000000, FAKE + 0x5000000
+    per_token = 8 * 768 * 4 + 8 * 2048 * 4  # h and y of the 2048 x 768 top-8 layer
+    fits = moe.MOE_STATIC_SCRATCH_BYTES // per_token
+    assert fits == 93
+    assert f(C.byref(st), LG, X, fits + 1, I, WT, C.byref(p), None, O, None) == moe.MOE_ERR_WORKSPACE
+    assert f(C.byref(st), LG, X, 0, I, WT, C.byref(p), None, O, None) == moe.MOE_OK  # no launch
+    assert f(C.byref(st), LG, X, -1, I, WT, C.byref(p), None, O, None) == moe.MOE_ERR_INVALID_ARG
+    assert f(C.byref(layer(top_k=0)), LG, X, 1, I, WT, C.byref(p), None, O, None) == moe.MOE_ERR_INVALID_ARG
+
