@@ -3,31 +3,37 @@
 
 A step is one pass of the whole hot path over one batch, moe_decode_layer:
 router, cohort planner, fused gate+up, down projection and combine.  For
-one token that is two launches (a gate+up kernel that routes for itself,
-then down + combine); for a batch, moe_route_plan (router and planner in
-one launch), the gate+up kernels and the down and combine kernels.  The
-default workload is the single-token decode layer (hidden 2048, dff 768, 128
-experts, top-8, B = 1, affine int4 g64 weights, bf16 activations).  Steps
-rotate over R layer instances resident in HBM (48 by default, 16.3 GB of
-weights, ~1 GB of distinct expert bytes touched per rotation), so the 256 MB
-Infinity Cache cannot serve repeated weight reads.  Every input is seeded
-synthetic data (moe_workloads); the weights are drawn and quantised on the
-device.
+up to 8 tokens that is two launches (a gate+up kernel that routes, plans
+and deduplicates for itself, then down + combine); for larger batches,
+moe_route_plan (or the router and planner kernels), the gate+up kernels and
+the down and combine kernels.  The default workload is the single-token
+decode layer (hidden 2048, dff 768, 128 experts, top-8, B = 1, affine int4
+g64 weights, bf16 activations).  Steps rotate over R layer instances
+resident in HBM (48 by default, 16.3 GB of weights, ~1 GB of distinct expert
+bytes touched per rotation), so the 256 MB Infinity Cache cannot serve
+repeated weight reads.  Every input is seeded synthetic data (moe_workloads);
+the weights are drawn and quantised on the device.
 
-Timed passes (HIP graphs of one rotation, replayed; HIP events on the
-capturing stream):
-  1. headline: K whole steps  -> steps/s, unique-expert GB/s
-  2. kernels : R launches of each half of the step alone (moe_route_gate_up,
-     moe_expert_down_combine) -> the average duration of the dominant
-     kernel (gate+up: two thirds of the bytes) for the roofline entry
-  3. ladder  : B = 4 / 8 (30 % sharing), B = 32 (Zipf 1.1) and prefill
-     chunks of B = 256 / 1024 on the same layers -> sublinearity of the
-     step time in B, and the expert GEMM rate of the large batches
-  4. next rows: the router projection (moe_router_logits) alone, the step
+Timed passes (HIP graphs, replayed; HIP events on the capturing stream):
+  1. headline : exactly K steps after W warm-up steps -> steps/s, unique
+     expert GB/s; then three more passes of K steps for the min-max spread
+  2. kernels  : R launches of each half of the step alone (moe_route_gate_up,
+     moe_expert_down_combine) -> the dominant kernel's (gate+up: two thirds
+     of the bytes) average duration for the roofline entry
+  3. calibration: a streaming read and a copy of 4 GiB, and the time per
+     node of a graph of tiny kernels (the launch floor of a graph)
+  4. ladder   : B = 4 / 8 (30 % sharing, random and disjoint routing), B =
+     32 (Zipf 1.1, random, disjoint), prefill chunks of B = 256 / 1024, and
+     the wide clamped layer (hidden 4096, dff 2048, 256 experts, top-6,
+     sidecar, clamp 10) at B = 1 / 4 -> each three passes, min-max
+  5. stack    : the 48-layer all-MoE step at B = 32 (Zipf 1.1 per layer),
+     each layer's output fed to the next through the residual, one graph
+  6. next rows: the router projection (moe_router_logits) alone, the step
      with the GeGLU activation and a down-projection sidecar, and the step
      at other weight widths (4-bit gate/up with 6-bit down; 8-bit)
 The oracle (plain fp64 C, OpenMP) is timed on a bounded sample of the same
-workload on the host cores (rank 0, N = 1 only).
+workload on the host's cores, at all cores and at one core, median of three
+(rank 0, N = 1 only).
 
 Prints ONE JSON line.  ``--gpus N`` with N > 1 exits: the library and its
 benchmark run on one GPU (how the path would shard is described, not
@@ -86,7 +92,8 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ladder", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle sample budget")
+    ap.add_argument("--cpu-seconds", type=float, default=4.0,
+                    help="oracle sample budget per pass (three passes at all cores, three at one)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration)")
     return ap.parse_args()
@@ -171,29 +178,52 @@ def time_graph(g, reps):
     return a.elapsed_time(b) / 1e3  # seconds
 
 
-def run_steps(rot, K, W):
-    """Headline pass: W warm-up steps, then exactly K timed steps."""
-    import torch
+class StepTimer:
+    """One rotation captured as a graph (plus a graph of the remainder of K
+    steps); passes of exactly K steps timed between HIP events."""
 
-    R = rot.R
-    g_all = capture(lambda: [rot.step(i) for i in range(R)])
-    rem = K % R
-    g_rem = capture(lambda: [rot.step(i) for i in range(rem)]) if rem else None
-    for _ in range(max(1, math.ceil(W / R))):
-        g_all.replay()
-    torch.cuda.synchronize()
-    a = torch.cuda.Event(enable_timing=True)
-    b = torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    a.record()
-    for _ in range(K // R):
-        g_all.replay()
-    if g_rem is not None:
-        g_rem.replay()
-    b.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    return a.elapsed_time(b) / 1e3, wall
+    def __init__(self, rot):
+        self.rot = rot
+        R = rot.R
+        self.g_all = capture(lambda: [rot.step(i) for i in range(R)])
+        self.g_rem = {}
+
+    def warm(self, W):
+        for _ in range(max(1, math.ceil(W / self.rot.R))):
+            self.g_all.replay()
+
+    def time(self, K):
+        """Seconds for exactly K steps, and the wall time around them."""
+        import torch
+
+        R = self.rot.R
+        rem = K % R
+        if rem and rem not in self.g_rem:
+            self.g_rem[rem] = capture(lambda: [self.rot.step(i) for i in range(rem)])
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        a.record()
+        for _ in range(K // R):
+            self.g_all.replay()
+        if rem:
+            self.g_rem[rem].replay()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / 1e3, time.perf_counter() - t0
+
+
+def spread(values):
+    v = sorted(values)
+    return {"min": v[0], "median": v[len(v) // 2], "max": v[-1], "n": len(v)}
+
+
+def run_steps(rot, K, W):
+    """W warm-up steps, then exactly K timed steps."""
+    st = StepTimer(rot)
+    st.warm(W)
+    return st.time(K)
 
 
 def run_kernel_pass(rot, reps=4):
@@ -297,6 +327,104 @@ def gate_up_bytes(shape, n_unique):
     return n_unique * 2 * shape.hidden * shape.dff * BYTES_PER_WEIGHT
 
 
+class StackChain:
+    """The 48-layer all-MoE step: layer l reads x_l, adds its expert output to
+    it (the residual) and writes x_{l+1}, which layer l+1 reads; B tokens,
+    logits pre-generated per layer (Zipf 1.1 expert popularity)."""
+
+    def __init__(self, moe, shape, layers, B, regime, seed):
+        import torch
+        from moe_workloads import make_logits, make_x
+
+        dev = torch.device("cuda")
+        self.moe, self.shape, self.B, self.layers = moe, shape, B, layers
+        L = len(layers)
+        self.logits = [torch.from_numpy(make_logits(shape, B, layer=l, regime=regime, seed=seed)).to(dev)
+                       for l in range(L)]
+        x0 = make_x(shape, B, layer=0, seed=seed)
+        self.xs = [torch.from_numpy(x0.view(np.int16)).to(dev).view(torch.bfloat16)]
+        self.xs += [torch.empty_like(self.xs[0]) for _ in range(L)]
+        k = shape.top_k
+        self.plans = [moe.Plan.allocate(shape.n_experts, B * k, device=dev) for _ in range(L)]
+        self.idx = torch.empty((B, k), dtype=torch.int32, device=dev)
+        self.w = torch.empty((B, k), dtype=torch.float32, device=dev)
+        self.ws = moe.alloc_workspace(layers[0], B, device=dev)
+
+    def step(self):
+        for l, layer in enumerate(self.layers):
+            self.moe.decode_layer(layer, self.xs[l], self.logits[l], self.plans[l], self.ws, self.xs[l + 1],
+                                  residual=self.xs[l], bufs={"idx": self.idx, "w": self.w})
+
+    def n_unique(self):
+        return [int(p.n_unique.item()) for p in self.plans]
+
+
+def run_stack_chain(moe, shape, layers, B, regime, seed, reps=5, passes=3):
+    import torch
+
+    sc = StackChain(moe, shape, layers, B, regime, seed)
+    g = capture(sc.step)
+    g.replay()
+    torch.cuda.synchronize()
+    ts = [time_graph(g, reps) / reps for _ in range(passes)]
+    nu = sc.n_unique()
+    ub = sum(unique_bytes(shape, n) for n in nu)
+    sp = spread(ts)
+    st = sp["median"]
+    return {"workload": f"{len(layers)}-layer all-MoE step, B={B}, {regime} routing, residual between layers",
+            "layers": len(layers), "B": B, "ms_per_step": st * 1e3,
+            "ms_per_step_min": sp["min"] * 1e3, "ms_per_step_max": sp["max"] * 1e3, "passes": passes,
+            "steps_per_s": 1 / st, "tokens_per_s": B / st, "unique_experts_per_layer": float(np.mean(nu)),
+            "unique_bytes_per_step": ub, "unique_gbps": ub / st / 1e9, "hbm_frac": ub / st / 1e9 / HBM_PEAK_GBPS}
+
+
+def calibration(n_bytes=4 << 30, reps=5):
+    """Streaming read and copy of n_bytes, and the time per node of a graph
+    of 100 one-element kernels (the launch floor of a graph node)."""
+    import torch
+
+    a = torch.ones(n_bytes // 4, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    out = torch.empty((), dtype=torch.float32, device="cuda")
+
+    def best(fn):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) / 1e3)
+        return min(ts)
+
+    t_read = best(lambda: torch.sum(a, dim=0, out=out))
+    t_copy = best(lambda: b.copy_(a))
+    del a, b
+    tiny = torch.zeros(1, device="cuda")
+    g = capture(lambda: [tiny.add_(1.0) for _ in range(100)])
+    g.replay()
+    t_node = min(time_graph(g, 10) / 1000 for _ in range(3))
+    torch.cuda.empty_cache()
+    return {"stream_read_gbps": n_bytes / t_read / 1e9, "copy_gbps": 2 * n_bytes / t_copy / 1e9,
+            "bytes": n_bytes, "graph_node_us": t_node * 1e6,
+            "note": "read: torch.sum over 4 GiB fp32; copy: 4 GiB each way (read + write counted); "
+                    "graph node: one-element add kernels, 100 per graph"}
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 # ------------------------------------------------------------ CPU oracle
 def cpu_baseline(rot, budget_s):
     """The oracle as it stands, on a bounded sample of the same workload:
@@ -323,32 +451,53 @@ def cpu_baseline(rot, budget_s):
                   down_q=np.zeros((E, H, F // 8), np.uint32), down_s=np.full((E, H, F // 64), POISON_F16, np.uint16),
                   down_b=np.full((E, H, F // 64), POISON_F16, np.uint16),
                   sidecar=None if t.get("sidecar") is None else t["sidecar"].cpu().numpy(), clamp=sh.clamp)
+        cols = rot.layers[i].down_layout == rot.moe.MOE_DOWN_COLS
         for e in ids:
-            for n in ("gate_q", "up_q", "down_q"):
-                getattr(L, n)[e] = t[n][e].cpu().numpy().view(np.uint32)
-            for n in ("gate_s", "gate_b", "up_s", "up_b", "down_s", "down_b"):
-                getattr(L, n)[e] = t[n][e].cpu().numpy().view(np.uint16)
+            for n in ("gate_q", "up_q"):
+                getattr(L, n)[e] = t[n][e].cpu().numpy().view(np.uint32).reshape(F, H // 8)
+            for n in ("gate_s", "gate_b", "up_s", "up_b"):
+                getattr(L, n)[e] = t[n][e].cpu().numpy().view(np.uint16).reshape(F, H // 64)
+            dq = t["down_q"][e].cpu().numpy().view(np.uint32)
+            # the column layout (moe_pack_down) back to the rows the oracle reads
+            L.down_q[e] = (dq.reshape(F // 32, H, 4).transpose(1, 0, 2).reshape(H, F // 8) if cols
+                           else dq.reshape(H, F // 8))
+            for n in ("down_s", "down_b"):
+                v = t[n][e].cpu().numpy().view(np.uint16)
+                getattr(L, n)[e] = v.reshape(F // 64, H).T if cols else v.reshape(H, F // 64)
         samples.append((L, x, lg))
     oracle.lib()
-    # one untimed warm-up step
-    L, x, lg = samples[0]
-    idx, w = oracle.route_topk(lg, sh.top_k)
-    oracle.plan(idx, E)
-    oracle.decode_step(L, x, idx, w)
-    done, t0 = 0, time.perf_counter()
-    while True:
-        L, x, lg = samples[done % n_slots]
-        idx, w = oracle.route_topk(lg, sh.top_k)
-        oracle.plan(idx, E)
-        oracle.decode_step(L, x, idx, w)
-        done += 1
-        el = time.perf_counter() - t0
-        if (el >= budget_s and done >= 3) or done >= 2000:
-            break
-    cores = int(os.environ.get("OMP_NUM_THREADS") or os.cpu_count() or 1)
-    return {"value": done / el, "unit": "steps/s", "cores": cores, "kind": "oracle",
-            "sample": f"{done} steps of the same workload over {n_slots} of its layer slots "
-                      f"({el:.1f} s of CPU time; fp64 per-slot oracle, no dedup)"}
+
+    def one_pass(budget):
+        done, t0 = 0, time.perf_counter()
+        while True:
+            L, x, lg = samples[done % n_slots]
+            idx, w = oracle.route_topk(lg, sh.top_k)
+            oracle.plan(idx, E)
+            oracle.decode_step(L, x, idx, w)
+            done += 1
+            el = time.perf_counter() - t0
+            if (el >= budget and done >= 3) or done >= 2000:
+                return done, el
+
+    all_threads = oracle.set_threads(int(os.environ.get("OMP_NUM_THREADS") or os.cpu_count() or 1))
+    res = {}
+    for label, threads in (("all", all_threads), ("one", 1)):
+        used = oracle.set_threads(threads)
+        one_pass(0.0)  # one untimed warm-up step
+        runs = [one_pass(budget_s) for _ in range(3)]
+        rates = sorted(d / el for d, el in runs)
+        res[label] = {"value": rates[1], "min": rates[0], "max": rates[2], "cores": used,
+                      "steps": [d for d, _ in runs], "seconds": [round(el, 2) for _, el in runs]}
+    oracle.set_threads(all_threads)
+    a_, o_ = res["all"], res["one"]
+    model = cpu_model()
+    return {"value": a_["value"], "unit": "steps/s", "cores": a_["cores"], "kind": "oracle",
+            "sample": f"median of 3 passes of ~{budget_s:.0f} s each ({sum(a_['steps'])} steps in all) of the "
+                      f"same workload over {n_slots} of its layer slots, at {a_['cores']} threads; fp64 per-slot "
+                      "oracle, no dedup: a correctness baseline, not a tuned CPU kernel",
+            "min": a_["min"], "max": a_["max"], "cpu_model": model,
+            "one_core": {"value": o_["value"], "min": o_["min"], "max": o_["max"], "cores": 1,
+                         "steps": o_["steps"], "seconds": o_["seconds"]}}
 
 
 # ------------------------------------------------------------------ main
@@ -415,32 +564,44 @@ def main():
     R = args.layers or max(8, min(48, int(math.ceil(16.3e9 / per_layer))))
     rot = Rotation(moe, sh, B, regime, R, args.seed)
 
-    secs, wall = run_steps(rot, args.steps, args.warmup)
+    timer = StepTimer(rot)
+    timer.warm(args.warmup)
+    secs, wall = timer.time(args.steps)  # the headline: exactly K steps
     nu = rot.n_unique()
     avg_unique = float(np.mean(nu))
     ms = secs * 1e3 / args.steps
     steps_per_s = args.steps / secs
     ub = unique_bytes(sh, avg_unique)
     gbps = ub / (secs / args.steps) / 1e9
+    passes = [timer.time(args.steps)[0] / args.steps * 1e6 for _ in range(3)]
     log(f"[bench] {args.workload}: {ms * 1e3:.2f} us/step, {steps_per_s:.0f} steps/s, "
-        f"unique {ub / 1e6:.2f} MB/step -> {gbps:.0f} GB/s ({gbps / HBM_PEAK_GBPS:.1%} of peak); wall {wall:.2f}s")
+        f"unique {ub / 1e6:.2f} MB/step -> {gbps:.0f} GB/s ({gbps / HBM_PEAK_GBPS:.1%} of peak); wall {wall:.2f}s; "
+        f"three more passes {' '.join(f'{p:.2f}' for p in passes)} us/step")
 
     if args.headline_only:
         print(json.dumps({"workload": args.workload, "regime": regime, "us_per_step": ms * 1e3,
-                          "unique_experts": avg_unique, "unique_gbps": gbps}), flush=True)
+                          "us_per_step_passes": passes, "unique_experts": avg_unique, "unique_gbps": gbps}),
+              flush=True)
         return
 
-    kt = run_kernel_pass(rot)
+    kpasses = [run_kernel_pass(rot) for _ in range(3)]
+    kt = {k: spread([kp[k] for kp in kpasses])["median"] for k in kpasses[0]}
     gu_bytes = gate_up_bytes(sh, avg_unique)
     dn_bytes = avg_unique * sh.hidden * sh.dff * BYTES_PER_WEIGHT
-    kernels = {k: {"us": v * 1e6} for k, v in kt.items()}
+    kernels = {k: {"us": v * 1e6, "us_min": min(kp[k] for kp in kpasses) * 1e6,
+                   "us_max": max(kp[k] for kp in kpasses) * 1e6} for k, v in kt.items()}
     kernels["route_gate_up"]["gbps"] = gu_bytes / kt["route_gate_up"] / 1e9
     kernels["down_combine"]["gbps"] = dn_bytes / kt["down_combine"] / 1e9
     log(f"[bench] kernels: " + ", ".join(f"{k} {v['us']:.2f} us" for k, v in kernels.items()))
     ach = gu_bytes / kt["route_gate_up"] / 1e9
-    gu_kernel = ("gate_up_route_kernel<64, 1, 4, true, 2, 4>" if B == 1 and sh.hidden == 2048 and sh.n_experts == 128
-                 else "gate_up_route_kernel" if B == 1 else "route_plan_kernel + gate_up kernels")
+    gu_kernel = ("gate_up_route_kernel<64, 1, 4, true, 2, 4, false>"
+                 if B == 1 and sh.hidden == 2048 and sh.n_experts == 128
+                 else "gate_up_route_kernel" if B <= 8 else "route_plan_kernel + gate_up kernels")
     traffic = counted_traffic(args.workload, gu_kernel)
+
+    cal = calibration()
+    log(f"[bench] calibration: streaming read {cal['stream_read_gbps']:.0f} GB/s, copy {cal['copy_gbps']:.0f} GB/s, "
+        f"graph node {cal['graph_node_us']:.2f} us")
 
     rp = run_router_projection(rot)
     log(f"[bench] router projection (next row): {rp['us']:.2f} us per launch, {rp['gbps']:.0f} GB/s")
@@ -457,32 +618,60 @@ def main():
             log(f"[bench] widths {kname} (next row): {v['us_per_step']:.2f} us/step, "
                 f"{v['unique_gbps']:.0f} GB/s of unique expert bytes")
 
-    ladder = []
+    t1 = secs / args.steps
+
+    def rung(wl, rg, layers, R2):
+        s2, b2, _, _ = WORKLOADS[wl]
+        s2h = SHAPES[s2]
+        lr = Rotation(moe, s2h, b2, rg, R2, args.seed, layers=layers)
+        tm = StepTimer(lr)
+        tm.warm(R2)
+        k2 = 2 * R2
+        sp = spread([tm.time(k2)[0] / k2 for _ in range(3)])
+        st = sp["median"]
+        nu2 = float(np.mean(lr.n_unique()))
+        ub2 = unique_bytes(s2h, nu2)
+        # multiply-adds actually required: 3 matrices of H x F per (token, k) slot
+        tflops = 2.0 * b2 * s2h.top_k * 3 * s2h.hidden * s2h.dff / st / 1e12
+        r = {"workload": wl, "B": b2, "routing": rg, "steps_per_s": 1.0 / st, "us_per_step": st * 1e6,
+             "us_per_step_min": sp["min"] * 1e6, "us_per_step_max": sp["max"] * 1e6, "passes": sp["n"],
+             "tokens_per_s": b2 / st, "unique_experts": nu2, "unique_bytes": ub2, "unique_gbps": ub2 / st / 1e9,
+             "hbm_frac": ub2 / st / 1e9 / HBM_PEAK_GBPS, "expert_tflops": tflops}
+        if s2h.hidden == sh.hidden and s2h.dff == sh.dff and s2h.n_experts == sh.n_experts:
+            r["step_time_vs_B1"] = st / t1
+        log(f"[bench] ladder {wl} ({rg}): {st * 1e6:.2f} us/step [{sp['min'] * 1e6:.2f}, {sp['max'] * 1e6:.2f}], "
+            f"n_unique {nu2:.1f}, {ub2 / st / 1e9:.0f} GB/s ({ub2 / st / 1e9 / HBM_PEAK_GBPS:.1%}), "
+            f"{tflops:.2f} TFLOP/s")
+        del lr, tm
+        return r
+
+    ladder, wide, stack = [], [], None
     if not args.no_ladder and sh.name in ("decode", "cohort", "stack"):
-        for wl in ("cohort4", "cohort8", "stack32", "prefill256", "prefill1024"):
-            s2, b2, r2, _ = WORKLOADS[wl]
-            lr = Rotation(moe, SHAPES[s2], b2, r2, R, args.seed, layers=rot.layers)
-            k2 = 2 * R
-            t2, _ = run_steps(lr, k2, R)
-            nu2 = float(np.mean(lr.n_unique()))
-            st = t2 / k2
-            s2h = SHAPES[s2]
-            # multiply-adds actually required: 3 matrices of H x F per (token, k) slot
-            tflops = 2.0 * b2 * s2h.top_k * 3 * s2h.hidden * s2h.dff / st / 1e12
-            ladder.append({"workload": wl, "B": b2, "steps_per_s": 1.0 / st, "us_per_step": st * 1e6,
-                           "tokens_per_s": b2 / st,
-                           "unique_experts": nu2, "unique_gbps": unique_bytes(s2h, nu2) / st / 1e9,
-                           "hbm_frac": unique_bytes(s2h, nu2) / st / 1e9 / HBM_PEAK_GBPS,
-                           "expert_tflops": tflops,
-                           "step_time_vs_B1": st / (secs / args.steps)})
-            log(f"[bench] ladder {wl}: {st * 1e6:.2f} us/step, n_unique {nu2:.1f}, "
-                f"t/t1 {st / (secs / args.steps):.2f}, {tflops:.2f} TFLOP/s")
-            del lr
+        for wl, rg in (("cohort4", "sharing"), ("cohort4", "normal"), ("cohort4", "disjoint"),
+                       ("cohort8", "sharing"), ("cohort8", "normal"), ("cohort8", "disjoint"),
+                       ("stack32", "zipf"), ("stack32", "normal"), ("stack32", "disjoint"),
+                       ("prefill256", "normal"), ("prefill1024", "normal")):
+            ladder.append(rung(wl, rg, rot.layers, R))
+        n_stack = min(48, len(rot.layers))
+        stack = run_stack_chain(moe, SHAPES["stack"], rot.layers[:n_stack], 32, "zipf", args.seed)
+        log(f"[bench] stack: {stack['ms_per_step']:.3f} ms per {n_stack}-layer step at B=32 "
+            f"[{stack['ms_per_step_min']:.3f}, {stack['ms_per_step_max']:.3f}], "
+            f"{stack['tokens_per_s']:.0f} tokens/s, {stack['unique_gbps']:.0f} GB/s ({stack['hbm_frac']:.1%})")
+        # the wide clamped layer on its own rotation (3.6 GB per layer)
+        wsh = SHAPES["wide"]
+        wper = wsh.n_experts * 3 * wsh.hidden * wsh.dff * BYTES_PER_WEIGHT
+        Rw = max(8, min(48, int(math.ceil(16.3e9 / wper))))
+        wrot = Rotation(moe, wsh, 1, "normal", Rw, args.seed)
+        for wl in ("wide1", "wide4"):
+            wide.append(rung(wl, "normal", wrot.layers, Rw))
+        del wrot
+        torch.cuda.empty_cache()
 
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(rot, args.cpu_seconds)
-        log(f"[bench] oracle: {cpu['value']:.2f} steps/s on {cpu['cores']} cores")
+        log(f"[bench] oracle: {cpu['value']:.2f} steps/s on {cpu['cores']} threads "
+            f"({cpu['one_core']['value']:.2f} on one), {cpu['cpu_model']}")
 
     line = {
         "metric": "MoE decode steps/s and unique-expert HBM GB/s (% of peak) at B=1/4/8/32",
@@ -495,7 +684,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": desc, "hidden": sh.hidden, "dff": sh.dff, "n_experts": sh.n_experts,
                    "top_k": sh.top_k, "n_tokens": B, "routing": regime,
@@ -504,12 +693,17 @@ def main():
                    "accumulation": "f32", "rotation_layers": R},
         "unique_gbps": gbps,
         "hbm_frac": gbps / HBM_PEAK_GBPS,
+        "hbm_frac_of_stream_read": gbps / cal["stream_read_gbps"],
         "unique_experts_per_step": avg_unique,
+        "passes_us_per_step": {"values": passes, **spread(passes)},
         "roofline": {"bound": "hbm", "kernel": gu_kernel, "achieved": ach, "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": ach / HBM_PEAK_GBPS, "traffic": traffic,
                      "bytes_per_launch": gu_bytes, "us_per_launch": kt["route_gate_up"] * 1e6},
         "kernels": kernels,
+        "calibration": cal,
         "ladder": ladder,
+        "stack48": stack,
+        "wide": wide,
         "next_rows": {"router_projection": rp, "geglu_down_sidecar": gg, "widths": widths},
         "cpu_baseline": cpu,
     }

@@ -76,6 +76,16 @@ def lib():
     return _lib
 
 
+def set_threads(n: int) -> int:
+    """OpenMP threads the oracle uses from now on (process-wide); returns
+    the number in effect.  Only the CPU-baseline timing changes it."""
+    lib()
+    gomp = C.CDLL("libgomp.so.1")
+    gomp.omp_set_num_threads(C.c_int(int(n)))
+    gomp.omp_get_max_threads.restype = C.c_int
+    return int(gomp.omp_get_max_threads())
+
+
 def _p(a: np.ndarray):
     return a.ctypes.data_as(C.c_void_p)
 
