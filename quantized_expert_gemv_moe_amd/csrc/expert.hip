@@ -411,8 +411,11 @@ __global__ __launch_bounds__(kBlock) void down_kernel(DownArgs a) {
 // tokens (from 16 tokens up the others go to the MFMA kernel), and every
 // stage issues its loads for all S slots whether or not they are used
 // (measured at 32 tokens: 93.6 us per step against 94.8 with four).
+// Sixteen-wave workgroups (dff 1536 and 2048) have 128 registers per wave;
+// with two slots per stage they spilled (dff 2048: 86 registers, 296 bytes
+// per lane of scratch), so they take one.
 template <int NW>
-constexpr int down_cols_stage() { return 2; }
+constexpr int down_cols_stage() { return NW >= 16 ? 1 : 2; }
 
 template <int NW, int CPW>
 __global__ __launch_bounds__(NW * kWave) void down_cols_kernel(const uint4 *__restrict__ q,
@@ -1005,10 +1008,25 @@ static int pow2_at_least(int k) {
     return p;
 }
 
-// LDS budget of the token-major down kernel, and the token counts from
-// which it takes two and four row blocks per workgroup.
-constexpr size_t kDownTokenLds = 65536;
+// LDS budget of the token-major down kernel: what one workgroup may hold on
+// the current device (160 KiB on gfx950; queried once per device, 64 KiB if
+// the query fails); and the token counts from which the kernel takes two
+// and four row blocks per workgroup.
 constexpr int kTokenRb2 = 2, kTokenRb4 = 4;
+static size_t down_token_lds_budget() {
+    static std::mutex mu;
+    static size_t budget[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 65536;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!budget[dev]) {
+        int v = 0;
+        budget[dev] = hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) == hipSuccess && v > 0
+                          ? (size_t)v
+                          : 65536;
+    }
+    return budget[dev];
+}
 
 static size_t down_token_lds(const moe_layer_t *L, int nw, int rb) {
     const int F = L->dff, G = F / kGroup, k = L->top_k;
@@ -1065,8 +1083,11 @@ static moe_status launch_down_token_k(const moe_layer_t *L, int n_tokens, const 
 // LDS budget and by hidden.
 static int down_token_rb(const moe_layer_t *L, int n_tokens, int nw) {
     const int rw = kWave / pow2_at_least(L->top_k);
-    for (int rb = n_tokens >= kTokenRb4 ? 4 : n_tokens >= kTokenRb2 ? 2 : 1; rb > 1; rb /= 2)
-        if (L->hidden % (rw * rb) == 0 && down_token_lds(L, nw, rb) <= kDownTokenLds) return rb;
+    // sixteen-wave workgroups (dff 1536, 2048) spill at four row blocks
+    const int rb_max = nw >= 16 ? 2 : 4;
+    int rb0 = n_tokens >= kTokenRb4 ? 4 : n_tokens >= kTokenRb2 ? 2 : 1;
+    for (int rb = rb0 < rb_max ? rb0 : rb_max; rb > 1; rb /= 2)
+        if (L->hidden % (rw * rb) == 0 && down_token_lds(L, nw, rb) <= down_token_lds_budget()) return rb;
     return 1;
 }
 
@@ -1078,7 +1099,7 @@ static moe_status launch_down_token(const moe_layer_t *L, int n_tokens, const fl
     int nw, cpw;
     if (L->down_layout != MOE_DOWN_COLS || !pick_down_cols(L->dff, &nw, &cpw)) return MOE_ERR_UNSUPPORTED;
     if (L->hidden % (kWave / pow2_at_least(L->top_k))) return MOE_ERR_UNSUPPORTED;
-    if (down_token_lds(L, nw, 1) > kDownTokenLds) return MOE_ERR_UNSUPPORTED;
+    if (down_token_lds(L, nw, 1) > down_token_lds_budget()) return MOE_ERR_UNSUPPORTED;
     const int rb = down_token_rb(L, n_tokens, nw);
     switch (nw * 100 + cpw) {
 #define MOE_DT(NW, CPW) \
