@@ -332,15 +332,21 @@ class StackChain:
     it (the residual) and writes x_{l+1}, which layer l+1 reads; B tokens,
     logits pre-generated per layer (Zipf 1.1 expert popularity)."""
 
-    def __init__(self, moe, shape, layers, B, regime, seed):
+    def __init__(self, moe, shape, layers, B, regime, seed, from_x=False):
         import torch
-        from moe_workloads import make_logits, make_x
+        from moe_workloads import make_logits, make_router, make_x
 
         dev = torch.device("cuda")
         self.moe, self.shape, self.B, self.layers = moe, shape, B, layers
         L = len(layers)
-        self.logits = [torch.from_numpy(make_logits(shape, B, layer=l, regime=regime, seed=seed)).to(dev)
-                       for l in range(L)]
+        self.routers = None
+        if from_x:  # each layer's logits projected from its own input (moe_router_logits)
+            self.routers = [torch.from_numpy(make_router(shape, layer=l, seed=seed).view(np.int16)).to(dev)
+                            .view(torch.bfloat16) for l in range(L)]
+            self.logits = [torch.empty((B, shape.n_experts), dtype=torch.float32, device=dev) for _ in range(L)]
+        else:
+            self.logits = [torch.from_numpy(make_logits(shape, B, layer=l, regime=regime, seed=seed)).to(dev)
+                           for l in range(L)]
         x0 = make_x(shape, B, layer=0, seed=seed)
         self.xs = [torch.from_numpy(x0.view(np.int16)).to(dev).view(torch.bfloat16)]
         self.xs += [torch.empty_like(self.xs[0]) for _ in range(L)]
@@ -352,6 +358,8 @@ class StackChain:
 
     def step(self):
         for l, layer in enumerate(self.layers):
+            if self.routers is not None:
+                self.moe.router_logits(self.xs[l], self.routers[l], self.logits[l])
             self.moe.decode_layer(layer, self.xs[l], self.logits[l], self.plans[l], self.ws, self.xs[l + 1],
                                   residual=self.xs[l], bufs={"idx": self.idx, "w": self.w})
 
@@ -359,10 +367,10 @@ class StackChain:
         return [int(p.n_unique.item()) for p in self.plans]
 
 
-def run_stack_chain(moe, shape, layers, B, regime, seed, reps=5, passes=3):
+def run_stack_chain(moe, shape, layers, B, regime, seed, reps=5, passes=3, from_x=False):
     import torch
 
-    sc = StackChain(moe, shape, layers, B, regime, seed)
+    sc = StackChain(moe, shape, layers, B, regime, seed, from_x=from_x)
     g = capture(sc.step)
     g.replay()
     torch.cuda.synchronize()
@@ -371,7 +379,8 @@ def run_stack_chain(moe, shape, layers, B, regime, seed, reps=5, passes=3):
     ub = sum(unique_bytes(shape, n) for n in nu)
     sp = spread(ts)
     st = sp["median"]
-    return {"workload": f"{len(layers)}-layer all-MoE step, B={B}, {regime} routing, residual between layers",
+    how = "routed from x by the router projection in front of each layer" if from_x else f"{regime} routing"
+    return {"workload": f"{len(layers)}-layer all-MoE step, B={B}, {how}, residual between layers",
             "layers": len(layers), "B": B, "ms_per_step": st * 1e3,
             "ms_per_step_min": sp["min"] * 1e3, "ms_per_step_max": sp["max"] * 1e3, "passes": passes,
             "steps_per_s": 1 / st, "tokens_per_s": B / st, "unique_experts_per_layer": float(np.mean(nu)),
@@ -645,7 +654,7 @@ def main():
         del lr, tm
         return r
 
-    ladder, wide, stack = [], [], None
+    ladder, wide, stack, stack_x = [], [], None, None
     if not args.no_ladder and sh.name in ("decode", "cohort", "stack"):
         for wl, rg in (("cohort4", "sharing"), ("cohort4", "normal"), ("cohort4", "disjoint"),
                        ("cohort8", "sharing"), ("cohort8", "normal"), ("cohort8", "disjoint"),
@@ -657,6 +666,10 @@ def main():
         log(f"[bench] stack: {stack['ms_per_step']:.3f} ms per {n_stack}-layer step at B=32 "
             f"[{stack['ms_per_step_min']:.3f}, {stack['ms_per_step_max']:.3f}], "
             f"{stack['tokens_per_s']:.0f} tokens/s, {stack['unique_gbps']:.0f} GB/s ({stack['hbm_frac']:.1%})")
+        stack_x = run_stack_chain(moe, SHAPES["stack"], rot.layers[:n_stack], 32, "normal", args.seed, from_x=True)
+        log(f"[bench] stack routed from x: {stack_x['ms_per_step']:.3f} ms per {n_stack}-layer step at B=32 "
+            f"[{stack_x['ms_per_step_min']:.3f}, {stack_x['ms_per_step_max']:.3f}], n_unique "
+            f"{stack_x['unique_experts_per_layer']:.1f}, {stack_x['unique_gbps']:.0f} GB/s ({stack_x['hbm_frac']:.1%})")
         # the wide clamped layer on its own rotation (3.6 GB per layer)
         wsh = SHAPES["wide"]
         wper = wsh.n_experts * 3 * wsh.hidden * wsh.dff * BYTES_PER_WEIGHT
@@ -703,6 +716,7 @@ def main():
         "calibration": cal,
         "ladder": ladder,
         "stack48": stack,
+        "stack48_from_x": stack_x,
         "wide": wide,
         "next_rows": {"router_projection": rp, "geglu_down_sidecar": gg, "widths": widths},
         "cpu_baseline": cpu,

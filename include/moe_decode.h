@@ -203,10 +203,11 @@ moe_status moe_route_plan(const float *logits, int32_t n_tokens, int32_t n_exper
  *   x         [n_tokens][hidden], act_dtype (bf16 or fp32), 16-byte aligned
  *   w_router  bf16 bits [n_experts][hidden], 16-byte aligned
  *   logits    fp32 [n_tokens][n_experts], the router's input
- * Products exact, fp32 accumulation in a fixed order.  MOE_ERR_UNSUPPORTED
- * when hidden has no lane geometry (hidden/8 must be a power of two up to 64
- * times 1..8) or n_experts > MOE_MAX_EXPERTS; n_tokens == 0 launches
- * nothing.  Asynchronous on hip_stream.
+ * Products exact, fp32 accumulation in a fixed order (a token's logits do
+ * not depend on the rest of the batch).  MOE_ERR_UNSUPPORTED when hidden has
+ * no lane geometry (hidden/8 must be a power of two up to 64 times 1..8),
+ * n_experts > MOE_MAX_EXPERTS or n_tokens > MOE_MAX_TOKENS; n_tokens == 0
+ * launches nothing.  Asynchronous on hip_stream.
  */
 moe_status moe_router_logits(const void *x, int32_t n_tokens, int32_t hidden, moe_dtype act_dtype,
                              const uint16_t *w_router, int32_t n_experts, float *logits, void *hip_stream);

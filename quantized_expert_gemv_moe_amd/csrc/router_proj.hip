@@ -4,9 +4,9 @@
 // router as one of the per-token costs).  Wr is a dense bf16 matrix
 // [n_experts][hidden].
 //
-// One wave per RPI = 64 / LPR expert rows: LPR lanes read a row as 16-byte
-// chunks (8 bf16), NV chunks per lane, once, and keep them in registers
-// while the wave walks the tokens.  With bf16 activations the products go
+// One wave per RPI = 64 / LPR expert rows and tile of tokens: LPR lanes read
+// a row as 16-byte chunks (8 bf16), NV chunks per lane, and apply them to
+// the tile's tokens from registers.  With bf16 activations the products go
 // through v_dot2_f32_bf16 (exact products, fp32 accumulation); with fp32
 // activations the weights are widened and multiplied with exact fp32 FMAs.
 // The lanes of a row are summed by a butterfly, so the sum order is fixed.
@@ -37,7 +37,14 @@ __device__ __forceinline__ float rp_dot8_f32(uint4 w, const float4 &x0, const fl
     return acc;
 }
 
-template <int LPR, int NV, bool XBF16>
+// Tokens per wave: a wave computes its rows for a tile of TT tokens, with
+// every activation load of the tile issued together; tiles go to separate
+// waves (grid y), so a batch spreads over many waves instead of one wave
+// walking every token.  A token's sum is formed the same way in any tile.
+template <int NV>
+constexpr int router_tile_tokens() { return NV <= 4 ? 4 : 2; }
+
+template <int LPR, int NV, bool XBF16, int TT>
 __global__ __launch_bounds__(kWave) void router_logits_kernel(const void *__restrict__ x,
                                                               const uint4 *__restrict__ wr,
                                                               float *__restrict__ logits, int n_tokens,
@@ -48,28 +55,50 @@ __global__ __launch_bounds__(kWave) void router_logits_kernel(const void *__rest
     const int row = blockIdx.x * RPI + lane / LPR;
     const int rr = row < n_experts ? row : n_experts - 1;
     const int K = hidden / 8;  // 16-byte chunks per row
+    const int t0 = blockIdx.y * TT;
     uint4 w[NV];
 #pragma unroll
     for (int v = 0; v < NV; ++v) w[v] = wr[(size_t)rr * K + v * LPR + sl];
-    for (int t = 0; t < n_tokens; ++t) {
-        float acc = 0.f;
+    float acc[TT];
+    if constexpr (XBF16) {
+        uint4 xv[TT][NV];  // tokens past the batch repeat its last one (not stored)
 #pragma unroll
-        for (int v = 0; v < NV; ++v) {
-            const int c = v * LPR + sl;
-            if constexpr (XBF16) {
-                const uint4 xv = ((const uint4 *)x)[(size_t)t * K + c];
-                acc = rp_dot2(w[v].x, xv.x, acc);
-                acc = rp_dot2(w[v].y, xv.y, acc);
-                acc = rp_dot2(w[v].z, xv.z, acc);
-                acc = rp_dot2(w[v].w, xv.w, acc);
-            } else {
-                const float4 *xp = (const float4 *)x + ((size_t)t * K + c) * 2;
-                acc = rp_dot8_f32(w[v], xp[0], xp[1], acc);
-            }
+        for (int i = 0; i < TT; ++i) {
+            const int t = t0 + i < n_tokens ? t0 + i : n_tokens - 1;
+#pragma unroll
+            for (int v = 0; v < NV; ++v) xv[i][v] = ((const uint4 *)x)[(size_t)t * K + v * LPR + sl];
         }
 #pragma unroll
-        for (int off = 1; off < LPR; off <<= 1) acc += __shfl_xor(acc, off, kWave);
-        if (sl == 0 && row < n_experts) logits[(size_t)t * n_experts + row] = acc;
+        for (int i = 0; i < TT; ++i) {
+            float a = 0.f;
+#pragma unroll
+            for (int v = 0; v < NV; ++v) {
+                a = rp_dot2(w[v].x, xv[i][v].x, a);
+                a = rp_dot2(w[v].y, xv[i][v].y, a);
+                a = rp_dot2(w[v].z, xv[i][v].z, a);
+                a = rp_dot2(w[v].w, xv[i][v].w, a);
+            }
+            acc[i] = a;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < TT; ++i) {
+            const int t = t0 + i < n_tokens ? t0 + i : n_tokens - 1;
+            float a = 0.f;
+#pragma unroll
+            for (int v = 0; v < NV; ++v) {
+                const float4 *xp = (const float4 *)x + ((size_t)t * K + v * LPR + sl) * 2;
+                a = rp_dot8_f32(w[v], xp[0], xp[1], a);
+            }
+            acc[i] = a;
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < TT; ++i) {
+        float a = acc[i];
+#pragma unroll
+        for (int off = 1; off < LPR; off <<= 1) a += __shfl_xor(a, off, kWave);
+        if (sl == 0 && row < n_experts && t0 + i < n_tokens) logits[(size_t)(t0 + i) * n_experts + row] = a;
     }
 }
 
@@ -92,13 +121,14 @@ template <int LPR, int NV>
 static void launch_router(const void *x, const uint16_t *wr, float *logits, int n_tokens, int hidden,
                           int n_experts, bool bf16, hipStream_t s) {
     constexpr int RPI = kWave / LPR;
-    const dim3 grid((n_experts + RPI - 1) / RPI);
+    constexpr int TT = router_tile_tokens<NV>();
+    const dim3 grid((n_experts + RPI - 1) / RPI, (n_tokens + TT - 1) / TT);
     if (bf16)
-        hipLaunchKernelGGL((router_logits_kernel<LPR, NV, true>), grid, dim3(kWave), 0, s, x, (const uint4 *)wr,
-                           logits, n_tokens, hidden, n_experts);
+        hipLaunchKernelGGL((router_logits_kernel<LPR, NV, true, TT>), grid, dim3(kWave), 0, s, x,
+                           (const uint4 *)wr, logits, n_tokens, hidden, n_experts);
     else
-        hipLaunchKernelGGL((router_logits_kernel<LPR, NV, false>), grid, dim3(kWave), 0, s, x, (const uint4 *)wr,
-                           logits, n_tokens, hidden, n_experts);
+        hipLaunchKernelGGL((router_logits_kernel<LPR, NV, false, TT>), grid, dim3(kWave), 0, s, x,
+                           (const uint4 *)wr, logits, n_tokens, hidden, n_experts);
 }
 
 }  // namespace moe
@@ -110,7 +140,7 @@ extern "C" moe_status moe_router_logits(const void *x, int32_t n_tokens, int32_t
                                         void *hip_stream) {
     if (n_tokens < 0 || hidden <= 0 || n_experts <= 0) return MOE_ERR_INVALID_ARG;
     if (act_dtype != MOE_DTYPE_BF16 && act_dtype != MOE_DTYPE_F32) return MOE_ERR_INVALID_ARG;
-    if (n_experts > MOE_MAX_EXPERTS) return MOE_ERR_UNSUPPORTED;
+    if (n_experts > MOE_MAX_EXPERTS || n_tokens > MOE_MAX_TOKENS) return MOE_ERR_UNSUPPORTED;
     int lpr = 0, nv = 0;
     if (hidden % 8 || !pick_router_geometry(hidden / 8, &lpr, &nv)) return MOE_ERR_UNSUPPORTED;
     if (n_tokens == 0) return MOE_OK;

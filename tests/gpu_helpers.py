@@ -23,13 +23,27 @@ REL_L2_GATE = 2e-3
 # p ~ 2 * 2e-6 / 2^-8 ~ 1e-3 of the elements moves by one bf16 ulp (2^-8
 # relative), so this distance is ~sqrt(p) * 2^-8 ~ 1.5e-4 on average and,
 # the flips being few in a small output, up to ~3e-4.  Rounding h, the
-# weights or the per-expert outputs to bf16 scores 2e-3 or more.
-REL_L2_DIAG = 5e-4
+# weights or the per-expert outputs to bf16 scores 2e-3 or more.  Largest
+# seen over every case of the suite: 2.4e-4 (4 sampled tokens of one stack
+# layer, where few flips weigh most); median 2.7e-5.
+REL_L2_DIAG = 3e-4
 # Intermediate h (fp32 on both sides): the bf16 nibble dot with its +128
 # offset carries ~2e-6 relative error; exact fp32 paths ~1e-7.
 REL_L2_H = 1e-5
 # Router weights: fp32 exp/divide against fp64.
 W_ABS = 1e-6
+
+
+def record(tag: str, **vals):
+    """Appends one case's figures to the JSON-lines file named by
+    MOE_PARITY_LOG, if set (pytest keeps passing tests' prints to itself)."""
+    import json
+    import os
+
+    path = os.environ.get("MOE_PARITY_LOG")
+    if path:
+        with open(path, "a") as f:
+            f.write(json.dumps({"case": tag, **vals}) + "\n")
 
 
 def log(msg):
@@ -122,6 +136,7 @@ def check_against_oracle(L, x, logits, run: GpuRun, tag: str, diag=True):
         ref16 = oracle.round_f32(out64).astype(np.float64)
     dg = rel_l2(got, ref16)
     log(f"[parity] {tag}: n_unique={p['n_unique']} h_rel={eh:.3g} out_rel={gate:.3g} diag={dg:.3g}")
+    record(tag, n_unique=int(p["n_unique"]), h=eh, out=gate, diag=dg)
     assert np.isfinite(got).all(), f"{tag}: non-finite output"
     assert eh <= REL_L2_H, f"{tag}: h rel L2 {eh}"
     assert gate <= REL_L2_GATE, f"{tag}: output rel L2 {gate}"

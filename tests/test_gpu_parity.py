@@ -11,7 +11,8 @@ import pytest
 import torch
 
 import quantized_expert_gemv_moe_amd as moe
-from gpu_helpers import GpuRun, check_against_oracle, dev_x, host_bits, layer_for, log, rel_l2
+from gpu_helpers import (REL_L2_DIAG, REL_L2_GATE, GpuRun, check_against_oracle, dev_x, host_bits, layer_for,
+                         log, record, rel_l2)
 from moe_workloads import SHAPES, Shape, make_layer, make_logits, make_router, make_x
 from oracle import oracle
 
@@ -494,7 +495,8 @@ def test_prefill_sized_batch_on_sampled_tokens(B, layout):
     eo = rel_l2(got, out64)
     dg = rel_l2(got, oracle.bf16_to_f64(oracle.round_bf16(out64)))
     log(f"[parity] prefill B={B} {layout}: {len(toks)} tokens h_rel={eh:.3g} out_rel={eo:.3g} diag={dg:.3g}")
-    assert eh <= 1e-5 and eo <= 2e-3 and dg <= 5e-4
+    record(f"prefill B{B} {layout}", h=eh, out=eo, diag=dg)
+    assert eh <= 1e-5 and eo <= REL_L2_GATE and dg <= REL_L2_DIAG
     assert np.isfinite(oracle.bf16_to_f64(run.out)).all()
 
 
@@ -603,6 +605,120 @@ def test_residual_stack_of_layers():
     e = rel_l2(got, oracle.bf16_to_f64(ref))
     log(f"[stack] final x rel L2 {e:.3g}")
     assert e <= 2e-3
+
+
+def _host_layer(sh, t, experts):
+    """A host copy of a device layer (rows layout) holding only `experts`;
+    the others keep poisoned scales, so a wrong gather cannot pass."""
+    from moe_workloads.gen import _empty_layer
+
+    L = _empty_layer(sh)
+    for e in experts:
+        for n in ("gate_q", "up_q", "down_q"):
+            dst = getattr(L, n)
+            dst[e] = t[n][e].cpu().numpy().view(np.uint32).reshape(dst.shape[1:])
+        for n in ("gate_s", "gate_b", "up_s", "up_b", "down_s", "down_b"):
+            dst = getattr(L, n)
+            dst[e] = t[n][e].cpu().numpy().view(np.uint16).reshape(dst.shape[1:])
+        L.materialised[e] = True
+    return L
+
+
+def _check_stack_chain(n_layers, B, from_x, seed):
+    """Runs the chained all-MoE stack layer by layer and checks every layer:
+    routing and plan bit-exact for all tokens (against the oracle's routing
+    of the logits the layer used); the layer's expert output against the
+    oracle on 4 sampled tokens, from the GPU chain's own input to that layer,
+    so each layer is checked without error carried over from the ones
+    before it; and the next layer's input bit-exact equal to
+    bf16(x + bf16(out)) for every token.  With from_x each layer's logits are
+    projected from its input (moe_router_logits) and checked against the
+    oracle's projection first.  Weights are drawn on the device; only the
+    experts the sampled tokens touch are copied for the oracle."""
+    from moe_workloads import make_layer_device
+
+    sh = SHAPES["stack"]
+    k, E = sh.top_k, sh.n_experts
+    rng = np.random.default_rng(seed)
+    x = dev_x(make_x(sh, B, seed=seed))
+    plan = moe.Plan.allocate(E, B * k)
+    ws = None
+    worst = 0.0
+    for l in range(n_layers):
+        if from_x:
+            wr = make_router(sh, layer=l, seed=seed)
+            lgt = moe.router_logits(x, torch.from_numpy(wr.view(np.int16)).cuda().view(torch.bfloat16))
+            torch.cuda.synchronize()
+            lg = lgt.cpu().numpy()
+            xb = host_bits(x)
+            ref = oracle.router_logits(xb, wr)
+            mag = np.abs(oracle.bf16_to_f64(xb)) @ np.abs(oracle.bf16_to_f64(wr)).T
+            assert np.all(np.abs(lg.astype(np.float64) - ref) <= 1e-5 * mag), f"layer {l}: router logits"
+        else:
+            lg = make_logits(sh, B, layer=l, regime="zipf", seed=seed)
+            lgt = torch.from_numpy(lg).cuda()
+        t = make_layer_device(sh, l, torch.device("cuda"), seed=seed)
+        rows = moe.DeviceLayer.from_tensors(sh.hidden, sh.dff, E, k, sh.act, 0.0, t)
+        dl = rows.pack_down()
+        if ws is None:
+            ws = moe.alloc_workspace(dl, B)
+        out = torch.empty_like(x)
+        nxt = torch.empty_like(x)
+        _, idx, w, _ = moe.decode_layer(dl, x, lgt, plan=plan, workspace=ws, out=out)
+        moe.decode_layer(dl, x, lgt, plan=plan, workspace=ws, out=nxt, residual=x)
+        torch.cuda.synchronize()
+        ridx, rw = oracle.route_topk(lg, k)
+        assert np.array_equal(idx.cpu().numpy(), ridx), f"layer {l}: routing"
+        assert float(np.abs(w.cpu().numpy() - rw).max()) <= 1e-6, f"layer {l}: router weights"
+        p = oracle.plan(ridx, E)
+        assert np.array_equal(plan.sorted_slots[:B * k].cpu().numpy(), p["sorted_slots"]), f"layer {l}: plan"
+        assert np.array_equal(plan.counts.cpu().numpy(), p["counts"]), f"layer {l}: plan counts"
+        xb, ob, nb = host_bits(x), host_bits(out), host_bits(nxt)
+        # NaN bit patterns carry no value: compare them as one value
+        canon = lambda a: np.where(np.isnan(oracle.bf16_to_f64(a)), np.uint16(0x7FC0), a)
+        want = oracle.residual_bf16(xb, oracle.bf16_to_f64(ob))
+        assert np.array_equal(canon(nb), canon(want)), f"layer {l}: residual"
+        # Nothing normalises the residual stream between layers, so on these
+        # N(0, 0.02) weights a few tokens' activations grow until they
+        # overflow bf16 in the last layers.  Sample finite tokens for the
+        # tolerance checks, and check that an overflowed token overflows in
+        # the oracle too.
+        fin = np.isfinite(oracle.bf16_to_f64(ob)).all(axis=1) & np.isfinite(oracle.bf16_to_f64(xb)).all(axis=1)
+        S = np.sort(rng.choice(np.flatnonzero(fin), min(4, int(fin.sum())), replace=False))
+        L = _host_layer(sh, t, np.unique(ridx[S]))
+        o64 = oracle.decode_step(L, xb[S], ridx[S], rw[S])
+        got = oracle.bf16_to_f64(ob[S])
+        gate = rel_l2(got, o64)
+        diag = rel_l2(got, oracle.bf16_to_f64(oracle.round_bf16(o64)))
+        record(f"stack {'from x ' if from_x else ''}layer {l}", n_unique=int(p["n_unique"]), out=gate, diag=diag,
+               overflowed_tokens=int(B - fin.sum()))
+        assert gate <= REL_L2_GATE, f"layer {l}: output rel L2 {gate}"
+        assert diag <= REL_L2_DIAG, f"layer {l}: diagnostic rel L2 {diag}"
+        if not fin.all():
+            v = int(np.flatnonzero(~fin)[0])
+            Lv = _host_layer(sh, t, np.unique(ridx[v]))
+            ov = oracle.round_bf16(oracle.decode_step(Lv, xb[v:v + 1], ridx[v:v + 1], rw[v:v + 1]))
+            assert not np.isfinite(oracle.bf16_to_f64(ov)).all(), f"layer {l}: token {v} overflows on the GPU only"
+        worst = max(worst, gate)
+        x = nxt
+        del t, rows, dl, L
+    return worst
+
+
+def test_48_layer_stack_step():
+    """The 48-layer all-MoE step at B = 32 with Zipf(1.1) routing per layer,
+    each layer reading the previous layer's output through the residual, as
+    the benchmark runs it; every layer checked (see _check_stack_chain)."""
+    worst = _check_stack_chain(48, 32, from_x=False, seed=48)
+    log(f"[stack48] worst layer output rel L2 {worst:.3g}")
+
+
+def test_stack_routed_from_x():
+    """Eight chained layers at B = 32 whose routing starts from x: each
+    layer's logits projected from its own input by moe_router_logits, as the
+    benchmark's stack routed from x runs it."""
+    worst = _check_stack_chain(8, 32, from_x=True, seed=49)
+    log(f"[stack from x] worst layer output rel L2 {worst:.3g}")
 
 
 def test_invalid_expert_id_gives_nan_for_that_token_only():
