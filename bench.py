@@ -245,23 +245,31 @@ def run_kernel_pass(rot, reps=4):
     return res
 
 
-def run_router_projection(rot, reps=4):
+def run_router_projection(rot, reps=4, batches=(1, 32)):
     """The router projection in front of the router (moe_router_logits),
-    timed alone on R distinct bf16 weight matrices; not part of the step,
-    whose router starts from logits."""
+    timed alone on R distinct bf16 weight matrices at each batch size; the
+    stack routed from x runs it in front of every layer."""
     import torch
+    from moe_workloads import make_x
 
     sh, R = rot.shape, rot.R
     gen = torch.Generator(device="cuda")
     gen.manual_seed(1234)
     wr = [(torch.randn((sh.n_experts, sh.hidden), device="cuda", generator=gen) / math.sqrt(sh.hidden))
           .to(torch.bfloat16) for _ in range(R)]
-    lg = [torch.empty((rot.B, sh.n_experts), dtype=torch.float32, device="cuda") for _ in range(R)]
-    g = capture(lambda: [rot.moe.router_logits(rot.x[i], wr[i], lg[i]) for i in range(R)])
-    g.replay()
-    t = time_graph(g, reps) / (reps * R)
     nbytes = sh.n_experts * sh.hidden * 2
-    return {"us": t * 1e6, "gbps": nbytes / t / 1e9, "bytes_per_launch": nbytes}
+    res = {"bytes_per_launch": nbytes}
+    for B in batches:
+        xb = make_x(sh, B, seed=77)
+        x = torch.from_numpy(xb.view(np.int16)).cuda().view(torch.bfloat16) if sh.act == "bf16" else \
+            torch.from_numpy(xb).cuda()
+        lg = [torch.empty((B, sh.n_experts), dtype=torch.float32, device="cuda") for _ in range(R)]
+        g = capture(lambda: [rot.moe.router_logits(x, wr[i], lg[i]) for i in range(R)])
+        g.replay()
+        t = time_graph(g, reps) / (reps * R)
+        res[f"B{B}"] = {"us": t * 1e6, "gbps": nbytes / t / 1e9}
+    res["us"], res["gbps"] = res[f"B{batches[0]}"]["us"], res[f"B{batches[0]}"]["gbps"]
+    return res
 
 
 def run_geglu_down_sidecar(rot, regime, seed):
@@ -613,7 +621,8 @@ def main():
         f"graph node {cal['graph_node_us']:.2f} us")
 
     rp = run_router_projection(rot)
-    log(f"[bench] router projection (next row): {rp['us']:.2f} us per launch, {rp['gbps']:.0f} GB/s")
+    log(f"[bench] router projection (next row): B=1 {rp['B1']['us']:.2f} us per launch ({rp['B1']['gbps']:.0f} GB/s), "
+        f"B=32 {rp['B32']['us']:.2f} us")
 
     gg = run_geglu_down_sidecar(rot, regime, args.seed)
     gg["step_time_vs_swiglu"] = gg["us_per_step"] / (ms * 1e3)

@@ -417,25 +417,26 @@ __global__ __launch_bounds__(kBlock) void down_kernel(DownArgs a) {
 template <int NW>
 constexpr int down_cols_stage() { return NW >= 16 ? 1 : 2; }
 
-// Block (bx: 64 output rows, u: distinct expert) of the column kernel; the
-// workgroup has exactly NW waves.
 template <int NW, int CPW>
-__device__ __forceinline__ void down_cols_block(const uint4 *__restrict__ q, const uint16_t *__restrict__ sc,
-                                                const uint16_t *__restrict__ bi, const float *__restrict__ h,
-                                                float *__restrict__ y, PlanView plan, int hidden, int dff,
-                                                int n_experts, int n_slots, int max_count, int bx, int u) {
+__global__ __launch_bounds__(NW * kWave) void down_cols_kernel(const uint4 *__restrict__ q,
+                                                               const uint16_t *__restrict__ sc,
+                                                               const uint16_t *__restrict__ bi,
+                                                               const float *__restrict__ h,
+                                                               float *__restrict__ y, PlanView plan,
+                                                               int hidden, int dff, int n_experts,
+                                                               int n_slots, int max_count) {
     constexpr int S = down_cols_stage<NW>();
     constexpr int NG = CPW / 2 + 1;  // groups a wave's CPW chunks can touch
     __shared__ float part[NW][S][kWave];
     __shared__ float4 hw[NW][S][NG][kGroup / 4];  // each wave's groups of h
     Work wk;
-    if (!plan_expert(plan, u, n_experts, n_slots, &wk)) return;
+    if (!plan_expert(plan, blockIdx.y, n_experts, n_slots, &wk)) return;
     if (wk.count > max_count) return;  // the MFMA kernel's expert
     const int lane = threadIdx.x & (kWave - 1);
     // wave index as a scalar: addresses built from it stay wave-uniform
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int H = hidden, F = dff, C = F / 32, G = F / kGroup;
-    const int m = bx * kWave + lane;  // hidden % 64 == 0: always a row
+    const int m = blockIdx.x * kWave + lane;  // hidden % 64 == 0: always a row
     const int c0 = wave * CPW;
     const int g0 = c0 / 2;  // first group of the wave's chunks
 
@@ -529,18 +530,6 @@ __device__ __forceinline__ void down_cols_block(const uint4 *__restrict__ q, con
     }
 }
 
-template <int NW, int CPW>
-__global__ __launch_bounds__(NW * kWave) void down_cols_kernel(const uint4 *__restrict__ q,
-                                                               const uint16_t *__restrict__ sc,
-                                                               const uint16_t *__restrict__ bi,
-                                                               const float *__restrict__ h,
-                                                               float *__restrict__ y, PlanView plan,
-                                                               int hidden, int dff, int n_experts,
-                                                               int n_slots, int max_count) {
-    down_cols_block<NW, CPW>(q, sc, bi, h, y, plan, hidden, dff, n_experts, n_slots, max_count, blockIdx.x,
-                             blockIdx.y);
-}
-
 // ----------------------------------------------------- down, MFMA tiles
 
 // Experts with many tokens, column layout: v_mfma_f32_16x16x32_bf16 with h
@@ -573,26 +562,26 @@ __device__ __forceinline__ void split3_pairs(const float *v, uint32_t (*o)[4]) {
     }
 }
 
-// Block (bx: 16 * RT output rows, u: distinct expert) of the MFMA kernel in
-// a workgroup of NWB >= NW waves: waves NW .. NWB - 1 only help fill LDS and
-// meet the barriers (the mixed launch gives both kernels one workgroup size).
-template <int NW, int GW, int RT, int NWB>
-__device__ __forceinline__ void down_mfma_block(const uint32_t *__restrict__ q, const uint16_t *__restrict__ sc,
-                                                const uint16_t *__restrict__ bi, const float *__restrict__ h,
-                                                float *__restrict__ y, PlanView plan, int hidden, int n_experts,
-                                                int n_slots, int min_count, int bx, int u, float *smem) {
+template <int NW, int GW, int RT>
+__global__ __launch_bounds__(NW * kWave) void down_mfma_kernel(const uint32_t *__restrict__ q,
+                                                               const uint16_t *__restrict__ sc,
+                                                               const uint16_t *__restrict__ bi,
+                                                               const float *__restrict__ h,
+                                                               float *__restrict__ y, PlanView plan,
+                                                               int hidden, int n_experts, int n_slots,
+                                                               int min_count) {
     constexpr int ROWS = 16 * RT;
     constexpr int G = NW * GW, C = 2 * G, F = C * 32;
+    extern __shared__ float smem[];
     Work wk;
-    if (!plan_expert(plan, u, n_experts, n_slots, &wk)) return;
+    if (!plan_expert(plan, blockIdx.y, n_experts, n_slots, &wk)) return;
     if (wk.count < min_count) return;  // the VALU kernel's expert
     const int H = hidden;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const bool active = NWB == NW || wave < NW;
     const int r16 = lane & 15, kq = lane >> 4;
-    const int m0 = bx * ROWS;
-    const int g0 = (active ? wave : 0) * GW;
+    const int m0 = blockIdx.x * ROWS;
+    const int g0 = wave * GW;
 
     // h of the lane's token (8 values of chunk 2g and 8 of chunk 2g + 1 per
     // group); unconditional loads (a lane without a token reads slot 0's
@@ -623,26 +612,23 @@ __device__ __forceinline__ void down_mfma_block(const uint32_t *__restrict__ q, 
 
     // this wave's weights: word kq of chunks 2g, 2g + 1 of each row tile
     uint32_t wa[GW][RT][2];
-    if (active) {  // (always, outside the mixed launch)
 #pragma unroll
-        for (int gi = 0; gi < GW; ++gi)
+    for (int gi = 0; gi < GW; ++gi)
 #pragma unroll
-            for (int t = 0; t < RT; ++t)
+        for (int t = 0; t < RT; ++t)
 #pragma unroll
-                for (int c2 = 0; c2 < 2; ++c2) {
-                    const int c = 2 * (g0 + gi) + c2;
-                    wa[gi][t][c2] =
-                        __builtin_nontemporal_load(q + (((size_t)wk.e * C + c) * H + m0 + 16 * t + r16) * 4 + kq);
-                }
-    }
+            for (int c2 = 0; c2 < 2; ++c2) {
+                const int c = 2 * (g0 + gi) + c2;
+                wa[gi][t][c2] = __builtin_nontemporal_load(q + (((size_t)wk.e * C + c) * H + m0 + 16 * t + r16) * 4 + kq);
+            }
     __builtin_amdgcn_sched_barrier(0);
     slot = r16 < wk.count ? slot : 0;
-    if (active) load_h(slot, r16 < wk.count);
+    load_h(slot, r16 < wk.count);
     // per [group][row]: 16 * scale, and bias - 16 * scale (the weights go
     // into the MFMA as 1 + q / 16)
     float *ss = smem, *sb = smem + G * ROWS;
     float *part = smem + 2 * G * ROWS;  // [wave][lane][4 * RT]
-    for (int i = threadIdx.x; i < ROWS * G; i += NWB * kWave) {
+    for (int i = threadIdx.x; i < ROWS * G; i += NW * kWave) {
         const int g = i / ROWS, r = i - g * ROWS;
         const size_t si = ((size_t)wk.e * G + g) * H + m0 + r;
         const float s1 = f16_bits_to_f32(sc[si]);
@@ -656,14 +642,13 @@ __device__ __forceinline__ void down_mfma_block(const uint32_t *__restrict__ q, 
         const bool live = r16 < nt;  // this lane's token column
         if (t0 > 0) {
             slot = live ? plan_slot(plan, wk, t0 + r16, n_slots) : 0;
-            if (active) load_h(slot, live);
+            load_h(slot, live);
         }
         f32x4_t acc[RT];
 #pragma unroll
         for (int t = 0; t < RT; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int gi = 0; gi < GW; ++gi) {
-            if (!active) break;
             const int g = g0 + gi;
             uint32_t hb[2][3][4];
             float hs = 0.f;
@@ -694,17 +679,15 @@ __device__ __forceinline__ void down_mfma_block(const uint32_t *__restrict__ q, 
                 acc[t][3] += fmaf(s1.w, d[3], b1.w * hs);
             }
         }
-        if (active) {
-            float *mine = part + ((size_t)wave * kWave + lane) * (4 * RT);
+        float *mine = part + ((size_t)wave * kWave + lane) * (4 * RT);
 #pragma unroll
-            for (int t = 0; t < RT; ++t)
+        for (int t = 0; t < RT; ++t)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) mine[t * 4 + i] = acc[t][i];
-        }
+            for (int i = 0; i < 4; ++i) mine[t * 4 + i] = acc[t][i];
         __syncthreads();
         // add the partials in wave order: output o = (row tile, row of the
         // lane's four) goes to wave o % NW
-        if (live && active) {
+        if (live) {
             for (int o = wave; o < 4 * RT; o += NW) {
                 const int t = o / 4, i = o % 4;
                 float v = 0.f;
@@ -715,46 +698,6 @@ __device__ __forceinline__ void down_mfma_block(const uint32_t *__restrict__ q, 
         }
         __syncthreads();
     }
-}
-
-template <int NW, int GW, int RT>
-__global__ __launch_bounds__(NW * kWave) void down_mfma_kernel(const uint32_t *__restrict__ q,
-                                                               const uint16_t *__restrict__ sc,
-                                                               const uint16_t *__restrict__ bi,
-                                                               const float *__restrict__ h,
-                                                               float *__restrict__ y, PlanView plan,
-                                                               int hidden, int n_experts, int n_slots,
-                                                               int min_count) {
-    extern __shared__ float smem[];
-    down_mfma_block<NW, GW, RT, NW>(q, sc, bi, h, y, plan, hidden, n_experts, n_slots, min_count, blockIdx.x,
-                                    blockIdx.y, smem);
-}
-
-// Both down kernels of a batch in one launch: blocks [0, mfma_blocks) are
-// MFMA blocks (row tile, distinct expert) for the experts with min_count or
-// more tokens, the later ones column blocks (64 rows, distinct expert) for
-// the others; the workgroup has the column kernel's NWC waves (>= NWM), so
-// its arithmetic is unchanged.  The two kinds run side by side instead of
-// one launch after the other.
-template <int NWC, int CPW, int NWM, int GW, int RT>
-__global__ __launch_bounds__(NWC * kWave) void down_mixed_kernel(const uint4 *__restrict__ q,
-                                                                 const uint16_t *__restrict__ sc,
-                                                                 const uint16_t *__restrict__ bi,
-                                                                 const float *__restrict__ h,
-                                                                 float *__restrict__ y, PlanView plan,
-                                                                 int hidden, int dff, int n_experts, int n_slots,
-                                                                 int min_count, int mfma_blocks, int rb_mfma) {
-    static_assert(NWM <= NWC, "the MFMA part runs on a subset of the workgroup's waves");
-    extern __shared__ float smem[];
-    const int b = blockIdx.x;
-    if (b < mfma_blocks) {
-        down_mfma_block<NWM, GW, RT, NWC>((const uint32_t *)q, sc, bi, h, y, plan, hidden, n_experts, n_slots,
-                                          min_count, b % rb_mfma, b / rb_mfma, smem);
-        return;
-    }
-    const int rb_cols = hidden / kWave, c = b - mfma_blocks;
-    down_cols_block<NWC, CPW>(q, sc, bi, h, y, plan, hidden, dff, n_experts, n_slots, min_count - 1, c % rb_cols,
-                              c / rb_cols);
 }
 
 // ---------------------------------------------------------------- combine
@@ -1325,38 +1268,6 @@ static moe_status launch_down_mfma(const moe_layer_t *L, const float *h, float *
     return MOE_OK;
 }
 
-// Both down kernels in one launch (down_mixed_kernel) for the dff values
-// whose column geometry has at least as many waves as the MFMA shape;
-// MOE_ERR_UNSUPPORTED otherwise (the caller launches them one after the
-// other).
-static moe_status launch_down_mixed(const moe_layer_t *L, const float *h, float *y, PlanView pv, int groups_y,
-                                    int n_slots, int nw_m, int gw, hipStream_t s) {
-    constexpr int RT = kMfmaDownRowTiles;
-    int nw_c = 0, cpw = 0;
-    if (!pick_down_cols(L->dff, &nw_c, &cpw) || nw_m > nw_c) return MOE_ERR_UNSUPPORTED;
-    const int G = L->dff / kGroup;
-    const size_t lds = ((size_t)2 * G * 16 * RT + (size_t)nw_m * kWave * 4 * RT) * sizeof(float);
-    const int rb_mfma = L->hidden / (16 * RT);
-    const int mfma_blocks = rb_mfma * groups_y;
-    const dim3 grid(mfma_blocks + (L->hidden / kWave) * groups_y);
-    const long key = ((long)nw_c * 100 + cpw) * 10000 + nw_m * 100 + gw;
-    switch (key) {
-#define MOE_DX(NWC, CPW, NWM, GW)                                                                                 \
-    case ((long)NWC * 100 + CPW) * 10000 + NWM * 100 + GW:                                                        \
-        hipLaunchKernelGGL((down_mixed_kernel<NWC, CPW, NWM, GW, RT>), grid, dim3(NWC * kWave), lds, s,            \
-                           (const uint4 *)L->down_q, L->down_s, L->down_b, h, y, pv, L->hidden, L->dff,           \
-                           L->n_experts, n_slots, kMfmaMinCount, mfma_blocks, rb_mfma);                          \
-        break;
-        // dff 128, 256, 512, 768, 1024 (1536 and 2048 spilled registers in one
-        // launch and keep two)
-        MOE_DX(4, 1, 2, 1) MOE_DX(8, 1, 4, 1) MOE_DX(8, 2, 8, 1) MOE_DX(8, 3, 6, 2)
-        MOE_DX(16, 2, 8, 2)
-#undef MOE_DX
-        default: return MOE_ERR_UNSUPPORTED;
-    }
-    return MOE_OK;
-}
-
 static moe_status enqueue_down_combine(const moe_layer_t *layer, int n_tokens, const int32_t *topk_idx,
                                        const float *topk_w, const moe_plan_t *plan,
                                        const void *residual, void *out, void *workspace,
@@ -1376,12 +1287,8 @@ static moe_status enqueue_down_combine(const moe_layer_t *layer, int n_tokens, c
         int nw = 0, gw = 0;
         const bool mfma = n_tokens >= kMfmaMinTokens && mfma_down_shape(layer, &nw, &gw);
         const int gy = groups_y_of(layer, n_tokens), n_slots = n_tokens * layer->top_k;
-        st = mfma ? launch_down_mixed(layer, h, y, plan_view(plan), gy, n_slots, nw, gw, stream) : MOE_ERR_UNSUPPORTED;
-        if (st == MOE_ERR_UNSUPPORTED) {
-            st = launch_down_cols(layer, h, y, plan_view(plan), gy, n_slots, mfma ? kMfmaMinCount - 1 : INT_MAX,
-                                  stream);
-            if (st == MOE_OK && mfma) st = launch_down_mfma(layer, h, y, plan_view(plan), gy, n_slots, nw, gw, stream);
-        }
+        st = launch_down_cols(layer, h, y, plan_view(plan), gy, n_slots, mfma ? kMfmaMinCount - 1 : INT_MAX, stream);
+        if (st == MOE_OK && mfma) st = launch_down_mfma(layer, h, y, plan_view(plan), gy, n_slots, nw, gw, stream);
     } else {
         Geometry gd;
         pick_geometry(layer->dff, &gd);

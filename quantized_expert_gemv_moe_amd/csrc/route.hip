@@ -50,15 +50,19 @@ __global__ __launch_bounds__(kBlock) void route_topk_kernel(const float *__restr
     }
 }
 
-// Small plans (<= 64 slots) run on one wave; larger ones on 256 threads.
-template <int PER_LANE>
-__global__ __launch_bounds__(kBlock) void expert_plan_kernel(const int *__restrict__ topk_idx, int n_slots,
-                                                             int n_experts, PlanOut p) {
+// Small plans (<= 64 slots) run on one wave; larger ones on NT threads:
+// 256, or 1024 from kPlanWideSlots slots on (the scatter's waves each walk
+// one range of the slots, so more waves shorten it).
+constexpr int kPlanWideSlots = 1024;
+
+template <int PER_LANE, int NT>
+__global__ __launch_bounds__(NT) void expert_plan_kernel(const int *__restrict__ topk_idx, int n_slots,
+                                                         int n_experts, PlanOut p) {
     if (n_slots <= kWave) {
         __shared__ int cnt[MOE_MAX_EXPERTS], off[MOE_MAX_EXPERTS], uix[MOE_MAX_EXPERTS];
         if (threadIdx.x < kWave) plan_wave_small<PER_LANE>(topk_idx, n_slots, n_experts, p, cnt, off, uix);
     } else {
-        plan_block<kBlock>(topk_idx, n_slots, n_experts, p);
+        plan_block<NT>(topk_idx, n_slots, n_experts, p);
     }
 }
 
@@ -132,9 +136,16 @@ extern "C" moe_status moe_expert_plan(const int32_t *topk_idx, int32_t n_tokens,
     if (st != MOE_OK) return st;
     hipStream_t stream = (hipStream_t)hip_stream;
     const int n_slots = n_tokens * top_k;
-    MOE_PER_LANE_SWITCH(per_lane_bucket(n_experts),
-                        hipLaunchKernelGGL(expert_plan_kernel<PL>, dim3(1), dim3(n_slots <= kWave ? kWave : kBlock),
-                                           0, stream, topk_idx, n_slots, n_experts, plan_out(plan)))
+    if (n_slots >= kPlanWideSlots) {
+        MOE_PER_LANE_SWITCH(per_lane_bucket(n_experts),
+                            hipLaunchKernelGGL((expert_plan_kernel<PL, 1024>), dim3(1), dim3(1024), 0, stream,
+                                               topk_idx, n_slots, n_experts, plan_out(plan)))
+    } else {
+        MOE_PER_LANE_SWITCH(per_lane_bucket(n_experts),
+                            hipLaunchKernelGGL((expert_plan_kernel<PL, kBlock>), dim3(1),
+                                               dim3(n_slots <= kWave ? kWave : kBlock), 0, stream, topk_idx, n_slots,
+                                               n_experts, plan_out(plan)))
+    }
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_DEVICE;
 }
 

@@ -209,28 +209,42 @@ struct PlanOut {
 };
 
 // The planner body for one workgroup of NT threads (256 or 1024).  `idx`
-// may live in global memory or in LDS.
+// may live in global memory or in LDS.  The slots are cut into one
+// contiguous range per wave; every wave counts its range per expert, each
+// wave's first position per expert follows from the expert's offset plus
+// the counts of the waves before it, and then every wave scatters its own
+// range in slot order (64 slots at a time), so the waves place their slots
+// at once and the sort stays stable.
 template <int NT>
 __device__ __forceinline__ void plan_block(const int *idx, int n_slots, int n_experts, const PlanOut &p) {
+    constexpr int NW = NT / kWave;
     __shared__ int cnt[MOE_MAX_EXPERTS];
-    __shared__ int cursor[MOE_MAX_EXPERTS];
+    __shared__ int cntw[NW][MOE_MAX_EXPERTS];  // per wave: count, then first position
     __shared__ int first_slot[MOE_MAX_EXPERTS];
-    __shared__ int uniq[MOE_MAX_EXPERTS];
-    __shared__ int lds_scan[NT / kWave];
+    __shared__ int lds_scan[NW];
     const int tid = threadIdx.x;
     const unsigned E = (unsigned)n_experts;
+    const int span = n_slots > NW ? (n_slots + NW - 1) / NW : 1;  // slots per wave range
 
     for (int e = tid; e < n_experts; e += NT) {
-        cnt[e] = 0;
         first_slot[e] = INT_MAX;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) cntw[w][e] = 0;
     }
     __syncthreads();
     for (int s = tid; s < n_slots; s += NT) {
         const int e = idx[s];
         if ((unsigned)e < E) {
-            atomicAdd(&cnt[e], 1);          // integer: order-free
+            atomicAdd(&cntw[s / span][e], 1);  // integer: order-free
             atomicMin(&first_slot[e], s);
         }
+    }
+    __syncthreads();
+    for (int e = tid; e < n_experts; e += NT) {
+        int c = 0;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) c += cntw[w][e];
+        cnt[e] = c;
     }
     __syncthreads();
 
@@ -252,11 +266,16 @@ __device__ __forceinline__ void plan_block(const int *idx, int n_slots, int n_ex
         if (e < n_experts) {
             p.counts[e] = c[i];
             p.offsets[e] = run;
-            cursor[e] = run;
+            int base = run;  // each wave's first position for e
+#pragma unroll
+            for (int w = 0; w < NW; ++w) {
+                const int cw = cntw[w][e];
+                cntw[w][e] = base;
+                base += cw;
+            }
             if (c[i] > 0) {
                 p.unique_experts[urun] = e;
                 p.work[urun] = make_int4(e, run, c[i], first_slot[e]);
-                uniq[urun] = e;
                 ++urun;
             }
         }
@@ -272,15 +291,18 @@ __device__ __forceinline__ void plan_block(const int *idx, int n_slots, int n_ex
     }
     __syncthreads();
 
-    // stable scatter, one wave, 64 slots at a time in slot order
-    if (tid < kWave) {
-        const int lane = tid;
+    // stable scatter: wave w walks its range in slot order, 64 slots at a time
+    {
+        const int lane = tid & (kWave - 1);
+        const int w = tid / kWave;
+        int *cursor = cntw[w];
         const int id_bits = n_experts > 1 ? 32 - __clz(n_experts - 1) : 0;
         const unsigned long long below = (1ull << lane) - 1ull;
-        for (int base = 0; base < n_slots; base += kWave) {
+        const int end = (w + 1) * span < n_slots ? (w + 1) * span : n_slots;
+        for (int base = w * span; base < end; base += kWave) {
             const int s = base + lane;
-            const int e = s < n_slots ? idx[s] : -1;
-            const bool ok = s < n_slots && (unsigned)e < E;
+            const int e = s < end ? idx[s] : -1;
+            const bool ok = s < end && (unsigned)e < E;
             unsigned long long peers = __ballot(ok);
             for (int b = 0; b < id_bits; ++b) {
                 const bool bit = ok && ((e >> b) & 1);

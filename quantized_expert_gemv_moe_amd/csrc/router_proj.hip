@@ -41,8 +41,10 @@ __device__ __forceinline__ float rp_dot8_f32(uint4 w, const float4 &x0, const fl
 // every activation load of the tile issued together; tiles go to separate
 // waves (grid y), so a batch spreads over many waves instead of one wave
 // walking every token.  A token's sum is formed the same way in any tile.
+// Up to 4 tokens per tile (2 for rows of more than 4 chunks per lane), never
+// more than the batch.
 template <int NV>
-constexpr int router_tile_tokens() { return NV <= 4 ? 4 : 2; }
+constexpr int router_tile_max() { return NV <= 4 ? 4 : 2; }
 
 template <int LPR, int NV, bool XBF16, int TT>
 __global__ __launch_bounds__(kWave) void router_logits_kernel(const void *__restrict__ x,
@@ -121,14 +123,23 @@ template <int LPR, int NV>
 static void launch_router(const void *x, const uint16_t *wr, float *logits, int n_tokens, int hidden,
                           int n_experts, bool bf16, hipStream_t s) {
     constexpr int RPI = kWave / LPR;
-    constexpr int TT = router_tile_tokens<NV>();
-    const dim3 grid((n_experts + RPI - 1) / RPI, (n_tokens + TT - 1) / TT);
-    if (bf16)
-        hipLaunchKernelGGL((router_logits_kernel<LPR, NV, true, TT>), grid, dim3(kWave), 0, s, x,
+    const int tt = n_tokens >= router_tile_max<NV>() ? router_tile_max<NV>() : n_tokens >= 2 ? 2 : 1;
+    const dim3 grid((n_experts + RPI - 1) / RPI, (n_tokens + tt - 1) / tt);
+#define MOE_RPT(TT)                                                                                         \
+    if (bf16)                                                                                               \
+        hipLaunchKernelGGL((router_logits_kernel<LPR, NV, true, TT>), grid, dim3(kWave), 0, s, x,           \
+                           (const uint4 *)wr, logits, n_tokens, hidden, n_experts);                         \
+    else                                                                                                    \
+        hipLaunchKernelGGL((router_logits_kernel<LPR, NV, false, TT>), grid, dim3(kWave), 0, s, x,          \
                            (const uint4 *)wr, logits, n_tokens, hidden, n_experts);
-    else
-        hipLaunchKernelGGL((router_logits_kernel<LPR, NV, false, TT>), grid, dim3(kWave), 0, s, x,
-                           (const uint4 *)wr, logits, n_tokens, hidden, n_experts);
+    if (tt == 1) {
+        MOE_RPT(1)
+    } else if (tt == 2 || router_tile_max<NV>() == 2) {
+        MOE_RPT(2)
+    } else {
+        MOE_RPT(router_tile_max<NV>())
+    }
+#undef MOE_RPT
 }
 
 }  // namespace moe
