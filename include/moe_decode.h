@@ -123,8 +123,13 @@ typedef enum { MOE_ACT_SWIGLU = 0, MOE_ACT_GEGLU = 1 } moe_activation;
  * multiplies that expert's down-projection output y before the weighted
  * combine: the second of the "both sidecars" that page "perf(moe):
  * attribute ..." names (Problem / Background), which it does not define
- * further.  Fields after expert_scale were appended in ABI versions 5
- * (down_scale, activation) and 6 (down_bits).
+ * further.
+ *
+ * Field order: the fields through expert_scale are those of the plain
+ * 4-bit layer, in that order; the extensions follow, and all-zero
+ * extensions mean the plain layer (rows-layout down, no down scale,
+ * SwiGLU, down projection as wide as gate and up), so a caller that only
+ * knows the plain fields and zero-fills the rest gets the plain layer.
  */
 typedef struct {
     int32_t hidden;      /* H, multiple of 64 */
@@ -133,15 +138,19 @@ typedef struct {
     int32_t top_k;       /* k, 1..min(E, MOE_MAX_TOP_K) */
     int32_t bits;        /* 4, 6 or 8 (gate and up) */
     int32_t group_size;  /* 32, 64 or 128; divides hidden and dff */
-    int32_t act_dtype;   /* moe_dtype of x, residual and out */
+    int32_t act_dtype;   /* moe_dtype of x, residual and out (int32, as wide as
+                            the enum, so that any value is defined to read) */
     float clamp_limit;   /* >= 0; 0 disables the clamp */
-    int32_t down_layout; /* moe_down_layout */
-    const uint32_t *gate_q, *up_q, *down_q;
-    const uint16_t *gate_s, *gate_b, *up_s, *up_b, *down_s, *down_b;
+    const uint32_t *gate_q, *up_q;
+    const uint16_t *gate_s, *gate_b, *up_s, *up_b;
+    const uint32_t *down_q;
+    const uint16_t *down_s, *down_b;
     const float *expert_scale; /* [E] or NULL */
+    /* extensions; zero = the plain layer */
+    int32_t down_layout;       /* moe_down_layout */
     const float *down_scale;   /* [E] or NULL */
     int32_t activation;        /* moe_activation */
-    int32_t down_bits;         /* 4, 6 or 8 (down projection) */
+    int32_t down_bits;         /* 4, 6 or 8 (down projection); 0 = bits */
 } moe_layer_t;
 
 /*
@@ -158,6 +167,9 @@ typedef struct {
  *                        the last distinct expert {-1, B*k, 0, 0}.  The
  *                        expert kernels read only this record before they
  *                        stream an expert's weights.  16-byte aligned.
+ *                        Appended after the five plain arrays; it is
+ *                        required (a plan without it is refused with
+ *                        MOE_ERR_INVALID_ARG).
  */
 typedef struct {
     int32_t *counts, *offsets, *sorted_slots, *unique_experts, *n_unique;
@@ -221,8 +233,7 @@ size_t moe_workspace_size(const moe_layer_t *layer, int32_t max_tokens);
  *   x         [n_tokens][hidden], act_dtype
  *   topk_idx  int32 [n_tokens][top_k], topk_w fp32 [n_tokens][top_k]
  *   plan      the plan of topk_idx (host struct of device pointers)
- *   residual  optional [n_tokens][hidden] act_dtype, NULL = none
- *   out       [n_tokens][hidden] act_dtype; must not alias x or residual
+ *   out       [n_tokens][hidden] act_dtype; must not alias x
  *   workspace device memory of at least moe_workspace_size(layer, n_tokens)
  *             bytes, 256-byte aligned; its contents need no initialisation
  *
@@ -235,7 +246,7 @@ size_t moe_workspace_size(const moe_layer_t *layer, int32_t max_tokens);
  *   y *= down_scale[e]             (if given)
  *   o_t = sum_{j<k} topk_w[t][j] * y_{t,j}, in j order, rounded once to
  *         act_dtype (round to nearest even)
- *   out_t = o_t, or with a residual: act(residual_t + o_t) in fp32
+ *   out_t = o_t
  *
  * The fp32 partials with one final rounding follow page "perf(moe):
  * batched decode scales 1.55x against 3.25x on dense", Implementation
@@ -250,9 +261,22 @@ size_t moe_workspace_size(const moe_layer_t *layer, int32_t max_tokens);
  * than 3 tokens stay bitwise equal.
  */
 moe_status moe_decode_step(const moe_layer_t *layer, const void *x, int32_t n_tokens,
-                           const int32_t *topk_idx, const float *topk_w,
-                           const moe_plan_t *plan, const void *residual, void *out,
-                           void *workspace, size_t workspace_bytes, void *hip_stream);
+                           const int32_t *topk_idx, const float *topk_w, const moe_plan_t *plan,
+                           void *out, void *workspace, size_t workspace_bytes, void *hip_stream);
+
+/*
+ * moe_decode_step with the residual add of a layer stack fused into the
+ * combine's store: out_t = act(residual_t + o_t), the sum formed in fp32
+ * from the unrounded o_t and rounded once to act_dtype (the layer stack
+ * runs every MoE layer on every decode tick, page "perf(moe):
+ * attribute the MoE decode gap at the M = 1 expert gather", Problem /
+ * Background).  residual is [n_tokens][hidden] act_dtype or NULL (then
+ * exactly moe_decode_step); out must not alias x or residual.
+ */
+moe_status moe_decode_step_residual(const moe_layer_t *layer, const void *x, int32_t n_tokens,
+                                    const int32_t *topk_idx, const float *topk_w,
+                                    const moe_plan_t *plan, const void *residual, void *out,
+                                    void *workspace, size_t workspace_bytes, void *hip_stream);
 
 /*
  * One layer step from router logits: moe_route_plan, then moe_decode_step,
@@ -352,7 +376,9 @@ moe_status moe_layer_check(const moe_layer_t *layer);
 /* Static description of a status code. */
 const char *moe_status_str(moe_status status);
 
-/* ABI version: bumped when a signature or struct changes (7: moe_decode_layer_static). */
+/* ABI version: bumped when a signature or struct changes (8: plain field
+ * order of moe_layer_t, moe_decode_step without a residual,
+ * moe_decode_step_residual). */
 int32_t moe_abi_version(void);
 
 #ifdef __cplusplus

@@ -38,11 +38,12 @@ class LayerStruct(C.Structure):
     _fields_ = [
         ("hidden", C.c_int32), ("dff", C.c_int32), ("n_experts", C.c_int32), ("top_k", C.c_int32),
         ("bits", C.c_int32), ("group_size", C.c_int32), ("act_dtype", C.c_int32),
-        ("clamp_limit", C.c_float), ("down_layout", C.c_int32),
-        ("gate_q", C.c_void_p), ("up_q", C.c_void_p), ("down_q", C.c_void_p),
+        ("clamp_limit", C.c_float),
+        ("gate_q", C.c_void_p), ("up_q", C.c_void_p),
         ("gate_s", C.c_void_p), ("gate_b", C.c_void_p), ("up_s", C.c_void_p), ("up_b", C.c_void_p),
-        ("down_s", C.c_void_p), ("down_b", C.c_void_p),
-        ("expert_scale", C.c_void_p), ("down_scale", C.c_void_p), ("activation", C.c_int32),
+        ("down_q", C.c_void_p), ("down_s", C.c_void_p), ("down_b", C.c_void_p),
+        ("expert_scale", C.c_void_p),
+        ("down_layout", C.c_int32), ("down_scale", C.c_void_p), ("activation", C.c_int32),
         ("down_bits", C.c_int32),
     ]
 
@@ -55,7 +56,7 @@ class PlanStruct(C.Structure):
 _lib = None
 
 EXPORTS = ("moe_router_logits", "moe_route_topk", "moe_expert_plan", "moe_route_plan", "moe_workspace_size",
-           "moe_decode_step",
+           "moe_decode_step", "moe_decode_step_residual",
            "moe_decode_layer", "moe_decode_layer_static", "moe_route_gate_up", "moe_expert_gate_up", "moe_expert_down_combine", "moe_pack_down",
            "moe_layer_check", "moe_status_str", "moe_abi_version")
 
@@ -86,8 +87,11 @@ def lib() -> C.CDLL:
         L.moe_workspace_size.argtypes = [C.POINTER(LayerStruct), i32]
         L.moe_workspace_size.restype = C.c_size_t
         L.moe_decode_step.argtypes = [C.POINTER(LayerStruct), vp, i32, vp, vp, C.POINTER(PlanStruct),
-                                      vp, vp, vp, C.c_size_t, vp]
+                                      vp, vp, C.c_size_t, vp]
         L.moe_decode_step.restype = C.c_int
+        L.moe_decode_step_residual.argtypes = [C.POINTER(LayerStruct), vp, i32, vp, vp, C.POINTER(PlanStruct),
+                                               vp, vp, vp, C.c_size_t, vp]
+        L.moe_decode_step_residual.restype = C.c_int
         L.moe_decode_layer.argtypes = [C.POINTER(LayerStruct), vp, vp, i32, vp, vp, C.POINTER(PlanStruct),
                                        vp, vp, vp, C.c_size_t, vp]
         L.moe_decode_layer.restype = C.c_int
@@ -383,7 +387,8 @@ def alloc_workspace(layer: DeviceLayer, max_tokens: int, device="cuda") -> torch
 def decode_step(layer: DeviceLayer, x: torch.Tensor, idx: torch.Tensor, w: torch.Tensor, plan: Plan,
                 out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
                 residual: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """moe_decode_step: x [B,H] (bf16 or fp32 per the layer) -> out [B,H]."""
+    """moe_decode_step: x [B,H] (bf16 or fp32 per the layer) -> out [B,H];
+    with a residual, moe_decode_step_residual (out = residual + the block)."""
     B = _check_x(layer, x)
     _check_routing(layer, B, idx, w)
     _check_plan(layer, plan, B)
@@ -393,9 +398,14 @@ def decode_step(layer: DeviceLayer, x: torch.Tensor, idx: torch.Tensor, w: torch
     if workspace is None:
         workspace = alloc_workspace(layer, B, device=x.device)
     _check_workspace(layer, B, workspace)
-    _check(lib().moe_decode_step(C.byref(layer.struct), _ptr(x), B, _ptr(idx), _ptr(w), C.byref(plan.struct),
-                                 _ptr(residual), _ptr(out), _ptr(workspace), workspace.numel(),
-                                 _stream(stream)), "moe_decode_step")
+    if residual is None:
+        _check(lib().moe_decode_step(C.byref(layer.struct), _ptr(x), B, _ptr(idx), _ptr(w), C.byref(plan.struct),
+                                     _ptr(out), _ptr(workspace), workspace.numel(), _stream(stream)),
+               "moe_decode_step")
+    else:
+        _check(lib().moe_decode_step_residual(C.byref(layer.struct), _ptr(x), B, _ptr(idx), _ptr(w),
+                                              C.byref(plan.struct), _ptr(residual), _ptr(out), _ptr(workspace),
+                                              workspace.numel(), _stream(stream)), "moe_decode_step_residual")
     return out
 
 

@@ -52,6 +52,30 @@ bool pick_down_cols(int dff, int *nw, int *cpw) {
     return *cpw <= 7 && C % *nw == 0;
 }
 
+// Which kernels a projection takes: 4 bits in groups of 64 the specialised
+// ones, any other width or group size the generic row kernels.
+bool fast_gate_up(const moe_layer_t *L) { return L->bits == 4 && L->group_size == 64; }
+bool fast_down(const moe_layer_t *L) { return down_bits_of(L) == 4 && L->group_size == 64; }
+
+// Lanes per row and units per lane of the generic row kernels for rows of K
+// inputs: the most lanes (a power of two up to a wave's 64) dividing K/16
+// units with at most kGenMaxUpl units per lane, UPL one of the instantiated
+// counts.
+bool pick_generic(int K, int *lpr, int *upl) {
+    if (K <= 0 || K % 16) return false;
+    const int units = K / 16;
+    for (int l = 64; l >= 1; l >>= 1) {
+        if (units % l) continue;
+        const int u = units / l;
+        if (u > kGenMaxUpl) return false;
+        if (u == 5 || u == 7) return false;
+        *lpr = l;
+        *upl = u;
+        return true;
+    }
+    return false;
+}
+
 static bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 
 moe_status check_layer(const moe_layer_t *L) {
@@ -61,7 +85,7 @@ moe_status check_layer(const moe_layer_t *L) {
     if (L->n_experts > MOE_MAX_EXPERTS) return MOE_ERR_UNSUPPORTED;
     if (L->top_k > L->n_experts) return MOE_ERR_INVALID_ARG;
     if (L->top_k > MOE_MAX_TOP_K) return MOE_ERR_UNSUPPORTED;
-    for (int b : {L->bits, L->down_bits})
+    for (int b : {L->bits, down_bits_of(L)})
         if (b != 4 && b != 6 && b != 8) return MOE_ERR_UNSUPPORTED;
     if (L->group_size != 32 && L->group_size != 64 && L->group_size != 128) return MOE_ERR_UNSUPPORTED;
     if (L->hidden % 64 || L->dff % 64) return MOE_ERR_UNSUPPORTED;
@@ -180,6 +204,6 @@ const char *moe_status_str(moe_status s) {
     return "unknown status";
 }
 
-int32_t moe_abi_version(void) { return 7; }
+int32_t moe_abi_version(void) { return 8; }
 
 }  // extern "C"

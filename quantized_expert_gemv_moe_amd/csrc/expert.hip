@@ -1336,10 +1336,10 @@ extern "C" moe_status moe_expert_down_combine(const moe_layer_t *layer, int32_t 
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_DEVICE;
 }
 
-extern "C" moe_status moe_decode_step(const moe_layer_t *layer, const void *x, int32_t n_tokens,
-                                      const int32_t *topk_idx, const float *topk_w,
-                                      const moe_plan_t *plan, const void *residual, void *out,
-                                      void *workspace, size_t workspace_bytes, void *hip_stream) {
+extern "C" moe_status moe_decode_step_residual(const moe_layer_t *layer, const void *x, int32_t n_tokens,
+                                               const int32_t *topk_idx, const float *topk_w,
+                                               const moe_plan_t *plan, const void *residual, void *out,
+                                               void *workspace, size_t workspace_bytes, void *hip_stream) {
     moe_status st = check_step(layer, n_tokens, plan, workspace, workspace_bytes);
     if (st != MOE_OK || n_tokens == 0) return st;
     if ((st = check_x(x)) != MOE_OK) return st;
@@ -1350,6 +1350,13 @@ extern "C" moe_status moe_decode_step(const moe_layer_t *layer, const void *x, i
     st = enqueue_down_combine(layer, n_tokens, topk_idx, topk_w, plan, residual, out, workspace, stream);
     if (st != MOE_OK) return st;
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_DEVICE;
+}
+
+extern "C" moe_status moe_decode_step(const moe_layer_t *layer, const void *x, int32_t n_tokens,
+                                      const int32_t *topk_idx, const float *topk_w, const moe_plan_t *plan,
+                                      void *out, void *workspace, size_t workspace_bytes, void *hip_stream) {
+    return moe_decode_step_residual(layer, x, n_tokens, topk_idx, topk_w, plan, nullptr, out, workspace,
+                                    workspace_bytes, hip_stream);
 }
 
 extern "C" moe_status moe_decode_layer(const moe_layer_t *layer, const float *logits, const void *x,

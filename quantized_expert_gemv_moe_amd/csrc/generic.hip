@@ -33,7 +33,6 @@ namespace moe {
 
 constexpr int kGenBlock = 256;  // four independent waves
 constexpr int kGenStage = 8;    // slots per pass over a lane's units (half for gate+up)
-constexpr int kGenMaxUpl = 8;   // units per lane
 
 struct GenericArgs {
     const uint32_t *q0, *q1;  // gate and up, or down (q1 unused)
@@ -201,27 +200,6 @@ __global__ __launch_bounds__(kGenBlock) void generic_rows_kernel(GenericArgs a) 
 
 // ------------------------------------------------------------- host side
 
-bool fast_gate_up(const moe_layer_t *L) { return L->bits == 4 && L->group_size == 64; }
-bool fast_down(const moe_layer_t *L) { return L->down_bits == 4 && L->group_size == 64; }
-
-// Lanes per row and units per lane for rows of K inputs: the most lanes (a
-// power of two up to 64) dividing K/16 units with at most kGenMaxUpl units
-// per lane, UPL one of the instantiated counts.
-bool pick_generic(int K, int *lpr, int *upl) {
-    if (K <= 0 || K % 16) return false;
-    const int units = K / 16;
-    for (int l = kWave; l >= 1; l >>= 1) {
-        if (units % l) continue;
-        const int u = units / l;
-        if (u > kGenMaxUpl) return false;
-        if (u == 5 || u == 7) return false;
-        *lpr = l;
-        *upl = u;
-        return true;
-    }
-    return false;
-}
-
 static int group_shift_of(int group) { return group == 32 ? 1 : group == 64 ? 2 : 3; }
 
 template <int BITS, bool GU, bool XBF16>
@@ -273,7 +251,7 @@ moe_status launch_generic_down(const moe_layer_t *L, int n_tokens, const moe_pla
                         0.f, MOE_ACT_SWIGLU, h, PlanView{(const int4 *)plan->work, plan->sorted_slots},
                         y, L->hidden, L->dff, L->n_experts, n_tokens * L->top_k, L->top_k, lpr,
                         group_shift_of(L->group_size)};
-    return launch_generic<false, false>(a, L->down_bits, upl, generic_groups_y(L, n_tokens), s);
+    return launch_generic<false, false>(a, down_bits_of(L), upl, generic_groups_y(L, n_tokens), s);
 }
 
 }  // namespace moe

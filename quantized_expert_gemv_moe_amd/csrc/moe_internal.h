@@ -29,8 +29,11 @@ bool pick_down_cols(int dff, int *nw, int *cpw);
 // width or group size takes the generic row kernels (rows layout only for
 // down).  pick_generic gives their lanes per row and 16-input units per lane
 // for rows of K inputs.
+constexpr int kGenMaxUpl = 8;  // 16-input units per lane of the generic row kernels
 bool fast_gate_up(const moe_layer_t *layer);
 bool fast_down(const moe_layer_t *layer);
+// Width of the down projection: down_bits, or bits when down_bits is 0.
+inline int down_bits_of(const moe_layer_t *layer) { return layer->down_bits ? layer->down_bits : layer->bits; }
 bool pick_generic(int K, int *lpr, int *upl);
 moe_status launch_generic_gate_up(const moe_layer_t *layer, const void *x, int n_tokens,
                                   const moe_plan_t *plan, float *h, hipStream_t stream);

@@ -32,7 +32,7 @@ def test_library_exports_every_declared_function():
     assert set(declared) == set(_lib.EXPORTS)
     for name in declared:
         assert hasattr(L, name), name
-    assert L.moe_abi_version() == 7
+    assert L.moe_abi_version() == 8
 
 
 def test_status_strings():
@@ -79,10 +79,85 @@ def test_layer_check_accepts_the_workload_shapes():
     assert check(dff=8192, down_bits=8) == moe.MOE_OK
 
 
+def test_zero_extensions_mean_the_plain_layer():
+    # down_bits 0 takes gate/up's width: an 8-bit layer then has an 8-bit
+    # (generic, rows-only) down projection, which refuses the column layout
+    assert check(down_bits=0) == moe.MOE_OK
+    assert check(bits=8, down_bits=0) == moe.MOE_OK
+    assert check(bits=8, down_bits=0, down_layout=moe.MOE_DOWN_COLS) == moe.MOE_ERR_UNSUPPORTED
+    assert check(bits=4, down_bits=0, down_layout=moe.MOE_DOWN_COLS) == moe.MOE_OK
+    assert check(bits=3, down_bits=0) == moe.MOE_ERR_UNSUPPORTED
+
+
+PLAIN_STRUCT = r"""
+#include <stddef.h>
+#include <stdio.h>
+#include "moe_decode.h"
+/* the plain 4-bit layer, field for field, as a caller that knows no
+   extension declares it */
+typedef struct {
+    int32_t hidden, dff, n_experts, top_k, bits, group_size;
+    moe_dtype act_dtype;
+    float clamp_limit;
+    const uint32_t *gate_q, *up_q;
+    const uint16_t *gate_s, *gate_b, *up_s, *up_b;
+    const uint32_t *down_q;
+    const uint16_t *down_s, *down_b;
+    const float *expert_scale;
+} plain_layer;
+typedef struct { int32_t *counts, *offsets, *sorted_slots, *unique_experts, *n_unique; } plain_plan;
+#define F(S, P, f) printf("%s %s %zu %zu\n", #S, #f, offsetof(S, f), offsetof(P, f));
+#define G(S, f) printf("%s %s %zu -\n", #S, #f, offsetof(S, f));
+int main(void) {
+    F(moe_layer_t, plain_layer, hidden) F(moe_layer_t, plain_layer, dff) F(moe_layer_t, plain_layer, n_experts)
+    F(moe_layer_t, plain_layer, top_k) F(moe_layer_t, plain_layer, bits) F(moe_layer_t, plain_layer, group_size)
+    F(moe_layer_t, plain_layer, act_dtype) F(moe_layer_t, plain_layer, clamp_limit)
+    F(moe_layer_t, plain_layer, gate_q) F(moe_layer_t, plain_layer, up_q) F(moe_layer_t, plain_layer, gate_s)
+    F(moe_layer_t, plain_layer, gate_b) F(moe_layer_t, plain_layer, up_s) F(moe_layer_t, plain_layer, up_b)
+    F(moe_layer_t, plain_layer, down_q) F(moe_layer_t, plain_layer, down_s) F(moe_layer_t, plain_layer, down_b)
+    F(moe_layer_t, plain_layer, expert_scale)
+    G(moe_layer_t, down_layout) G(moe_layer_t, down_scale) G(moe_layer_t, activation) G(moe_layer_t, down_bits)
+    F(moe_plan_t, plain_plan, counts) F(moe_plan_t, plain_plan, offsets) F(moe_plan_t, plain_plan, sorted_slots)
+    F(moe_plan_t, plain_plan, unique_experts) F(moe_plan_t, plain_plan, n_unique) G(moe_plan_t, work)
+    printf("sizeof %zu %zu %zu\n", sizeof(moe_layer_t), sizeof(plain_layer), sizeof(moe_plan_t));
+    return 0;
+}
+"""
+
+
+def test_struct_layout_matches_the_header_and_keeps_the_plain_prefix(tmp_path):
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    src = tmp_path / "layout.c"
+    src.write_text(PLAIN_STRUCT)
+    exe = tmp_path / "layout"
+    inc = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
+    subprocess.run([cc, "-std=c11", "-Wall", "-Werror", "-I", inc, str(src), "-o", str(exe)], check=True)
+    lines = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split("\n")
+    py = {"moe_layer_t": _lib.LayerStruct, "moe_plan_t": _lib.PlanStruct}
+    seen = 0
+    for ln in lines:
+        parts = ln.split()
+        if not parts:
+            continue
+        if parts[0] == "sizeof":
+            assert int(parts[1]) == C.sizeof(_lib.LayerStruct) and int(parts[3]) == C.sizeof(_lib.PlanStruct)
+            assert int(parts[2]) < int(parts[1])
+            continue
+        struct, field, off, plain = parts
+        assert getattr(py[struct], field).offset == int(off), (struct, field)
+        if plain != "-":
+            assert int(plain) == int(off), (struct, field)  # a plain caller's struct is a prefix
+        seen += 1
+    assert seen == len(_lib.LayerStruct._fields_) + len(_lib.PlanStruct._fields_)
+
+
 @pytest.mark.parametrize("kw,want", [
     (dict(bits=2), moe.MOE_ERR_UNSUPPORTED),
     (dict(bits=5), moe.MOE_ERR_UNSUPPORTED),
-    (dict(down_bits=0), moe.MOE_ERR_UNSUPPORTED),
     (dict(down_bits=3), moe.MOE_ERR_UNSUPPORTED),
     (dict(group_size=16), moe.MOE_ERR_UNSUPPORTED),
     (dict(group_size=48), moe.MOE_ERR_UNSUPPORTED),
@@ -168,12 +243,23 @@ def test_decode_step_validation_before_any_launch():
     st = layer()
     p = _lib.PlanStruct(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
     ws_need = L.moe_workspace_size(C.byref(st), 4)
-    f = L.moe_decode_step
+    f = L.moe_decode_step_residual
     X, O, W = FAKE + 0x1000000, FAKE + 0x2000000, FAKE + 0x3000000
 
     def call(lay=st, x=X, n=4, plan=p, res=None, out=O, ws=W, wsb=ws_need):
         return f(C.byref(lay), x, n, FAKE, FAKE, C.byref(plan) if plan is not None else None,
                  res, out, ws, wsb, None)
+
+    def plain(lay=st, x=X, n=4, plan=p, out=O, ws=W, wsb=ws_need):
+        return L.moe_decode_step(C.byref(lay), x, n, FAKE, FAKE, C.byref(plan) if plan is not None else None,
+                                 out, ws, wsb, None)
+
+    # the plain call takes out where the residual variant takes the residual
+    assert plain(n=0) == moe.MOE_OK
+    assert plain(out=X) == moe.MOE_ERR_INVALID_ARG
+    assert plain(out=None) == moe.MOE_ERR_INVALID_ARG
+    assert plain(wsb=ws_need - 1) == moe.MOE_ERR_WORKSPACE
+    assert plain(lay=layer(bits=2)) == moe.MOE_ERR_UNSUPPORTED
 
     assert call(n=0) == moe.MOE_OK  # empty batch: nothing launched
     assert call(lay=layer(bits=2)) == moe.MOE_ERR_UNSUPPORTED

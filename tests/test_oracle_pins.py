@@ -493,6 +493,24 @@ def test_geglu_h_is_the_normal_cdf_gelu_within_the_tanh_form_error():
     assert np.abs(h[0] - exact).max() > 0  # the tanh form, not the exact one
 
 
+def test_geglu_tanh_form_matches_an_independent_implementation():
+    # PyTorch's own tanh-form GELU (fp64, CPU) pins both constants of the
+    # form to rounding level: a wrong cubic coefficient or sqrt(2/pi) moves
+    # h far more than 1e-12 of its largest value at |g| up to ~6.  (Deep in
+    # the negative tail 1 + tanh cancels, and the two tanh implementations
+    # leave different residues of order 1e-16 there.)
+    import torch
+    sh, L = _geglu_layer()
+    x = make_x(sh, 1, seed=44) * np.float32(40.0)
+    idx = np.array([[2]], np.int32)
+    _, h = oracle.decode_step(L, x, idx, np.ones((1, 1)), want_h=True)
+    g = bf.dequant_dense(L.gate_q[2], L.gate_s[2], L.gate_b[2]) @ x[0].astype(np.float64)
+    u = bf.dequant_dense(L.up_q[2], L.up_s[2], L.up_b[2]) @ x[0].astype(np.float64)
+    assert np.abs(g).max() > 3.0
+    ref = torch.nn.functional.gelu(torch.from_numpy(g), approximate="tanh").numpy() * u
+    assert np.allclose(h[0], ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
+
+
 def test_geglu_and_swiglu_differ_only_in_the_gate_function():
     sh_g, Lg = _geglu_layer()
     _, Ls = _geglu_layer(activation="swiglu")
