@@ -253,12 +253,13 @@ size_t moe_workspace_size(const moe_layer_t *layer, int32_t max_tokens);
  * Notes.  Repeated calls are bitwise equal.  Batch invariance: below 16
  * tokens a token's result depends only on that token (bitwise the same
  * whatever else is in the batch).  From 16 tokens up, an expert that holds
- * 3 or more of the batch's tokens runs on the MFMA kernels, which add the
- * same exact fp32 products in another order; a token routed to such an
- * expert may then differ from its single-token result by fp32 rounding
- * only (relative L2 within 5e-4 of each other, both within the output
- * tolerance of the fp64 definition).  Tokens whose experts all hold fewer
- * than 3 tokens stay bitwise equal.
+ * 3 or more of the batch's tokens runs on the MFMA kernels, and from 128
+ * tokens up every expert runs on the MFMA tile kernels; they add the same
+ * exact fp32 products in another order, so a token routed to such an
+ * expert may differ from its single-token result by fp32 rounding only
+ * (relative L2 within 5e-4 of each other, both within the output
+ * tolerance of the fp64 definition).  Between 16 and 127 tokens, tokens
+ * whose experts all hold fewer than 3 tokens stay bitwise equal.
  */
 moe_status moe_decode_step(const moe_layer_t *layer, const void *x, int32_t n_tokens,
                            const int32_t *topk_idx, const float *topk_w, const moe_plan_t *plan,
@@ -266,9 +267,10 @@ moe_status moe_decode_step(const moe_layer_t *layer, const void *x, int32_t n_to
 
 /*
  * moe_decode_step with the residual add of a layer stack fused into the
- * combine's store: out_t = act(residual_t + o_t), the sum formed in fp32
- * from the unrounded o_t and rounded once to act_dtype (the layer stack
- * runs every MoE layer on every decode tick, page "perf(moe):
+ * combine's store: out_t = act(residual_t + act(o_t)), i.e. the block's
+ * output rounded to act_dtype as moe_decode_step stores it, added to the
+ * residual in fp32 and rounded again (the layer stack runs every MoE
+ * layer on every decode tick, page "perf(moe):
  * attribute the MoE decode gap at the M = 1 expert gather", Problem /
  * Background).  residual is [n_tokens][hidden] act_dtype or NULL (then
  * exactly moe_decode_step); out must not alias x or residual.

@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB_NAME = "libmoe_decode.so"
 LIB_PATH = os.path.join(BUILD_DIR, LIB_NAME)
-SOURCES = ["abi.cpp", "route.hip", "expert.hip", "gate_up_route.hip", "generic.hip", "pack.hip", "router_proj.hip"]
+SOURCES = ["abi.cpp", "route.hip", "expert.hip", "gate_up_route.hip", "generic.hip", "pack.hip", "router_proj.hip", "tile.hip"]
 ARCH = "gfx950"
 
 

@@ -34,6 +34,7 @@
 #include "device_util.h"
 #include "expert_device.h"
 #include "gate_up_device.h"
+#include "mfma_device.h"
 #include "moe_internal.h"
 #include "route_device.h"
 
@@ -57,64 +58,11 @@ void gate_up_kernel(GateUpArgs a) {
 // MFMA.  Output lane l holds token l % 16 and rows 4 * (l / 16) .. + 3.  The
 // waves' partial sums meet in LDS and are added in wave order; tokens go in
 // tiles of 16.
-typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
-typedef __attribute__((ext_vector_type(4))) float f32x4_t;
-
-__device__ __forceinline__ f32x4_t mfma16x16x32(const uint32_t *a, const uint32_t *b, f32x4_t c) {
-    typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
-    const u32x4_t av = {a[0], a[1], a[2], a[3]};
-    const u32x4_t bv = {b[0], b[1], b[2], b[3]};
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av),
-                                                   __builtin_bit_cast(bf16x8_t, bv), c, 0, 0, 0);
-}
-
-// Nibbles of one word as the four bf16 pairs (128 + q_p, 128 + q_{p+4}).
-__device__ __forceinline__ void q4_pairs(uint32_t w, uint32_t *o) {
-    const uint32_t M = 0x000F000Fu, B = 0x43004300u;
-    o[0] = (w & M) | B;
-    o[1] = ((w >> 4) & M) | B;
-    o[2] = ((w >> 8) & M) | B;
-    o[3] = ((w >> 12) & M) | B;
-}
-
-// The same nibble pairs as bf16 values 1 + q / 16 (q in mantissa bits 3..6
-// of 1.0).  For the MFMA kernels: the offset that the group bias has to take
-// back out is then 16 times the nibble unit instead of 128 times, so the
-// cancellation between the two terms of the epilogue loses about eight
-// times fewer bits of the fp32 accumulation.
-__device__ __forceinline__ void q4_pairs16(uint32_t w, uint32_t *o) {
-    uint32_t M, B;  // opaque, for v_and_or_b32 (see dot8_q4_bf16)
-    asm("s_mov_b32 %0, 0x780078" : "=s"(M));
-    asm("v_mov_b32 %0, 0x3f803f80" : "=v"(B));
-    o[0] = ((w << 3) & M) | B;
-    o[1] = ((w >> 1) & M) | B;
-    o[2] = ((w >> 5) & M) | B;
-    o[3] = ((w >> 9) & M) | B;
-}
-
-// Eight bf16 activations (one 16-byte word) as the pairs (x_p, x_{p+4}),
-// and their sum added into *acc.
-__device__ __forceinline__ void x8_pairs(uint4 w, uint32_t *o, float *acc) {
-    const uint32_t ones = 0x3F803F80u;
-    o[0] = (w.x & 0xFFFFu) | (w.z << 16);
-    o[1] = (w.x >> 16) | (w.z & 0xFFFF0000u);
-    o[2] = (w.y & 0xFFFFu) | (w.w << 16);
-    o[3] = (w.y >> 16) | (w.w & 0xFFFF0000u);
-    *acc = dot2_bf16(w.x, ones, dot2_bf16(w.y, ones, dot2_bf16(w.z, ones, dot2_bf16(w.w, ones, *acc))));
-}
-
 constexpr int kMfmaTokens = 16;  // token tile
 
 // 16-row tiles per MFMA gate+up workgroup: one from eight waves up (the
 // workgroup's registers then leave room for two workgroups per CU), two below.
 constexpr int mfma_row_tiles(int nw) { return nw >= 8 ? 1 : 2; }
-
-// Streaming 8-byte load (two words of one row).
-__device__ __forceinline__ uint2 load_stream2(const uint2 *p) {
-    typedef uint32_t v2u __attribute__((ext_vector_type(2)));
-    const v2u v = __builtin_nontemporal_load((const v2u *)p);
-    return make_uint2(v.x, v.y);
-}
 
 // NW waves, GW 64-groups per wave (NW * GW = hidden / 64), RT 16-row tiles.
 // Every weight load of a wave is issued before its first MFMA, and every
@@ -546,22 +494,6 @@ __global__ __launch_bounds__(NW * kWave) void down_cols_kernel(const uint4 *__re
 // tile (256 contiguous bytes per chunk and tile across the wave) and the h
 // of token r in the same nibble pairing as gate+up's MFMA kernel.  Partial
 // sums meet in LDS and are added in wave order; tokens go in tiles of 16.
-__device__ __forceinline__ void split3_pairs(const float *v, uint32_t (*o)[4]) {
-    // v[0..7] -> o[part][p] = (bf16 part of v[p], bf16 part of v[p + 4])
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        const float a = v[p], b = v[p + 4];
-        const uint32_t a1 = __float_as_uint(a) & 0xFFFF0000u, b1 = __float_as_uint(b) & 0xFFFF0000u;
-        const float ar = a - __uint_as_float(a1), br = b - __uint_as_float(b1);
-        const uint32_t a2 = __float_as_uint(ar) & 0xFFFF0000u, b2 = __float_as_uint(br) & 0xFFFF0000u;
-        const float ar2 = ar - __uint_as_float(a2), br2 = br - __uint_as_float(b2);
-        const uint32_t a3 = __float_as_uint(ar2) & 0xFFFF0000u, b3 = __float_as_uint(br2) & 0xFFFF0000u;
-        o[0][p] = (a1 >> 16) | b1;
-        o[1][p] = (a2 >> 16) | b2;
-        o[2][p] = (a3 >> 16) | b3;
-    }
-}
-
 template <int NW, int GW, int RT>
 __global__ __launch_bounds__(NW * kWave) void down_mfma_kernel(const uint32_t *__restrict__ q,
                                                                const uint16_t *__restrict__ sc,
@@ -1187,6 +1119,8 @@ moe_status enqueue_gate_up(const moe_layer_t *layer, const void *x, int n_tokens
     const Workspace ws = workspace_layout(layer, n_tokens);
     float *h = (float *)((char *)workspace + ws.h_off);
     if (!fast_gate_up(layer)) return launch_generic_gate_up(layer, x, n_tokens, plan, h, stream);
+    if (n_tokens >= kTileMinTokens && tile_gate_up_ok(layer))
+        return launch_gate_up_tile(layer, x, n_tokens, plan, h, stream);
     Geometry gu;
     pick_geometry_gate_up(layer->hidden, &gu);
     int nw = 0, gw = 0;
@@ -1283,6 +1217,8 @@ static moe_status enqueue_down_combine(const moe_layer_t *layer, int n_tokens, c
     }
     if (!fast) {
         st = launch_generic_down(layer, n_tokens, plan, h, y, stream);
+    } else if (n_tokens >= kTileMinTokens && tile_down_ok(layer)) {
+        st = launch_down_tile(layer, n_tokens, plan, h, y, stream);
     } else if (layer->down_layout == MOE_DOWN_COLS) {
         int nw = 0, gw = 0;
         const bool mfma = n_tokens >= kMfmaMinTokens && mfma_down_shape(layer, &nw, &gw);

@@ -51,6 +51,18 @@ moe_status check_x(const void *x);
 moe_status check_out(const void *x, const int32_t *topk_idx, const float *topk_w, const void *residual,
                      const void *out);
 
+// Tile kernels (tile.hip) for batches of kTileMinTokens tokens or more:
+// every distinct expert's tokens in blocks of 64 on MFMA, the workgroup's
+// waves splitting the output rows.  The *_ok checks say whether a layer
+// has them; the launchers take checked arguments.
+constexpr int kTileMinTokens = 128;
+bool tile_gate_up_ok(const moe_layer_t *layer);
+bool tile_down_ok(const moe_layer_t *layer);
+moe_status launch_gate_up_tile(const moe_layer_t *layer, const void *x, int n_tokens, const moe_plan_t *plan,
+                               float *h, hipStream_t stream);
+moe_status launch_down_tile(const moe_layer_t *layer, int n_tokens, const moe_plan_t *plan, const float *h,
+                            float *y, hipStream_t stream);
+
 // Enqueues the deduplicated gate+up kernels of a planned batch (h into the
 // workspace); the layer and arguments are already checked.
 moe_status enqueue_gate_up(const moe_layer_t *layer, const void *x, int n_tokens, const moe_plan_t *plan,

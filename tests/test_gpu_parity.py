@@ -500,6 +500,41 @@ def test_prefill_sized_batch_on_sampled_tokens(B, layout):
     assert np.isfinite(oracle.bf16_to_f64(run.out)).all()
 
 
+@pytest.mark.parametrize("H,F,E,k,B,regime,layout,act", [
+    (256, 256, 8, 2, 128, "normal", "cols", "swiglu"),    # ~32 tokens per expert: one block of two tiles
+    (256, 192, 8, 2, 300, "zipf", "rows", "swiglu"),      # skewed counts over several blocks; a ragged gate row block
+    (192, 256, 8, 2, 300, "zipf", "cols", "swiglu"),      # a ragged down row block (hidden 192); gate+up on its own kernels
+    (512, 256, 16, 4, 200, "normal", "rows", "swiglu"),   # rows-layout down keeps its own kernels
+    (256, 256, 256, 8, 160, "normal", "cols", "swiglu"),  # 256 plan records (four per lane); ~5 tokens each
+    (256, 256, 4, 1, 129, "same", "cols", "swiglu"),      # one expert holds all 129 tokens: blocks of 64, 64, 1
+    (4096, 256, 4, 2, 128, "normal", "cols", "swiglu"),   # 64 groups of hidden: 128 KB of scales in LDS
+    (1024, 512, 8, 2, 140, "normal", "cols", "geglu"),    # GeGLU, both sidecars and the clamp
+    (256, 128, 8, 2, 130, "normal", "cols", "swiglu"),    # dff 128: no whole load ring, the earlier kernels
+])
+def test_tile_kernels_match_oracle(H, F, E, k, B, regime, layout, act):
+    """Batches of 128 tokens or more run the tile kernels: every distinct
+    expert's tokens in blocks of 64 on MFMA (gate+up always, down with the
+    column layout).  Whole outputs against the oracle; three tokens alone
+    against the batch (a different kernel, the same exact products)."""
+    geglu = act == "geglu"
+    sh = Shape(f"t{H}x{F}", 40, H, F, E, k, "bf16", sidecar=geglu, clamp=10.0 if geglu else 0.0,
+               activation=act, down_sidecar=geglu)
+    log(f"[case] tile {H}x{F}x{E}x{k} B={B} {regime} {layout} {act}")
+    lg = make_logits(sh, B, regime=regime, seed=H + B)
+    L = make_layer(sh, seed=H + B)
+    x = make_x(sh, B, seed=H + B, scale=4.0 if geglu else 1.0)
+    dl = moe.DeviceLayer.from_host(L)
+    if layout == "cols":
+        dl = dl.pack_down()
+    run = GpuRun(L, x, lg, dl=dl)
+    check_against_oracle(L, x, lg, run, f"tile {H}x{F}x{E}x{k} B{B} {regime} {layout} {act}")
+    counts = run.plan_np["counts"]
+    log(f"[tile] counts min {counts[counts > 0].min()} max {counts.max()}")
+    for t in (0, B // 2, B - 1):
+        one = GpuRun(L, x[t:t + 1], lg[t:t + 1], dl=dl)
+        assert rel_l2(oracle.bf16_to_f64(one.out[0]), oracle.bf16_to_f64(run.out[t])) <= 5e-4
+
+
 # --------------------------------------------------------------- invariants
 @pytest.mark.parametrize("layout", ["rows", "cols"])
 def test_determinism_batch_invariance_permutation_and_duplicates(layout):
