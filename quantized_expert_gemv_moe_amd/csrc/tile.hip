@@ -208,9 +208,7 @@ __global__ __launch_bounds__(kTileThreads) void gate_up_tile_kernel(GateUpArgs a
             uint32_t o[4];
             float sum = 0.f;
             x8_pairs(v[u], o, &sum);
-            sum += __shfl_xor(sum, 1, kWave);
-            sum += __shfl_xor(sum, 2, kWave);
-            sum += __shfl_xor(sum, 4, kWave);
+            sum = seg_sum<8>(sum);  // DPP within the token's eight lanes
             *(uint4 *)(b + (((xp & 1) * 64 + xt) * 4 + (xp >> 1)) * 16) = make_uint4(o[0], o[1], o[2], o[3]);
             if (xp == 0) *(float *)(b + 2 * 64 * 64 + 4 * xt) = sum;
         }
@@ -237,9 +235,49 @@ __global__ __launch_bounds__(kTileThreads) void gate_up_tile_kernel(GateUpArgs a
     // one pass: the next pass's loads go out first (past the last pass they
     // repeat it), then the four groups, each staging the next group's
     // activations into the other LDS buffer before its MFMAs
+    // The MFMAs of one group for NT token tiles: every LDS read first, then
+    // the MFMA chains (one copy per tile count, no branch between them).
+    auto tiles = [&](auto ntiles, const unsigned char *xg, const uint32_t (&b)[RT][2][2][4],
+                     const float (&s16)[RT][2], const float (&bp)[RT][2]) __attribute__((always_inline)) {
+        constexpr int NT = decltype(ntiles)::value;
+        uint4 A0[NT], A1[NT];
+        float4 S4[NT];
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt) {
+            const int tok = 16 * tt + r16;
+            A0[tt] = *(const uint4 *)(xg + ((0 * 64 + tok) * 4 + kq) * 16);
+            A1[tt] = *(const uint4 *)(xg + ((1 * 64 + tok) * 4 + kq) * 16);
+            // the group sums of the D rows' tokens 16 tt + 4 kq .. + 3
+            S4[tt] = *(const float4 *)(xg + 2 * 64 * 64 + 4 * (16 * tt + 4 * kq));
+        }
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt) {
+            const uint32_t xa[2][4] = {{A0[tt].x, A0[tt].y, A0[tt].z, A0[tt].w}, {A1[tt].x, A1[tt].y, A1[tt].z, A1[tt].w}};
+            const float xs[4] = {S4[tt].x, S4[tt].y, S4[tt].z, S4[tt].w};
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                for (int m = 0; m < 2; ++m) {
+                    f32x4_t d = mfma16x16x32(xa[0], b[rt][m][0], f32x4_t{0.f, 0.f, 0.f, 0.f});
+                    d = mfma16x16x32(xa[1], b[rt][m][1], d);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        acc[rt][tt][m][i] = fmaf(bp[rt][m], xs[i], fmaf(s16[rt][m], d[i], acc[rt][tt][m][i]));
+                }
+        }
+    };
     auto pass = [&](auto set, int k) __attribute__((always_inline)) {
         constexpr int S = decltype(set)::value;
         load_pass(Slot<1 - S>{}, k + 1 < K ? k + 1 : K - 1);
+        // the pass's scales and biases, all four groups' at once
+        uint32_t sbp[4][RT][2];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                for (int m = 0; m < 2; ++m)
+                    sbp[j][rt][m] = sbl[(m * G + 4 * k + j) * ROWS + (row_w - row_b) + 16 * rt + r16];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int g = 4 * k + j;
@@ -252,34 +290,20 @@ __global__ __launch_bounds__(kTileThreads) void gate_up_tile_kernel(GateUpArgs a
                 for (int m = 0; m < 2; ++m) {
                     q4_pairs16(wq[S][rt][m][j].x, b[rt][m][0]);
                     q4_pairs16(wq[S][rt][m][j].y, b[rt][m][1]);
-                    const uint32_t sb = sbl[(m * G + g) * ROWS + (row_w - row_b) + 16 * rt + r16];
+                    const uint32_t sb = sbp[j][rt][m];
                     const float sv = f16_bits_to_f32((uint16_t)(sb & 0xFFFFu));
                     s16[rt][m] = 16.f * sv;
                     bp[rt][m] = fmaf(-16.f, sv, f16_bits_to_f32((uint16_t)(sb >> 16)));
                 }
             const unsigned char *xg = xl + (size_t)(g & 1) * kXStageBytes;
-#pragma unroll
-            for (int tt = 0; tt < TT; ++tt) {
-                if (tt < ntt) {
-                    const int tok = 16 * tt + r16;
-                    const uint4 v0 = *(const uint4 *)(xg + ((0 * 64 + tok) * 4 + kq) * 16);
-                    const uint4 v1 = *(const uint4 *)(xg + ((1 * 64 + tok) * 4 + kq) * 16);
-                    const uint32_t xa[2][4] = {{v0.x, v0.y, v0.z, v0.w}, {v1.x, v1.y, v1.z, v1.w}};
-                    // the group sums of the D rows' tokens 16 tt + 4 kq .. + 3
-                    const float4 s4 = *(const float4 *)(xg + 2 * 64 * 64 + 4 * (16 * tt + 4 * kq));
-                    const float xs[4] = {s4.x, s4.y, s4.z, s4.w};
-#pragma unroll
-                    for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-                        for (int m = 0; m < 2; ++m) {
-                            f32x4_t d = mfma16x16x32(xa[0], b[rt][m][0], f32x4_t{0.f, 0.f, 0.f, 0.f});
-                            d = mfma16x16x32(xa[1], b[rt][m][1], d);
-#pragma unroll
-                            for (int i = 0; i < 4; ++i)
-                                acc[rt][tt][m][i] = fmaf(bp[rt][m], xs[i], fmaf(s16[rt][m], d[i], acc[rt][tt][m][i]));
-                        }
-                }
-            }
+            // tiles past the live tokens hold the first token's activations;
+            // their rows of D are never stored
+            if (ntt >= 3)
+                tiles(Slot<4>{}, xg, b, s16, bp);
+            else if (ntt == 2)
+                tiles(Slot<2>{}, xg, b, s16, bp);
+            else
+                tiles(Slot<1>{}, xg, b, s16, bp);
             __syncthreads();
         }
     };
@@ -393,9 +417,7 @@ __global__ __launch_bounds__(kTileThreads) void down_tile_kernel(const uint32_t 
             uint32_t o[3][4];
             split3_pairs(v, o);
             float sum = ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
-            sum += __shfl_xor(sum, 1, kWave);
-            sum += __shfl_xor(sum, 2, kWave);
-            sum += __shfl_xor(sum, 4, kWave);
+            sum = seg_sum<8>(sum);  // DPP within the token's eight lanes
 #pragma unroll
             for (int p = 0; p < 3; ++p)
                 *(uint4 *)(b + ((((hp >> 2) * 3 + p) * 64 + ht) * 4 + (hp & 3)) * 16) =
@@ -422,56 +444,65 @@ __global__ __launch_bounds__(kTileThreads) void down_tile_kernel(const uint32_t 
 #pragma unroll
         for (int tt = 0; tt < TT; ++tt) acc[rt][tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    auto step = [&](auto slot, int g) __attribute__((always_inline)) {
-        constexpr int s = decltype(slot)::value;
-        {
-            stage_h((g + 1) & 1, hr[(s + 1) % NR]);
-            uint32_t b[RT][2][4];
-            float s16[RT], bp[RT];
+    // The MFMAs of one group for NT token tiles: every LDS read first, then
+    // the MFMA chains (one copy per tile count, no branch between them).
+    auto tiles = [&](auto ntiles, const unsigned char *hg, const uint32_t (&b)[RT][2][4], const float (&s16)[RT],
+                     const float (&bp)[RT]) __attribute__((always_inline)) {
+        constexpr int NT = decltype(ntiles)::value;
+        uint4 A[NT][2][3];
+        float4 S4[NT];
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt) {
+            const int tok = 16 * tt + r16;
+#pragma unroll
+            for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+                for (int p = 0; p < 3; ++p) A[tt][c2][p] = *(const uint4 *)(hg + (((c2 * 3 + p) * 64 + tok) * 4 + kq) * 16);
+            S4[tt] = *(const float4 *)(hg + 2 * 3 * 64 * 64 + 4 * (16 * tt + 4 * kq));
+        }
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt) {
+            const float hs[4] = {S4[tt].x, S4[tt].y, S4[tt].z, S4[tt].w};
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt) {
-                q4_pairs16(wr[s][rt][0], b[rt][0]);
-                q4_pairs16(wr[s][rt][1], b[rt][1]);
-                const uint32_t sb = sbl[g * ROWS + (row_w - row_b) + 16 * rt + r16];
-                const float sv = f16_bits_to_f32((uint16_t)(sb & 0xFFFFu));
-                s16[rt] = 16.f * sv;
-                bp[rt] = fmaf(-16.f, sv, f16_bits_to_f32((uint16_t)(sb >> 16)));
-            }
-            load(slot, g + NR < G ? g + NR : G - 1);
-            const unsigned char *hg = hl + (size_t)(g & 1) * kHStageBytes;
+                f32x4_t d = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int tt = 0; tt < TT; ++tt) {
-                if (tt < ntt) {
-                    const int tok = 16 * tt + r16;
-                    uint32_t ha[2][3][4];
+                for (int c2 = 0; c2 < 2; ++c2)
 #pragma unroll
-                    for (int c2 = 0; c2 < 2; ++c2)
-#pragma unroll
-                        for (int p = 0; p < 3; ++p) {
-                            const uint4 v = *(const uint4 *)(hg + (((c2 * 3 + p) * 64 + tok) * 4 + kq) * 16);
-                            ha[c2][p][0] = v.x;
-                            ha[c2][p][1] = v.y;
-                            ha[c2][p][2] = v.z;
-                            ha[c2][p][3] = v.w;
-                        }
-                    const float4 s4 = *(const float4 *)(hg + 2 * 3 * 64 * 64 + 4 * (16 * tt + 4 * kq));
-                    const float hs[4] = {s4.x, s4.y, s4.z, s4.w};
-#pragma unroll
-                    for (int rt = 0; rt < RT; ++rt) {
-                        f32x4_t d = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                        for (int c2 = 0; c2 < 2; ++c2) {
-                            d = mfma16x16x32(ha[c2][0], b[rt][c2], d);
-                            d = mfma16x16x32(ha[c2][1], b[rt][c2], d);
-                            d = mfma16x16x32(ha[c2][2], b[rt][c2], d);
-                        }
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) acc[rt][tt][i] = fmaf(bp[rt], hs[i], fmaf(s16[rt], d[i], acc[rt][tt][i]));
+                    for (int p = 0; p < 3; ++p) {
+                        const uint32_t ha[4] = {A[tt][c2][p].x, A[tt][c2][p].y, A[tt][c2][p].z, A[tt][c2][p].w};
+                        d = mfma16x16x32(ha, b[rt][c2], d);
                     }
-                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[rt][tt][i] = fmaf(bp[rt], hs[i], fmaf(s16[rt], d[i], acc[rt][tt][i]));
             }
-            __syncthreads();
         }
+    };
+    auto step = [&](auto slot, int g) __attribute__((always_inline)) {
+        constexpr int s = decltype(slot)::value;
+        stage_h((g + 1) & 1, hr[(s + 1) % NR]);
+        uint32_t b[RT][2][4];
+        float s16[RT], bp[RT];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            q4_pairs16(wr[s][rt][0], b[rt][0]);
+            q4_pairs16(wr[s][rt][1], b[rt][1]);
+            const uint32_t sb = sbl[g * ROWS + (row_w - row_b) + 16 * rt + r16];
+            const float sv = f16_bits_to_f32((uint16_t)(sb & 0xFFFFu));
+            s16[rt] = 16.f * sv;
+            bp[rt] = fmaf(-16.f, sv, f16_bits_to_f32((uint16_t)(sb >> 16)));
+        }
+        load(slot, g + NR < G ? g + NR : G - 1);
+        const unsigned char *hg = hl + (size_t)(g & 1) * kHStageBytes;
+        // tiles past the live tokens hold the first token's h; their rows
+        // of D are never stored
+        if (ntt >= 3)
+            tiles(Slot<4>{}, hg, b, s16, bp);
+        else if (ntt == 2)
+            tiles(Slot<2>{}, hg, b, s16, bp);
+        else
+            tiles(Slot<1>{}, hg, b, s16, bp);
+        __syncthreads();
     };
     for (int g4 = 0; g4 < G; g4 += NR) {
         step(Slot<0>{}, g4);
