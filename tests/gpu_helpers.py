@@ -75,7 +75,7 @@ def as_f64(a: np.ndarray) -> np.ndarray:
     return a.astype(np.float64)
 
 
-class GpuRun:
+class DeviceRun:
     """One layer step on the GPU through the C ABI, results as numpy."""
 
     def __init__(self, layer_np, x: np.ndarray, logits: np.ndarray, residual: np.ndarray = None,
@@ -116,7 +116,7 @@ def layer_for(shape, logits, layer=0, seed=0, std=0.02):
     return make_layer(shape, layer=layer, experts=np.unique(idx), seed=seed, std=std)
 
 
-def check_against_oracle(L, x, logits, run: GpuRun, tag: str, diag=True):
+def check_against_oracle(L, x, logits, run: DeviceRun, tag: str, diag=True):
     sh = L.shape
     idx, w = oracle.route_topk(logits, sh.top_k)
     assert np.array_equal(run.idx, idx), f"{tag}: router indices differ"

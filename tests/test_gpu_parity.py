@@ -11,7 +11,7 @@ import pytest
 import torch
 
 import quantized_expert_gemv_moe_amd as moe
-from gpu_helpers import (REL_L2_DIAG, REL_L2_GATE, GpuRun, check_against_oracle, dev_x, host_bits, layer_for,
+from gpu_helpers import (REL_L2_DIAG, REL_L2_GATE, DeviceRun, check_against_oracle, dev_x, host_bits, layer_for,
                          log, record, rel_l2)
 from moe_workloads import SHAPES, Shape, make_layer, make_logits, make_router, make_x
 from oracle import oracle
@@ -164,7 +164,7 @@ def test_decode_step_matches_oracle(name, B, regime, xs, layout):
     lg = make_logits(sh, B, regime=regime, seed=3)
     L = layer_for(sh, lg, seed=3) if sh.n_experts > 8 else make_layer(sh, seed=3)
     x = make_x(sh, B, seed=3, scale=xs)
-    run = GpuRun(L, x, lg, cols=layout == "cols")
+    run = DeviceRun(L, x, lg, cols=layout == "cols")
     check_against_oracle(L, x, lg, run, f"{name}/B{B}/{regime}/x{xs}/{layout}")
     if xs > 1.0:
         h64 = oracle.decode_step(L, x, *oracle.route_topk(lg, sh.top_k), want_h=True)[1]
@@ -186,7 +186,7 @@ def test_decode_step_other_shapes(H, F, E, k, act):
     lg = make_logits(sh, B, seed=H + F)
     L = make_layer(sh, seed=H + F)
     x = make_x(sh, B, seed=H + F)
-    run = GpuRun(L, x, lg)
+    run = DeviceRun(L, x, lg)
     check_against_oracle(L, x, lg, run, f"{H}x{F}x{E}x{k}/{act}")
 
 
@@ -218,7 +218,7 @@ def test_decode_step_column_layout_geometries(H, F, E, k):
     lg = make_logits(sh, B, seed=H * F)
     L = make_layer(sh, seed=H * F)
     x = make_x(sh, B, seed=H * F)
-    run = GpuRun(L, x, lg, cols=True)
+    run = DeviceRun(L, x, lg, cols=True)
     check_against_oracle(L, x, lg, run, f"cols {H}x{F}x{E}x{k}")
 
 
@@ -238,7 +238,7 @@ def test_column_down_in_stages(H, F, E, k, B, regime):
     lg = make_logits(sh, B, regime=regime, seed=F + B)
     L = layer_for(sh, lg, seed=F + B) if E > 8 else make_layer(sh, seed=F + B)
     x = make_x(sh, B, seed=F + B)
-    run = GpuRun(L, x, lg, cols=True)
+    run = DeviceRun(L, x, lg, cols=True)
     check_against_oracle(L, x, lg, run, f"cols stages {H}x{F}x{E}x{k} B{B} {regime}")
 
 
@@ -262,7 +262,7 @@ def test_gate_up_mfma_path(H, F, E, k, B, layout):
     x = make_x(sh, B, seed=H + B)
     if layout == "cols" and F in (192, 64):
         pytest.skip(f"dff {F} has no column-layout down kernel")
-    run = GpuRun(L, x, lg, cols=layout == "cols")
+    run = DeviceRun(L, x, lg, cols=layout == "cols")
     check_against_oracle(L, x, lg, run, f"mfma {H}x{F}x{E}x{k} B{B} {layout}")
     assert run.plan_np["counts"].max() >= 3
 
@@ -285,7 +285,7 @@ def test_down_mfma_path(H, F, E, k, B, act):
     L = make_layer(sh, seed=F + B)
     x = make_x(sh, B, seed=F + B)
     log(f"[case] down mfma {H}x{F}x{E}x{k} B={B} {act}")
-    run = GpuRun(L, x, lg, cols=True)
+    run = DeviceRun(L, x, lg, cols=True)
     check_against_oracle(L, x, lg, run, f"down mfma {H}x{F}x{E}x{k} B{B} {act}")
     assert run.plan_np["counts"].max() >= 3
 
@@ -363,7 +363,7 @@ def test_geglu_with_down_sidecar_matches_oracle(name, B, regime, layout):
     L = layer_for(sh, lg, seed=11)
     assert L.activation == "geglu" and L.down_sidecar is not None
     x = make_x(sh, B, seed=11)
-    run = GpuRun(L, x, lg, cols=layout == "cols")
+    run = DeviceRun(L, x, lg, cols=layout == "cols")
     check_against_oracle(L, x, lg, run, f"geglu {name}/B{B}/{regime}/{layout}")
 
 
@@ -378,14 +378,14 @@ def test_power_of_two_down_sidecar_scales_the_output_exactly(B):
     lg = make_logits(sh, B, regime="sharing", seed=B)
     L = layer_for(sh, lg, seed=B)
     x = make_x(sh, B, seed=B)
-    base = GpuRun(L, x, lg, cols=True)
+    base = DeviceRun(L, x, lg, cols=True)
     L.down_sidecar = np.full(sh.n_experts, 2.0, np.float32)
-    two = GpuRun(L, x, lg, cols=True)
+    two = DeviceRun(L, x, lg, cols=True)
     assert np.array_equal(two.out, base.out * 2)
     assert np.array_equal(two.h, base.h)
     check_against_oracle(L, x, lg, two, f"down sidecar x2 B{B}")
     L.down_sidecar = np.where(np.arange(sh.n_experts) % 2, 4.0, 2.0).astype(np.float32)
-    check_against_oracle(L, x, lg, GpuRun(L, x, lg, cols=True), f"down sidecar 2/4 B{B}")
+    check_against_oracle(L, x, lg, DeviceRun(L, x, lg, cols=True), f"down sidecar 2/4 B{B}")
 
 
 # ------------------------------------------- other widths and group sizes
@@ -405,7 +405,7 @@ def test_other_widths_match_oracle(bits, down_bits, group, name, B, regime):
     lg = make_logits(sh, B, regime=regime, seed=bits * 10 + down_bits)
     L = layer_for(sh, lg, seed=group) if sh.n_experts > 8 else make_layer(sh, seed=group)
     x = make_x(sh, B, seed=group)
-    run = GpuRun(L, x, lg)
+    run = DeviceRun(L, x, lg)
     check_against_oracle(L, x, lg, run, f"w{bits}/{down_bits}g{group} {name} B{B} {regime}")
 
 
@@ -420,7 +420,7 @@ def test_other_widths_on_the_wide_layer_with_geglu_and_sidecars(bits, down_bits,
     lg = make_logits(sh, 2, seed=7)
     L = layer_for(sh, lg, seed=7)
     x = make_x(sh, 2, seed=7, scale=4.0)  # some gate values beyond the clamp
-    run = GpuRun(L, x, lg)
+    run = DeviceRun(L, x, lg)
     check_against_oracle(L, x, lg, run, f"wide w{bits}/{down_bits}g{group}")
 
 
@@ -439,7 +439,7 @@ def test_mixed_width_layers_take_each_projections_kernels(bits, down_bits, layou
     lg = make_logits(sh, B, regime="sharing", seed=bits + B)
     L = layer_for(sh, lg, seed=bits + B)
     x = make_x(sh, B, seed=bits + B)
-    run = GpuRun(L, x, lg, cols=layout == "cols")
+    run = DeviceRun(L, x, lg, cols=layout == "cols")
     check_against_oracle(L, x, lg, run, f"mixed {bits}/{down_bits} {layout} B{B}")
 
 
@@ -453,9 +453,9 @@ def test_other_widths_batch_invariance_and_entry_points():
     L = layer_for(sh, lg, seed=4)
     x = make_x(sh, B, seed=4)
     dl = moe.DeviceLayer.from_host(L)
-    a = GpuRun(L, x, lg, dl=dl)
+    a = DeviceRun(L, x, lg, dl=dl)
     for t in range(B):
-        one = GpuRun(L, x[t:t + 1], lg[t:t + 1], dl=dl)
+        one = DeviceRun(L, x[t:t + 1], lg[t:t + 1], dl=dl)
         assert np.array_equal(one.out[0], a.out[t]), f"token {t}"
     lgt = torch.from_numpy(lg).cuda()
     idx2, w2, plan2 = moe.route_plan(lgt, sh.top_k)
@@ -478,7 +478,7 @@ def test_prefill_sized_batch_on_sampled_tokens(B, layout):
     lg = make_logits(sh, B, regime="normal", seed=B + 5)
     L = layer_for(sh, lg, seed=B + 5)
     x = make_x(sh, B, seed=B + 5)
-    run = GpuRun(L, x, lg, cols=layout == "cols")
+    run = DeviceRun(L, x, lg, cols=layout == "cols")
     idx, w = oracle.route_topk(lg, sh.top_k)
     assert np.array_equal(run.idx, idx)
     assert float(np.abs(run.w - w).max()) <= 1e-6
@@ -526,12 +526,12 @@ def test_tile_kernels_match_oracle(H, F, E, k, B, regime, layout, act):
     dl = moe.DeviceLayer.from_host(L)
     if layout == "cols":
         dl = dl.pack_down()
-    run = GpuRun(L, x, lg, dl=dl)
+    run = DeviceRun(L, x, lg, dl=dl)
     check_against_oracle(L, x, lg, run, f"tile {H}x{F}x{E}x{k} B{B} {regime} {layout} {act}")
     counts = run.plan_np["counts"]
     log(f"[tile] counts min {counts[counts > 0].min()} max {counts.max()}")
     for t in (0, B // 2, B - 1):
-        one = GpuRun(L, x[t:t + 1], lg[t:t + 1], dl=dl)
+        one = DeviceRun(L, x[t:t + 1], lg[t:t + 1], dl=dl)
         assert rel_l2(oracle.bf16_to_f64(one.out[0]), oracle.bf16_to_f64(run.out[t])) <= 5e-4
 
 
@@ -547,8 +547,8 @@ def test_determinism_batch_invariance_permutation_and_duplicates(layout):
     dl = moe.DeviceLayer.from_host(L)
     if layout == "cols":
         dl = dl.pack_down()
-    a = GpuRun(L, x, lg, dl=dl)
-    b = GpuRun(L, x, lg, dl=dl)
+    a = DeviceRun(L, x, lg, dl=dl)
+    b = DeviceRun(L, x, lg, dl=dl)
     assert np.array_equal(a.out, b.out), "run-to-run results differ"
     # A token's result is bitwise the same alone and in the batch when its
     # experts take the same kernel variant.  Batches under 16 tokens run the
@@ -556,12 +556,12 @@ def test_determinism_batch_invariance_permutation_and_duplicates(layout):
     # experts hold three tokens: in a batch of 16 they would go to MFMA).
     assert a.plan_np["counts"].max() >= 3
     for t in range(B):
-        one = GpuRun(L, x[t:t + 1], lg[t:t + 1], dl=dl)
+        one = DeviceRun(L, x[t:t + 1], lg[t:t + 1], dl=dl)
         assert np.array_equal(one.out[0], a.out[t]), f"token {t} alone differs from the batch"
     perm = np.array([5, 2, 7, 0, 1, 6, 3, 4])
-    p = GpuRun(L, x[perm], lg[perm], dl=dl)
+    p = DeviceRun(L, x[perm], lg[perm], dl=dl)
     assert np.array_equal(p.out, a.out[perm])
-    d = GpuRun(L, np.repeat(x[2:3], 4, axis=0), dup_lg, dl=dl)
+    d = DeviceRun(L, np.repeat(x[2:3], 4, axis=0), dup_lg, dl=dl)
     assert d.plan_np["n_unique"] == sh.top_k
     assert np.all(d.out == d.out[0:1])
     assert np.array_equal(d.out[0], a.out[2])
@@ -580,12 +580,12 @@ def test_batch_invariance_across_the_mfma_switch(layout):
     dl = moe.DeviceLayer.from_host(L)
     if layout == "cols":
         dl = dl.pack_down()
-    a = GpuRun(L, x, lg, dl=dl)
+    a = DeviceRun(L, x, lg, dl=dl)
     check_against_oracle(L, x, lg, a, f"cohort B16 sharing {layout}")
     counts = a.plan_np["counts"]
     n_mfma = 0
     for t in range(B):
-        one = GpuRun(L, x[t:t + 1], lg[t:t + 1], dl=dl)
+        one = DeviceRun(L, x[t:t + 1], lg[t:t + 1], dl=dl)
         if counts[a.idx[t]].max() < 3:
             assert np.array_equal(one.out[0], a.out[t]), f"token {t} alone differs from the batch"
         else:
@@ -835,5 +835,5 @@ def test_layer_routed_from_the_projection(name, B):
     torch.cuda.synchronize()
     lg_np = lg.cpu().numpy()
     L = layer_for(sh, lg_np, seed=40)
-    run = GpuRun(L, x, lg_np, cols=True)
+    run = DeviceRun(L, x, lg_np, cols=True)
     check_against_oracle(L, x, lg_np, run, f"projected {name} B{B}")

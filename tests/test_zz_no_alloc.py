@@ -8,7 +8,7 @@ import pytest
 import torch
 
 import quantized_expert_gemv_moe_amd as moe
-from gpu_helpers import GpuRun, check_against_oracle, dev_x, host_bits, layer_for, log
+from gpu_helpers import DeviceRun, check_against_oracle, dev_x, host_bits, layer_for, log
 from moe_workloads import SHAPES, make_logits, make_x
 
 pytestmark = pytest.mark.gpu
@@ -25,7 +25,7 @@ def test_static_scratch_entry_point_matches_decode_layer():
         L = layer_for(sh, lg, seed=seed)
         x = make_x(sh, B, seed=seed)
         dl = moe.DeviceLayer.from_host(L).pack_down()
-        ref = GpuRun(L, x, lg, dl=dl)  # moe_decode_layer with its workspace
+        ref = DeviceRun(L, x, lg, dl=dl)  # moe_decode_layer with its workspace
         check_against_oracle(L, x, lg, ref, f"static reference B{B}")
         xt, lgt = dev_x(x), torch.from_numpy(lg).cuda()
         plan = moe.Plan.allocate(E, B * k)
