@@ -107,6 +107,7 @@ __device__ __forceinline__ void gate_up_mfma_block(const GateUpArgs &a, int rb, 
     __builtin_amdgcn_sched_barrier(0);
 
     // this wave's weights: words 2kq and 2kq+1 of each group, per row tile
+    // (ordinary loads: the streaming hint measured ~1.5 % slower at 32 tokens)
     uint2 wgq[GW][RT], wuq[GW][RT];
     {
         const uint2 *gq = (const uint2 *)a.gate_q, *uq = (const uint2 *)a.up_q;
@@ -116,8 +117,8 @@ __device__ __forceinline__ void gate_up_mfma_block(const GateUpArgs &a, int rb, 
             const size_t rb = ((size_t)wk.e * F + (row < F ? row : F - 1)) * (H / 16) + g0 * 4 + kq;
 #pragma unroll
             for (int gi = 0; gi < GW; ++gi) {
-                wgq[gi][t] = load_stream2(gq + rb + gi * 4);
-                wuq[gi][t] = load_stream2(uq + rb + gi * 4);
+                wgq[gi][t] = gq[rb + gi * 4];
+                wuq[gi][t] = uq[rb + gi * 4];
             }
         }
     }
@@ -543,6 +544,7 @@ __global__ __launch_bounds__(NW * kWave) void down_mfma_kernel(const uint32_t *_
     __builtin_amdgcn_sched_barrier(0);
 
     // this wave's weights: word kq of chunks 2g, 2g + 1 of each row tile
+    // (ordinary loads, as in the MFMA gate+up kernel)
     uint32_t wa[GW][RT][2];
 #pragma unroll
     for (int gi = 0; gi < GW; ++gi)
@@ -551,7 +553,7 @@ __global__ __launch_bounds__(NW * kWave) void down_mfma_kernel(const uint32_t *_
 #pragma unroll
             for (int c2 = 0; c2 < 2; ++c2) {
                 const int c = 2 * (g0 + gi) + c2;
-                wa[gi][t][c2] = __builtin_nontemporal_load(q + (((size_t)wk.e * C + c) * H + m0 + 16 * t + r16) * 4 + kq);
+                wa[gi][t][c2] = q[(((size_t)wk.e * C + c) * H + m0 + 16 * t + r16) * 4 + kq];
             }
     __builtin_amdgcn_sched_barrier(0);
     slot = r16 < wk.count ? slot : 0;

@@ -76,11 +76,4 @@ __device__ __forceinline__ void split3_pairs(const float *v, uint32_t (*o)[4]) {
     }
 }
 
-// Streaming 8-byte load (two words of one row).
-__device__ __forceinline__ uint2 load_stream2(const uint2 *p) {
-    typedef uint32_t v2u __attribute__((ext_vector_type(2)));
-    const v2u v = __builtin_nontemporal_load((const v2u *)p);
-    return make_uint2(v.x, v.y);
-}
-
 }  // namespace moe

@@ -9,7 +9,9 @@
 //
 // Work is cut into tile items: (distinct expert u, block of up to 64 of
 // its tokens), items in the plan's order of distinct experts, ceil(count /
-// 64) of them per expert.  A workgroup takes one item and one block of
+// 64) of them per expert.  The items of one expert read its weights again,
+// so the weights go through the caches with ordinary loads here (the
+// streaming hint of the few-token kernels measured ~9 % slower).  A workgroup takes one item and one block of
 // output rows; its eight waves split the rows, 16 * RT each, and each wave
 // holds all 64 tokens (four 16-token tiles) of the item in its
 // accumulators while it walks the whole input dimension, 64-group by
@@ -189,8 +191,8 @@ __global__ __launch_bounds__(kTileThreads) void gate_up_tile_kernel(GateUpArgs a
         for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                wq[S][rt][0][j] = load_stream2(gq + woff[rt] + 4 * (4 * k + j));
-                wq[S][rt][1][j] = load_stream2(uq + woff[rt] + 4 * (4 * k + j));
+                wq[S][rt][0][j] = gq[woff[rt] + 4 * (4 * k + j)];
+                wq[S][rt][1][j] = uq[woff[rt] + 4 * (4 * k + j)];
             }
 #pragma unroll
         for (int j = 0; j < 4; ++j)
@@ -398,7 +400,7 @@ __global__ __launch_bounds__(kTileThreads) void down_tile_kernel(const uint32_t 
         for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
             for (int c2 = 0; c2 < 2; ++c2)
-                wr[s][rt][c2] = __builtin_nontemporal_load(q + wbase[rt] + (size_t)(2 * g + c2) * H * 4);
+                wr[s][rt][c2] = q[wbase[rt] + (size_t)(2 * g + c2) * H * 4];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             hr[s][u][0] = hsrc[u][16 * g];
