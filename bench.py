@@ -539,6 +539,25 @@ def counted_traffic(workload: str, kernel: str):
     return rec["kernels"][kernel]["traffic_bytes"]
 
 
+TRACE_RECORD = os.path.join(ROOT, "profiles", "decode_b1_kernel_trace.md")
+
+
+def traced_kernel_us(workload: str, kernel: str):
+    """Average duration of `kernel` in the committed rocprofv3 kernel trace
+    of this workload (the tracer's own clock, which stretches each
+    dispatch), or None."""
+    if workload != "decode" or not os.path.exists(TRACE_RECORD):
+        return None
+    for line in open(TRACE_RECORD):
+        cells = [c.strip() for c in line.strip().strip("|").split("|")]
+        if len(cells) >= 3 and cells[0] == f"`{kernel}`":
+            try:
+                return float(cells[2])
+            except ValueError:
+                return None
+    return None
+
+
 def copy_calibration():
     import torch
 
@@ -615,6 +634,7 @@ def main():
                  if B == 1 and sh.hidden == 2048 and sh.n_experts == 128
                  else "gate_up_route_kernel" if B <= 8 else "route_plan_kernel + gate_up kernels")
     traffic = counted_traffic(args.workload, gu_kernel)
+    traced_us = traced_kernel_us(args.workload, gu_kernel)
 
     cal = calibration()
     log(f"[bench] calibration: streaming read {cal['stream_read_gbps']:.0f} GB/s, copy {cal['copy_gbps']:.0f} GB/s, "
@@ -720,7 +740,12 @@ def main():
         "passes_us_per_step": {"values": passes, **spread(passes)},
         "roofline": {"bound": "hbm", "kernel": gu_kernel, "achieved": ach, "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": ach / HBM_PEAK_GBPS, "traffic": traffic,
-                     "bytes_per_launch": gu_bytes, "us_per_launch": kt["route_gate_up"] * 1e6},
+                     "bytes_per_launch": gu_bytes, "us_per_launch": kt["route_gate_up"] * 1e6,
+                     # the same kernel's average under the kernel tracer (committed
+                     # profile of this workload): its clock includes the tracer's own
+                     # per-dispatch cost and excludes the gap between graph nodes
+                     "us_per_launch_traced": traced_us,
+                     "frac_traced": (gu_bytes / traced_us / 1e3 / HBM_PEAK_GBPS) if traced_us else None},
         "kernels": kernels,
         "calibration": cal,
         "ladder": ladder,
