@@ -653,9 +653,40 @@ __device__ __forceinline__ void store_out(float o, const void *residual, void *o
     }
 }
 
+// The residual as fp32 (a bf16 value widens exactly), and the output from o
+// and that value: the same arithmetic as store_out, with the residual read
+// ahead by the caller.
+template <bool BF16>
+__device__ __forceinline__ float load_residual(const void *residual, size_t i) {
+    if constexpr (BF16)
+        return bf16_bits_to_f32(((const uint16_t *)residual)[i]);
+    else
+        return ((const float *)residual)[i];
+}
+
+template <bool BF16>
+__device__ __forceinline__ void store_out_res(float o, bool has_res, float rv, void *out, size_t i) {
+    if constexpr (BF16) {
+        uint16_t r = f32_to_bf16_rne(o);
+        if (has_res) r = f32_to_bf16_rne(rv + bf16_bits_to_f32(r));
+        ((uint16_t *)out)[i] = r;
+    } else {
+        if (has_res) o = rv + o;
+        ((float *)out)[i] = o;
+    }
+}
+
 // out[t][m] = sum_j w[t][j] * (y[t * k + j][m] * dscale[e]): fp32 FMAs in j
 // order, the down-projection sidecar (if any) applied to y as it enters
-// the sum; a token with an invalid expert id gets NaN.
+// the sum; a token with an invalid expert id gets NaN.  The loads of up to
+// kCombineBatch slots go out together (ids, weights, y, then the sidecar
+// entries the ids name) before any of them is used, and the residual's
+// ahead of them all: one memory round trip per batch instead of one per
+// slot.  Loads past top_k repeat its last slot and are not used; with no
+// sidecar or residual the same loads read valid memory that is not used,
+// so no load sits under a branch.
+constexpr int kCombineBatch = 8;
+
 template <bool BF16>
 __global__ __launch_bounds__(kBlock) void combine_kernel(const float *__restrict__ y,
                                                          const int *__restrict__ topk_idx,
@@ -663,22 +694,44 @@ __global__ __launch_bounds__(kBlock) void combine_kernel(const float *__restrict
                                                          const float *__restrict__ dscale,
                                                          const void *residual, void *out,
                                                          int hidden, int top_k, int n_experts) {
+    constexpr int U = kCombineBatch;
     const int t = blockIdx.y;
     const int m = blockIdx.x * kBlock + threadIdx.x;
     if (m >= hidden) return;
+    const size_t oi = (size_t)t * hidden + m;
+    const bool has_res = residual != nullptr;
+    const float rv = load_residual<BF16>(has_res ? residual : (const void *)y, has_res ? oi : (size_t)m);
+    const float *dsrc = dscale ? dscale : topk_w;
     float acc = 0.f;
     bool bad = false;
-    for (int j = 0; j < top_k; ++j) {
-        const int s = t * top_k + j;
-        const int e = topk_idx[s];
-        const bool invalid = (unsigned)e >= (unsigned)n_experts;
-        bad |= invalid;
-        float v = y[(size_t)s * hidden + m];
-        if (dscale && !invalid) v *= dscale[e];
-        acc = fmaf(topk_w[s], v, acc);
+    for (int j0 = 0; j0 < top_k; j0 += U) {
+        int e[U];
+        float w[U], v[U], ds[U];
+#pragma unroll
+        for (int i = 0; i < U; ++i) {
+            const int s = t * top_k + (j0 + i < top_k ? j0 + i : top_k - 1);
+            e[i] = topk_idx[s];
+            w[i] = topk_w[s];
+            v[i] = y[(size_t)s * hidden + m];
+        }
+#pragma unroll
+        for (int i = 0; i < U; ++i) {
+            const bool ok = (unsigned)e[i] < (unsigned)n_experts;
+            ds[i] = dsrc[dscale && ok ? e[i] : 0];
+        }
+        // every product formed, the sum taking the live ones (x * 1 is x)
+#pragma unroll
+        for (int i = 0; i < U; ++i) {
+            const bool invalid = (unsigned)e[i] >= (unsigned)n_experts;
+            const bool live = j0 + i < top_k;
+            const float x = v[i] * (dscale && !invalid ? ds[i] : 1.f);
+            const float a = fmaf(w[i], x, acc);
+            acc = live ? a : acc;
+            bad |= live && invalid;
+        }
     }
     if (bad) acc = __builtin_nanf("");
-    store_out<BF16>(acc, residual, out, (size_t)t * hidden + m);
+    store_out_res<BF16>(acc, has_res, rv, out, oi);
 }
 
 // ------------------------------------ down + combine, token by token
@@ -788,6 +841,13 @@ __global__ __launch_bounds__(NW * kWave) void down_token_kernel(const uint4 *__r
     // generic-pointer load would wait for every load in flight)
     const float ds_ld = dscale ? dscale[e] : topk_w[0];
     const float dsj = (dscale && live) ? ds_ld : 1.f;
+    // the residual of the output this lane stores (row block `wave`, if it
+    // has one), read now rather than after the combine; without a
+    // residual (or a row block) a valid word is read and not used
+    const bool has_res = residual != nullptr;
+    const int rb_res = wave < RB ? wave : 0;
+    const float rv = load_residual<BF16>(has_res ? residual : (const void *)topk_w,
+                                         has_res ? (size_t)t * H + mb + rb_res * RW + (lane < RW ? r : 0) : 0);
     __builtin_amdgcn_sched_barrier(0);
 
     // stage h and its group sums while the weights are in flight; a pair
@@ -879,7 +939,13 @@ __global__ __launch_bounds__(NW * kWave) void down_token_kernel(const uint4 *__r
             o = fmaf(wk, part[b * kWave + jk * RW + r], o);
         }
         if (bad) o = __builtin_nanf("");
-        if (lane < RW) store_out<BF16>(o, residual, out, (size_t)t * H + mb + b * RW + r);
+        if (lane < RW) {
+            const size_t oi = (size_t)t * H + mb + b * RW + r;
+            if (b == wave)
+                store_out_res<BF16>(o, has_res, rv, out, oi);
+            else
+                store_out<BF16>(o, residual, out, oi);
+        }
     }
 }
 

@@ -9,10 +9,12 @@
 // the tile's tokens from registers.  With bf16 activations the products go
 // through v_dot2_f32_bf16 (exact products, fp32 accumulation); with fp32
 // activations the weights are widened and multiplied with exact fp32 FMAs.
-// The lanes of a row are summed by a butterfly, so the sum order is fixed.
+// The lanes of a row are summed by a fixed tree of cross-lane VALU moves, so
+// the sum order is fixed.
 #include <hip/hip_runtime.h>
 
 #include "device_util.h"
+#include "gate_up_device.h"
 #include "moe_internal.h"
 
 namespace moe {
@@ -35,6 +37,22 @@ __device__ __forceinline__ float rp_dot8_f32(uint4 w, const float4 &x0, const fl
     acc = fmaf(__uint_as_float(w.w << 16), x1.z, acc);
     acc = fmaf(__uint_as_float(w.w & 0xFFFF0000u), x1.w, acc);
     return acc;
+}
+
+// Sum over aligned segments of LPR lanes, every lane of a segment with the
+// same total: DPP quad swaps and mirrors inside 16-lane rows, then
+// v_permlane16_swap and v_permlane32_swap across rows, all VALU (a shuffle
+// through the LDS crossbar per step had made the sums the longest chain of
+// a wave).
+template <int LPR>
+__device__ __forceinline__ float rp_seg_sum(float v) {
+    if constexpr (LPR >= 2) v += dpp<kDppQuad1032>(v);
+    if constexpr (LPR >= 4) v += dpp<kDppQuad2301>(v);
+    if constexpr (LPR >= 8) v += dpp<kDppHalfMirror>(v);
+    if constexpr (LPR >= 16) v += dpp<kDppMirror>(v);
+    if constexpr (LPR >= 32) v = swap16_sum(v, v);
+    if constexpr (LPR >= 64) v = swap32_sum(v, v);
+    return v;
 }
 
 // Tokens per wave: a wave computes its rows for a tile of TT tokens, with
@@ -97,9 +115,7 @@ __global__ __launch_bounds__(kWave) void router_logits_kernel(const void *__rest
     }
 #pragma unroll
     for (int i = 0; i < TT; ++i) {
-        float a = acc[i];
-#pragma unroll
-        for (int off = 1; off < LPR; off <<= 1) a += __shfl_xor(a, off, kWave);
+        const float a = rp_seg_sum<LPR>(acc[i]);
         if (sl == 0 && row < n_experts && t0 + i < n_tokens) logits[(size_t)(t0 + i) * n_experts + row] = a;
     }
 }

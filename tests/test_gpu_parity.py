@@ -802,6 +802,11 @@ def test_empty_batch_decode_step_is_a_no_op():
     (384, 37, 5, "bf16"),      # 16 x 3; E not a multiple of the rows per wave
     (8, 5, 2, "f32"),          # one chunk per row
     (3072, 64, 2, "f32"),      # 64 x 6
+    (384, 37, 9, "bf16"),      # larger batches: a ragged last tile
+    (256, 8, 8, "f32"),        # 32-lane segments summed across two rows
+    (3072, 64, 8, "f32"),
+    (4096, 256, 16, "bf16"),   # 64 x 8: 2-token tiles
+    (2048, 100, 33, "bf16"),   # E not a multiple of 4; ragged tile
 ])
 def test_router_logits_match_oracle(H, E, B, act):
     sh = Shape(f"rp{H}x{E}", 39, H, 64, E, 1, act)
