@@ -756,8 +756,15 @@ __device__ __forceinline__ int xcd_block(int b, int n) {
     return (b % kXcds) * (n / kXcds) + b / kXcds;
 }
 
+// Sixteen-wave workgroups with one row block and four chunks per wave fit
+// 64 registers, so two workgroups share a CU (eight waves per SIMD); the
+// other shapes would spill there and keep the compiler's choice.
+template <int NW, int CPW, int RB>
+constexpr int down_token_waves_per_simd() { return NW >= 16 && RB == 1 && CPW == 4 ? 8 : 1; }
+
 template <int NW, int CPW, int KP, int RB, bool BF16>
-__global__ __launch_bounds__(NW * kWave) void down_token_kernel(const uint4 *__restrict__ q,
+__global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(down_token_waves_per_simd<NW, CPW, RB>())))
+void down_token_kernel(const uint4 *__restrict__ q,
                                                                 const uint16_t *__restrict__ sc,
                                                                 const uint16_t *__restrict__ bi,
                                                                 const float *__restrict__ h,
@@ -1080,12 +1087,17 @@ static moe_status launch_down_token_k(const moe_layer_t *L, int n_tokens, const 
 // Row blocks per workgroup of the token-major down kernel: one for a single
 // token (the most workgroups, the shortest path), more as tokens add
 // workgroups, so the staged h of a token serves more rows; bounded by the
-// LDS budget and by hidden.
-static int down_token_rb(const moe_layer_t *L, int n_tokens, int nw) {
+// LDS budget and by hidden.  Sixteen-wave workgroups (dff 1536, 2048) spill
+// at four row blocks; with four chunks per wave (dff 2048) they take two
+// row blocks for one token, where a workgroup stages as many bytes of h as
+// it reads of weights (wide layer, one token: 33.3 -> 29.5 us per step),
+// and one from two tokens, two workgroups per CU (four tokens: 120.2 ->
+// 117.3 us).
+static int down_token_rb(const moe_layer_t *L, int n_tokens, int nw, int cpw) {
     const int rw = kWave / pow2_at_least(L->top_k);
-    // sixteen-wave workgroups (dff 1536, 2048) spill at four row blocks
     const int rb_max = nw >= 16 ? 2 : 4;
     int rb0 = n_tokens >= kTokenRb4 ? 4 : n_tokens >= kTokenRb2 ? 2 : 1;
+    if (nw >= 16 && cpw == 4) rb0 = n_tokens == 1 ? 2 : 1;
     for (int rb = rb0 < rb_max ? rb0 : rb_max; rb > 1; rb /= 2)
         if (L->hidden % (rw * rb) == 0 && down_token_lds(L, nw, rb) <= down_token_lds_budget()) return rb;
     return 1;
@@ -1100,7 +1112,7 @@ static moe_status launch_down_token(const moe_layer_t *L, int n_tokens, const fl
     if (L->down_layout != MOE_DOWN_COLS || !pick_down_cols(L->dff, &nw, &cpw)) return MOE_ERR_UNSUPPORTED;
     if (L->hidden % (kWave / pow2_at_least(L->top_k))) return MOE_ERR_UNSUPPORTED;
     if (down_token_lds(L, nw, 1) > down_token_lds_budget()) return MOE_ERR_UNSUPPORTED;
-    const int rb = down_token_rb(L, n_tokens, nw);
+    const int rb = down_token_rb(L, n_tokens, nw, cpw);
     switch (nw * 100 + cpw) {
 #define MOE_DT(NW, CPW) \
     case NW * 100 + CPW: return launch_down_token_k<NW, CPW>(L, n_tokens, h, idx, w, residual, out, rb, s);
