@@ -168,14 +168,24 @@ def _check_routing(layer: "DeviceLayer", B: int, idx: torch.Tensor, w: torch.Ten
     _need(w, "w", torch.float32, (B, layer.top_k))
 
 
-def _check_plan(layer: "DeviceLayer", plan: "Plan", B: int):
-    E = layer.n_experts
+def _check_plan_buffers(plan: "Plan", n_experts: int, n_slots: int):
+    E = n_experts
     if (plan.counts.numel() < E or plan.offsets.numel() < E + 1 or plan.unique_experts.numel() < E
-            or plan.work.numel() < 4 * E or plan.sorted_slots.numel() < B * layer.top_k):
+            or plan.work.numel() < 4 * E or plan.sorted_slots.numel() < n_slots or plan.n_unique.numel() < 1):
         raise ValueError("plan buffers are too small for this layer and batch")
     for t in (plan.counts, plan.offsets, plan.sorted_slots, plan.unique_experts, plan.n_unique, plan.work):
         if t.dtype != torch.int32 or not t.is_contiguous() or not t.is_cuda:
             raise ValueError("plan buffers must be contiguous int32 device tensors")
+
+
+def _check_plan(layer: "DeviceLayer", plan: "Plan", B: int):
+    _check_plan_buffers(plan, layer.n_experts, B * layer.top_k)
+
+
+def _check_logits(logits: torch.Tensor):
+    if (logits is None or logits.dtype != torch.float32 or logits.dim() != 2 or not logits.is_contiguous()
+            or not logits.is_cuda):
+        raise ValueError("logits must be a contiguous fp32 [B, E] device tensor")
 
 
 def _check_out(layer: "DeviceLayer", B: int, out: torch.Tensor, residual: Optional[torch.Tensor]):
@@ -328,13 +338,14 @@ def router_logits(x: torch.Tensor, w_router: torch.Tensor, logits: Optional[torc
 def route_topk(logits: torch.Tensor, top_k: int, idx: Optional[torch.Tensor] = None,
                w: Optional[torch.Tensor] = None, stream=None):
     """moe_route_topk: fp32 logits [B,E] -> (int32 idx [B,k], fp32 w [B,k])."""
-    if logits.dtype != torch.float32 or logits.dim() != 2 or not logits.is_contiguous():
-        raise ValueError("logits must be a contiguous fp32 [B, E] tensor")
+    _check_logits(logits)
     B, E = logits.shape
     if idx is None:
         idx = torch.empty((B, top_k), dtype=torch.int32, device=logits.device)
     if w is None:
         w = torch.empty((B, top_k), dtype=torch.float32, device=logits.device)
+    _need(idx, "idx", torch.int32, (B, top_k))
+    _need(w, "w", torch.float32, (B, top_k))
     _check(lib().moe_route_topk(_ptr(logits), B, E, top_k, _ptr(idx), _ptr(w), _stream(stream)),
            "moe_route_topk")
     return idx, w
@@ -342,13 +353,12 @@ def route_topk(logits: torch.Tensor, top_k: int, idx: Optional[torch.Tensor] = N
 
 def expert_plan(idx: torch.Tensor, n_experts: int, plan: Optional[Plan] = None, stream=None) -> Plan:
     """moe_expert_plan over int32 idx [B,k]."""
-    if idx.dtype != torch.int32 or idx.dim() != 2 or not idx.is_contiguous():
-        raise ValueError("idx must be a contiguous int32 [B, k] tensor")
+    if idx.dtype != torch.int32 or idx.dim() != 2 or not idx.is_contiguous() or not idx.is_cuda:
+        raise ValueError("idx must be a contiguous int32 [B, k] device tensor")
     B, k = idx.shape
     if plan is None:
         plan = Plan.allocate(n_experts, B * k, device=idx.device)
-    if plan.sorted_slots.numel() < B * k or plan.counts.numel() < n_experts:
-        raise ValueError("plan buffers are too small")
+    _check_plan_buffers(plan, n_experts, B * k)
     _check(lib().moe_expert_plan(_ptr(idx), B, n_experts, k, C.byref(plan.struct), _stream(stream)),
            "moe_expert_plan")
     return plan
@@ -357,8 +367,7 @@ def expert_plan(idx: torch.Tensor, n_experts: int, plan: Optional[Plan] = None, 
 def route_plan(logits: torch.Tensor, top_k: int, plan: Optional[Plan] = None, idx: Optional[torch.Tensor] = None,
                w: Optional[torch.Tensor] = None, stream=None):
     """moe_route_plan: router and planner in one launch; returns (idx, w, plan)."""
-    if logits.dtype != torch.float32 or logits.dim() != 2 or not logits.is_contiguous():
-        raise ValueError("logits must be a contiguous fp32 [B, E] tensor")
+    _check_logits(logits)
     B, E = logits.shape
     if idx is None:
         idx = torch.empty((B, top_k), dtype=torch.int32, device=logits.device)
@@ -366,8 +375,9 @@ def route_plan(logits: torch.Tensor, top_k: int, plan: Optional[Plan] = None, id
         w = torch.empty((B, top_k), dtype=torch.float32, device=logits.device)
     if plan is None:
         plan = Plan.allocate(E, B * top_k, device=logits.device)
-    if plan.sorted_slots.numel() < B * top_k or plan.counts.numel() < E:
-        raise ValueError("plan buffers are too small")
+    _need(idx, "idx", torch.int32, (B, top_k))
+    _need(w, "w", torch.float32, (B, top_k))
+    _check_plan_buffers(plan, E, B * top_k)
     _check(lib().moe_route_plan(_ptr(logits), B, E, top_k, _ptr(idx), _ptr(w), C.byref(plan.struct),
                                 _stream(stream)), "moe_route_plan")
     return idx, w, plan

@@ -372,3 +372,22 @@ def test_static_entry_point_refuses_what_its_scratch_cannot_hold():
     assert f(C.byref(st), LG, X, -1, I, WT, C.byref(p), None, O, None) == moe.MOE_ERR_INVALID_ARG
     assert f(C.byref(layer(top_k=0)), LG, X, 1, I, WT, C.byref(p), None, O, None) == moe.MOE_ERR_INVALID_ARG
 
+
+
+def test_routing_wrappers_check_buffers_before_the_library():
+    """The routing wrappers refuse host tensors, mis-shaped index/weight
+    buffers and plans too small for the batch before anything reaches the
+    library (a wrong size would otherwise become an out-of-bounds write)."""
+    import torch
+
+    with pytest.raises(ValueError, match="device"):
+        moe.route_topk(torch.zeros((2, 128)), 8)
+    with pytest.raises(ValueError, match="device"):
+        moe.route_plan(torch.zeros((2, 128)), 8)
+    with pytest.raises(ValueError, match="device"):
+        moe.expert_plan(torch.zeros((2, 8), dtype=torch.int32), 128)
+    # a plan allocated for fewer slots than the batch holds
+    small = moe.Plan(*[torch.zeros(n, dtype=torch.int32) for n in (128, 129, 4, 128, 1)],
+                     torch.zeros((128, 4), dtype=torch.int32), None)
+    with pytest.raises(ValueError, match="too small"):
+        _lib._check_plan_buffers(small, 128, 16)
