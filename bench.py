@@ -82,7 +82,8 @@ def parse():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=480)
-    ap.add_argument("--warmup", type=int, default=48)
+    ap.add_argument("--warmup", type=int, default=480,
+                    help="untimed steps before the timed ones (ten graph replays of the 48-layer rotation)")
     ap.add_argument("--workload", default="decode", choices=sorted(WORKLOADS))
     ap.add_argument("--regime", default=None,
                     help="routing regime override (normal, sharing, disjoint, zipf, same)")
