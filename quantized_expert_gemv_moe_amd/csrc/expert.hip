@@ -1000,7 +1000,7 @@ static moe_status launch_down_cols(const moe_layer_t *L, const float *h, float *
 #define MOE_DC(NW, CPW) \
     case NW * 100 + CPW: launch_down_cols_t<NW, CPW>(L, h, y, pv, groups_y, n_slots, max_count, s); break;
         MOE_DC(4, 1) MOE_DC(4, 3) MOE_DC(4, 5) MOE_DC(4, 7)
-        MOE_DC(8, 1) MOE_DC(8, 2) MOE_DC(8, 3)
+        MOE_DC(8, 1) MOE_DC(8, 2) MOE_DC(12, 2)
         MOE_DC(16, 2) MOE_DC(16, 3) MOE_DC(16, 4)
 #undef MOE_DC
         default: return MOE_ERR_UNSUPPORTED;
@@ -1117,7 +1117,7 @@ static moe_status launch_down_token(const moe_layer_t *L, int n_tokens, const fl
 #define MOE_DT(NW, CPW) \
     case NW * 100 + CPW: return launch_down_token_k<NW, CPW>(L, n_tokens, h, idx, w, residual, out, rb, s);
         MOE_DT(4, 1) MOE_DT(4, 3) MOE_DT(4, 5) MOE_DT(4, 7)
-        MOE_DT(8, 1) MOE_DT(8, 2) MOE_DT(8, 3)
+        MOE_DT(8, 1) MOE_DT(8, 2) MOE_DT(12, 2)
         MOE_DT(16, 2) MOE_DT(16, 3) MOE_DT(16, 4)
 #undef MOE_DT
         default: return MOE_ERR_UNSUPPORTED;

@@ -223,8 +223,8 @@ def test_decode_step_column_layout_geometries(H, F, E, k):
 
 
 @pytest.mark.parametrize("H,F,E,k,B,regime", [
-    (2048, 768, 128, 8, 12, "same"),    # 8 waves, 4-slot stages: every expert holds all 12 tokens
-    (2048, 768, 128, 8, 9, "sharing"),  # stages of 1..4 slots
+    (2048, 768, 128, 8, 12, "same"),    # 12 waves, 2-slot stages: every expert holds all 12 tokens
+    (2048, 768, 128, 8, 9, "sharing"),  # 12 waves x 2 chunks; stages of 1 or 2 slots
     (512, 2048, 16, 4, 10, "same"),     # 16 waves, 2-slot stages: five stages per expert
     (256, 1536, 8, 2, 11, "normal"),    # 16 waves x 3 chunks
     (128, 896, 8, 2, 13, "same"),       # 4 waves x 7 chunks: four groups per wave and slot
